@@ -1,0 +1,40 @@
+"""CPU oracle for content-adaptive block-sparse video attention (NABLA pipeline).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP kernels or their host
+library; the only common dependency is the seeded input generator in
+`workloads`, which holds none of the method's arithmetic.
+
+Everything is plain numpy in float64 from the exact input values, following
+the steps of the NABLA technical summary (gist.science/es/paper/2507.13546,
+"Metodologia: NABLA", items 1-3) in the page's order.  See `nabla.py` for the
+per-function citations and the readings taken where the page is silent.
+
+Pinned (checked against closed forms, brute force or library routines in
+tests/test_oracle_pins.py): fractal_positions, permute, inverse_permute,
+pool_blocks, reduced_map, cdf_keep, sta_window, csr_from_keep,
+block_sparse_attention, dense_attention.  No function is "parity unpinned".
+"""
+from .nabla import (
+    fractal_positions,
+    permute,
+    inverse_permute,
+    pool_blocks,
+    reduced_map,
+    cdf_keep,
+    sta_window,
+    csr_from_keep,
+    head_mask,
+    build_mask,
+    block_sparse_attention,
+    dense_attention,
+    attention_pipeline,
+    tile_coords,
+)
+
+__all__ = [
+    "fractal_positions", "permute", "inverse_permute", "pool_blocks", "reduced_map",
+    "cdf_keep", "sta_window", "csr_from_keep", "head_mask", "build_mask",
+    "block_sparse_attention", "dense_attention", "attention_pipeline", "tile_coords",
+]
