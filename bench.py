@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse video attention hot path on one MI355X.
+
+One step = the whole path over one batch already resident in HBM:
+  build_mask(q, k)  (block pooling, float64 block logits, CDF cut + window, CSR)
+  prepare_v(v)      (V to fractal block order, per-block transposed)
+  attend(q, k, v')  (block-sparse attention over the kept 64 x 64 tiles)
+The fractal permutation of Q, K and O is fused into the loads/stores of these
+kernels (inputs and outputs stay in original (t, h, w) order).
+
+Prints ONE JSON line.  `value` is dense-equivalent TFLOP/s of a whole step
+(4*B*heads*L^2*D / step time); `roofline` covers the attention kernel
+(executed FLOPs / its own event-timed duration vs the bf16 MFMA peak);
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
+workload and extrapolates it to one full call.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", "attn_bf16.hip")
+
+
+def kernel_sha() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per attention launch from the committed PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
+    """Time the oracle on a bounded sample and extrapolate to one full call."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    S, N = cfg.S, cfg.block
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    wmask = None
+    if cfg.window is not None:
+        wmask = oracle.sta_window(cfg.T, cfg.H // cfg.patch, cfg.W // cfg.patch, cfg.window)
+    # mask: whole heads
+    t0 = time.perf_counter()
+    n_heads = 0
+    while True:
+        b, h = divmod(n_heads, cfg.heads)
+        oracle.head_mask(inputs["q"][b, h][src], inputs["k"][b, h][src], N, cfg.thr, wmask)
+        n_heads += 1
+        if time.perf_counter() - t0 > budget_s / 3 or n_heads >= cfg.batch * cfg.heads:
+            break
+    t_mask = (time.perf_counter() - t0) / n_heads * cfg.batch * cfg.heads
+    # attention: random CSR rows until the budget is used
+    rng = np.random.default_rng(cfg.seed)
+    order = rng.permutation(cfg.rows)
+    t0 = time.perf_counter()
+    flops = 0.0
+    n_rows = 0
+    for r in order:
+        bh, i = divmod(int(r), S)
+        b, h = divmod(bh, cfg.heads)
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]].astype(np.int64)
+        ktok = src[(cols[:, None] * N + np.arange(N)).reshape(-1)]
+        qf = inputs["q"][b, h][src[i * N:(i + 1) * N]][None, None].astype(np.float64)
+        kf = inputs["k"][b, h][ktok][None, None].astype(np.float64)
+        vf = inputs["v"][b, h][ktok][None, None].astype(np.float64)
+        nb = len(cols)
+        qpad = np.zeros((1, 1, N * nb, cfg.head_dim))
+        qpad[:, :, :N] = qf
+        oracle.block_sparse_attention(qpad, kf, vf, np.array([0, nb]), np.arange(nb, dtype=np.int32), N, rows=[0])
+        flops += 4.0 * N * N * cfg.head_dim * nb
+        n_rows += 1
+        if time.perf_counter() - t0 > 2 * budget_s / 3:
+            break
+    t_attn = (time.perf_counter() - t0) / flops * exec_flops
+    total = t_mask + t_attn
+    return {
+        "value": cfg.dense_flops / total / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: mask of {n_heads} of {cfg.batch * cfg.heads} heads and attention of "
+                   f"{n_rows} of {cfg.rows} CSR rows ({flops / 1e9:.1f} GFLOP), extrapolated to one full call "
+                   f"by head count and executed-FLOP share = {total:.1f} s per call"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload index (default 4: HunyuanVideo-scale hybrid)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also print per-stage details on stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path shards by (batch, head) "
+                                   "without communication, and no multi-GPU run is part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_fractal_amd as bsa
+    from workloads import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    bsa.lib()
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.config)
+    if cfg.dtype != "bf16":
+        print(json.dumps({"error": "the benchmark times the bf16 MFMA path; pick a bf16 config (1-4)"}))
+        sys.exit(2)
+
+    t_gen = time.perf_counter()
+    inputs = make_inputs(cfg)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(inputs[n + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+               for n in "qkv")
+    for n in ("q_bits", "k_bits", "v_bits"):
+        inputs.pop(n)
+    t_gen = time.perf_counter() - t_gen
+    g = bsa.VideoGrid(cfg.T, cfg.H, cfg.W, cfg.patch, cfg.block)
+    prob = bsa.make_problem(q, g)
+    sz = bsa.query_sizes(prob)
+    mask_ws = torch.empty(sz["mask_ws"], dtype=torch.uint8, device=dev)
+    fwd_ws = torch.empty(max(sz["fwd_ws"], 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window, workspace=mask_ws)
+        if ev is not None:
+            ev[1].record(stream)
+        vt = bsa.prepare_v(v, g)
+        if ev is not None:
+            ev[2].record(stream)
+        bsa.attend(q, k, vt, mask, g, workspace=fwd_ws, out=o)
+        if ev is not None:
+            ev[3].record(stream)
+        return mask
+
+    for _ in range(args.warmup):
+        mask = step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        mask = step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    nnz = mask.nnz()
+    rows, S = mask.rows, mask.S
+    density = nnz / float(rows * S)
+    exec_flops = 4.0 * cfg.block * cfg.block * cfg.head_dim * nnz
+    achieved = exec_flops / (attn_ms * 1e-3) / 1e12
+    elt = 2
+    mask_bytes = 2.0 * cfg.batch * cfg.heads * cfg.L * cfg.head_dim * elt + 4.0 * (rows + 1) + 4.0 * nnz
+    mask_gbs = mask_bytes / (mask_ms * 1e-3) / 1e9
+    prep_bytes = 2.0 * cfg.batch * cfg.heads * cfg.L * cfg.head_dim * elt
+    prep_gbs = prep_bytes / (prep_ms * 1e-3) / 1e9
+    value = cfg.dense_flops / (ms_step * 1e-3) / 1e12
+
+    win = "none" if cfg.window is None else "+-%d,%d,%d tiles" % cfg.window
+    line = {
+        "metric": "block-sparse attn ms/call + dense-equiv TFLOP/s; % MFMA peak on executed FLOPs",
+        "value": round(value, 3),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + positional term, bf16)",
+        "config": {
+            "workload": f"config {cfg.idx} {cfg.name}: B={cfg.batch}, heads={cfg.heads}, T x H x W = "
+                        f"{cfg.T}x{cfg.H}x{cfg.W} (L={cfg.L}), D={cfg.head_dim}, P={cfg.patch}, N={cfg.block}, "
+                        f"thr={cfg.thr}, window={win}",
+            "global_batch": cfg.batch,
+            "seq_len": cfg.L,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for_current_kernel(),
+            "kernel": "attn_bf16_kernel",
+            "flops_per_launch": exec_flops,
+            "avg_launch_ms": round(attn_ms, 4),
+        },
+        "stages_ms": {"build_mask": round(mask_ms, 4), "prepare_v": round(prep_ms, 4), "attend": round(attn_ms, 4)},
+        "mask_stage": {"algorithmic_bytes": mask_bytes, "gbs": round(mask_gbs, 1),
+                       "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4)},
+        "prepare_v": {"gbs": round(prep_gbs, 1), "hbm_frac": round(prep_gbs / HBM_PEAK_GBS, 4)},
+        "density": round(density, 5),
+        "nnz": nnz,
+        "executed_tflop": round(exec_flops / 1e12, 3),
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+        ci = mask.col_idx[:nnz].cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline(cfg, inputs, rp, ci, exec_flops, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+"""Torch-facing binding of libbsa: tensors in, tensors out, no arithmetic here.
+
+Every function validates tensor metadata, allocates outputs/workspace with
+torch on the tensors' device, and calls the C ABI on the current HIP stream.
+All computation runs in the HIP kernels.
+"""
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import BSA_BF16, BSA_F32, BSA_LAYOUT_FRACTAL, BSA_LAYOUT_ORIGINAL, check, lib
+
+_LAYOUTS = {"original": BSA_LAYOUT_ORIGINAL, "fractal": BSA_LAYOUT_FRACTAL}
+
+
+@dataclass(frozen=True)
+class VideoGrid:
+    """Token grid of one attention call: T x H x W tokens, fractal patch P, block N."""
+    T: int
+    H: int
+    W: int
+    patch: int = 8
+    block: int = 64
+
+    @property
+    def L(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def S(self) -> int:
+        return self.L // self.block
+
+
+@dataclass
+class BlockMask:
+    """CSR block mask on the device: row r = (b*heads + h)*S + i lists the kept key
+    blocks of query block i, ascending.  col_idx has capacity batch*heads*S*S."""
+    row_ptr: torch.Tensor     # int32 [rows + 1]
+    col_idx: torch.Tensor     # int32 [capacity]
+    nnz_dev: torch.Tensor     # int32 [1]
+    rows: int
+    S: int
+
+    def nnz(self) -> int:
+        return int(self.nnz_dev.item())
+
+    def density(self) -> float:
+        return self.nnz() / float(self.rows * self.S)
+
+    def as_struct(self) -> _lib.CSR:
+        return _lib.CSR(self.row_ptr.data_ptr(), self.col_idx.data_ptr(), self.col_idx.numel(),
+                        self.nnz_dev.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [batch, heads, L, head_dim]")
+        if t.dim() != 4 or t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q/k/v must share shape [batch, heads, L, head_dim], dtype and device")
+
+
+def make_problem(x: torch.Tensor, grid: VideoGrid, layout: str = "original") -> _lib.Problem:
+    B, nh, L, D = x.shape
+    if L != grid.L:
+        raise ValueError(f"tensor has L={L} tokens but the grid has {grid.L}")
+    return _lib.Problem(B, nh, grid.T, grid.H, grid.W, D, grid.patch, grid.block, _dtype_code(x),
+                        _LAYOUTS[layout])
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def query_sizes(prob: _lib.Problem) -> dict:
+    rows, max_nnz, mws, fws = (ctypes.c_int64() for _ in range(4))
+    check(lib().bsa_query_sizes(ctypes.byref(prob), ctypes.byref(rows), ctypes.byref(max_nnz),
+                                ctypes.byref(mws), ctypes.byref(fws)))
+    return {"rows": rows.value, "max_nnz": max_nnz.value, "mask_ws": mws.value, "fwd_ws": fws.value}
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes or ws.data_ptr() % 256:
+            raise ValueError(f"workspace must hold {nbytes} bytes and be 256-byte aligned")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def permute(x: torch.Tensor, grid: VideoGrid, inverse: bool = False) -> torch.Tensor:
+    """Original (t,h,w) order -> fractal order (inverse=False) or back; bit-exact copy."""
+    _check_qkv(x)
+    y = torch.empty_like(x)
+    prob = make_problem(x, grid)
+    check(lib().bsa_permute(ctypes.byref(prob), x.data_ptr(), y.data_ptr(), int(inverse), _stream(x.device)))
+    return y
+
+
+def pool(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, layout: str = "original") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block means of q and k, float64 [batch, heads, S, head_dim]."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    B, nh, _, D = q.shape
+    qp = torch.empty((B, nh, grid.S, D), dtype=torch.float64, device=q.device)
+    kp = torch.empty_like(qp)
+    check(lib().bsa_pool(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), qp.data_ptr(), kp.data_ptr(),
+                         _stream(q.device)))
+    return qp, kp
+
+
+def block_map(qp: torch.Tensor, kp: torch.Tensor, grid: VideoGrid, dtype=torch.bfloat16) -> torch.Tensor:
+    """Reduced softmax map over pooled blocks, float64 [batch, heads, S, S]."""
+    if qp.dtype != torch.float64 or kp.dtype != torch.float64 or not qp.is_contiguous() or not kp.is_contiguous():
+        raise ValueError("qp, kp must be contiguous float64 tensors from pool()")
+    B, nh, S, D = qp.shape
+    probe = torch.empty((B, nh, grid.L, D), dtype=dtype, device="meta")
+    prob = make_problem(probe, grid)
+    out = torch.empty((B, nh, S, S), dtype=torch.float64, device=qp.device)
+    check(lib().bsa_block_map(ctypes.byref(prob), qp.data_ptr(), kp.data_ptr(), out.data_ptr(),
+                              _stream(qp.device)))
+    return out
+
+
+def build_mask(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, thr: float,
+               window: Optional[Tuple[int, int, int]] = None, layout: str = "original",
+               workspace: Optional[torch.Tensor] = None) -> BlockMask:
+    """Pool -> reduced map -> CDF cut at 1-thr (-> union with +-window tiles) -> CSR."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    sz = query_sizes(prob)
+    dev = q.device
+    row_ptr = torch.empty(sz["rows"] + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(sz["max_nnz"], dtype=torch.int32, device=dev)
+    nnz = torch.empty(1, dtype=torch.int32, device=dev)
+    mask = BlockMask(row_ptr, col_idx, nnz, sz["rows"], grid.S)
+    ws = _workspace(sz["mask_ws"], dev, workspace)
+    wt, wh, ww = window if window is not None else (-1, -1, -1)
+    mp = _lib.MaskParams(float(thr), wt, wh, ww, 0)
+    csr = mask.as_struct()
+    check(lib().bsa_build_mask(ctypes.byref(prob), ctypes.byref(mp), q.data_ptr(), k.data_ptr(),
+                               ctypes.byref(csr), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return mask
+
+
+def mask_from_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int) -> BlockMask:
+    """Wrap a caller-made CSR (int32 device tensors) for forward()."""
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    rows = row_ptr.numel() - 1
+    nnz = row_ptr[-1:].clone()
+    return BlockMask(row_ptr.contiguous(), col_idx.contiguous(), nnz, rows, S)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+            layout: str = "original", return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Attention of every query block over the tokens of its kept key blocks."""
+    _check_qkv(q, k, v)
+    prob = make_problem(q, grid, layout)
+    sz = query_sizes(prob)
+    if mask.rows != sz["rows"]:
+        raise ValueError(f"mask has {mask.rows} rows, the problem needs {sz['rows']}")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(sz["fwd_ws"], q.device, workspace)
+    csr = mask.as_struct()
+    check(lib().bsa_forward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
+                            o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                            ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def prepare_v(v: torch.Tensor, grid: VideoGrid, layout: str = "original") -> torch.Tensor:
+    """bf16 only: V in the attention kernel's layout (fractal block order, per-block
+    transposed).  Returned as a flat bf16 tensor of V's size."""
+    _check_qkv(v)
+    prob = make_problem(v, grid, layout)
+    vt = torch.empty(v.numel(), dtype=v.dtype, device=v.device)
+    check(lib().bsa_prepare_v(ctypes.byref(prob), v.data_ptr(), vt.data_ptr(), _stream(v.device)))
+    return vt
+
+
+def attend(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+           layout: str = "original", return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None):
+    """The attention kernel alone: `vp` = prepare_v(v) for bf16, or v itself for float32."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    sz = query_sizes(prob)
+    if mask.rows != sz["rows"]:
+        raise ValueError(f"mask has {mask.rows} rows, the problem needs {sz['rows']}")
+    if vp.numel() != q.numel() or vp.dtype != q.dtype or not vp.is_contiguous():
+        raise ValueError("vp must be a contiguous tensor with q's dtype and size")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(256, q.device, workspace)
+    csr = mask.as_struct()
+    check(lib().bsa_attend(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), vp.data_ptr(), ctypes.byref(csr),
+                           o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                           ws.data_ptr(), ws.numel() if workspace is not None else sz["fwd_ws"], _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def attention(q, k, v, grid: VideoGrid, thr: float, window=None, layout: str = "original",
+              return_lse: bool = False):
+    """The whole hot path: mask from (q, k), then block-sparse attention."""
+    mask = build_mask(q, k, grid, thr, window, layout)
+    out = forward(q, k, v, mask, grid, layout, return_lse)
+    return (out, mask)

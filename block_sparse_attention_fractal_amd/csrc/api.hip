@@ -1,0 +1,238 @@
+// libbsa entry points: host-side validation, workspace carving and launches.
+// Declarations and contracts: include/bsa.h.
+#include <cmath>
+#include <mutex>
+#include <string>
+
+#include "bsa.h"
+#include "kernels.h"
+#include "validate.h"
+
+using namespace bsa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(BSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Compute units of the current device, cached per device id.
+int current_cu_count(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(BSA_ERR_HIP, "device id out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    cache[dev] = n > 0 ? n : 1;
+  }
+  *out = cache[dev];
+  return BSA_OK;
+}
+
+int geom_or_fail(const bsa_problem* p, Geom* g) {
+  std::string msg;
+  const int st = make_geom(p, g, &msg);
+  if (st != BSA_OK) return fail(st, msg);
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_version(void) { return 100; }
+
+const char* bsa_status_str(int s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_SHAPE: return "BSA_ERR_SHAPE";
+    case BSA_ERR_DTYPE: return "BSA_ERR_DTYPE";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_CAPACITY: return "BSA_ERR_CAPACITY";
+    case BSA_ERR_WORKSPACE: return "BSA_ERR_WORKSPACE";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    default: return "BSA_ERR_UNKNOWN";
+  }
+}
+
+const char* bsa_last_error(void) { return g_last_error.c_str(); }
+
+int bsa_query_sizes(const bsa_problem* p, int64_t* rows, int64_t* max_nnz, int64_t* mask_ws, int64_t* fwd_ws) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (rows) *rows = g.rows;
+  if (max_nnz) *max_nnz = g.rows * g.S;
+  if (mask_ws) *mask_ws = mask_ws_layout(g).total;
+  if (fwd_ws) *fwd_ws = fwd_ws_layout(g).total;
+  return BSA_OK;
+}
+
+int bsa_permute(const bsa_problem* p, const void* x, void* y, int inverse, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!x || !y) return fail(BSA_ERR_INVALID_ARG, "bsa_permute: null tensor pointer");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_permute: tensors must be 16-byte aligned");
+  if (x == y) return fail(BSA_ERR_INVALID_ARG, "bsa_permute: in-place permutation is not supported");
+  hipError_t e = launch_permute(g, x, y, inverse, stream);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return BSA_OK;
+}
+
+int bsa_pool(const bsa_problem* p, const void* q, const void* k, double* qp, double* kp, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !qp || !kp) return fail(BSA_ERR_INVALID_ARG, "bsa_pool: null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(qp, 8) || !aligned(kp, 8))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_pool: misaligned pointer");
+  hipError_t e = launch_pool(g, q, k, qp, kp, stream);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  return BSA_OK;
+}
+
+int bsa_block_map(const bsa_problem* p, const double* qp, const double* kp, double* probs, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!qp || !kp || !probs) return fail(BSA_ERR_INVALID_ARG, "bsa_block_map: null pointer");
+  if (!aligned(qp, 16) || !aligned(kp, 16) || !aligned(probs, 8))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_block_map: misaligned pointer");
+  hipError_t e = launch_block_logits(g, qp, kp, probs, stream);
+  if (e != hipSuccess) return hip_fail(e, "block logits launch");
+  e = launch_block_softmax(g, probs, probs, stream);
+  if (e != hipSuccess) return hip_fail(e, "block softmax launch");
+  return BSA_OK;
+}
+
+int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* q, const void* k, const bsa_csr* out,
+                   void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  std::string msg;
+  st = check_mask_params(g, mp, &msg);
+  if (st != BSA_OK) return fail(st, msg);
+  if (!q || !k || !out || !out->row_ptr || !out->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_build_mask: null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out->row_ptr, 4) || !aligned(out->col_idx, 4))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_build_mask: misaligned pointer");
+  if (out->capacity < g.rows * g.S)
+    return fail(BSA_ERR_CAPACITY, "bsa_build_mask: col_idx capacity " + std::to_string(out->capacity) +
+                                      " < batch*heads*S*S = " + std::to_string(g.rows * g.S));
+  const MaskWs w = mask_ws_layout(g);
+  if (!ws || ws_bytes < w.total)
+    return fail(BSA_ERR_WORKSPACE, "bsa_build_mask: workspace needs " + std::to_string(w.total) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, "bsa_build_mask: workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  double* qp = reinterpret_cast<double*>(base + w.qp);
+  double* kp = reinterpret_cast<double*>(base + w.kp);
+  double* z = reinterpret_cast<double*>(base + w.z);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
+  const bool win = mp->win_t >= 0;
+  // Candidates for the sort: blocks within lambda of the row's max logit.  The
+  // rest carry total mass < S * exp(-lambda) = 1e-17 * thr (see select_kernel).
+  const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)g.S) - std::log(mp->thr) : 0.0;
+  hipError_t e = launch_pool(g, q, k, qp, kp, stream);
+  if (e == hipSuccess) e = launch_block_logits(g, qp, kp, z, stream);
+  if (e == hipSuccess)
+    e = launch_select(g, z, mp->thr, lambda, win ? mp->win_t : -1, win ? mp->win_h : -1, win ? mp->win_w : -1,
+                      bitmap, counts, w.words, stream);
+  if (e == hipSuccess) e = launch_scan(g, counts, out->row_ptr, out->nnz, stream);
+  if (e == hipSuccess) e = launch_compact(g, bitmap, w.words, out->row_ptr, out->col_idx, stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_build_mask launch");
+  return BSA_OK;
+}
+
+static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const void* k, const void* v,
+                             const bsa_csr* mask, const void* o, const float* lse, void* ws, int64_t ws_bytes,
+                             const char* who) {
+  int st = geom_or_fail(p, g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !o || !mask || !mask->row_ptr || !mask->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": misaligned pointer");
+  const FwdWs w = fwd_ws_layout(*g);
+  if (!ws || ws_bytes < w.total)
+    return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(w.total) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace must be 256-byte aligned");
+  return BSA_OK;
+}
+
+static int enqueue_attend(const Geom& g, const void* q, const void* k, const void* vp, const bsa_csr* mask, void* o,
+                          float* lse, char* ws, hipStream_t stream) {
+  const FwdWs w = fwd_ws_layout(g);
+  hipError_t e;
+  if (g.dtype == BSA_BF16) {
+    int ncu = 0;
+    const int st = current_cu_count(&ncu);
+    if (st != BSA_OK) return st;
+    int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
+    e = launch_zero_i32(counter, 1, stream);
+    if (e == hipSuccess)
+      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter, ncu, stream);
+  } else {
+    e = launch_attn_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
+                        mask->col_idx, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return BSA_OK;
+}
+
+int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (g.dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_prepare_v: only bf16 uses a prepared V");
+  if (!v || !vt) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v: null pointer");
+  if (!aligned(v, 16) || !aligned(vt, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v: misaligned pointer");
+  if (v == vt) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v: v and vt must not alias");
+  hipError_t e = launch_prep_vt(g, v, vt, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare_v launch");
+  return BSA_OK;
+}
+
+int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask, void* o,
+               float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = check_attend_args(p, &g, q, k, vp, mask, o, lse, ws, ws_bytes, "bsa_attend");
+  if (st != BSA_OK) return st;
+  return enqueue_attend(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream);
+}
+
+int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask, void* o,
+                float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = check_attend_args(p, &g, q, k, v, mask, o, lse, ws, ws_bytes, "bsa_forward");
+  if (st != BSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  const void* vp = v;
+  if (g.dtype == BSA_BF16) {
+    void* vt = base + fwd_ws_layout(g).vt;
+    hipError_t e = launch_prep_vt(g, v, vt, stream);
+    if (e != hipSuccess) return hip_fail(e, "prepare_v launch");
+    vp = vt;
+  }
+  return enqueue_attend(g, q, k, vp, mask, o, lse, base, stream);
+}
+
+}  // extern "C"

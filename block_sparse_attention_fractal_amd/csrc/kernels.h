@@ -1,0 +1,39 @@
+// Launchers of the HIP kernels (one translation unit per kernel family).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geom.h"
+
+namespace bsa {
+
+// Fractal flattening as a bit-exact copy of [B*nh, L, D] rows.
+hipError_t launch_permute(const Geom& g, const void* x, void* y, int inverse, hipStream_t s);
+// V in the tensor's layout -> Vt [B*nh, S, D, 64] bf16: block-major, each
+// block transposed to d-major with keys in MFMA operand order.
+hipError_t launch_prep_vt(const Geom& g, const void* v, void* vt, hipStream_t s);
+// Block means of Q and K in float64 -> qp, kp [B*nh, S, D].
+hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, double* kp, hipStream_t s);
+// Block logits z[bh, i, j] = qp_i . kp_j / sqrt(D) in float64.
+hipError_t launch_block_logits(const Geom& g, const double* qp, const double* kp, double* z, hipStream_t s);
+// Row softmax of z -> probs (inspection entry point).
+hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, hipStream_t s);
+// CDF cut + window union per row -> bitmap [rows, words] and kept counts [rows].
+hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h,
+                         int win_w, uint32_t* bitmap, int32_t* counts, int words, hipStream_t s);
+// Exclusive scan of counts -> row_ptr [rows+1]; row_ptr[rows] also copied to nnz (if not null).
+hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* nnz, hipStream_t s);
+// Bitmap -> ascending col_idx at row_ptr offsets.
+hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr,
+                          int32_t* col_idx, hipStream_t s);
+// Block-sparse attention forward.
+hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
+                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counter, int num_cu,
+                            hipStream_t s);
+hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s);
+// Zero a small device counter (a fill kernel, safe under stream capture).
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+
+}  // namespace bsa

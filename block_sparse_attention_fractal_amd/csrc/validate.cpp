@@ -1,0 +1,92 @@
+// Host-side validation and workspace layout for libbsa.  No HIP dependency:
+// every rejection here happens before anything touches a GPU.
+#include "validate.h"
+
+#include <cmath>
+#include <cstdio>
+
+namespace bsa {
+
+static int fail(std::string* msg, int code, const char* fmt, long long a = 0, long long b = 0) {
+  if (msg) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, fmt, a, b);
+    *msg = buf;
+  }
+  return code;
+}
+
+int make_geom(const bsa_problem* p, Geom* g, std::string* msg) {
+  if (!p || !g) return fail(msg, BSA_ERR_INVALID_ARG, "null problem pointer");
+  if (p->dtype != BSA_F32 && p->dtype != BSA_BF16)
+    return fail(msg, BSA_ERR_DTYPE, "dtype %lld is neither BSA_F32 nor BSA_BF16", p->dtype);
+  if (p->layout != BSA_LAYOUT_ORIGINAL && p->layout != BSA_LAYOUT_FRACTAL)
+    return fail(msg, BSA_ERR_INVALID_ARG, "layout %lld is not a valid layout", p->layout);
+  if (p->batch <= 0 || p->heads <= 0 || p->T <= 0 || p->H <= 0 || p->W <= 0 ||
+      p->head_dim <= 0 || p->patch <= 0 || p->block <= 0)
+    return fail(msg, BSA_ERR_SHAPE, "all sizes must be positive");
+  if (p->H % p->patch || p->W % p->patch)
+    return fail(msg, BSA_ERR_SHAPE, "H=%lld and W=%lld must be multiples of the patch size", p->H, p->W);
+  const long long L = (long long)p->T * p->H * p->W;
+  if (L % p->block)
+    return fail(msg, BSA_ERR_SHAPE, "L=%lld is not a multiple of the block size %lld", L, p->block);
+  if (p->block != 64)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "block size %lld: only N = 64 is implemented", p->block);
+  if (p->layout == BSA_LAYOUT_ORIGINAL && (long long)p->patch * p->patch != p->block)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "original layout needs P*P == N (P=%lld, N=%lld)", p->patch, p->block);
+  if (p->dtype == BSA_BF16 && p->head_dim != 128)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "bf16 head_dim %lld: only 128 is implemented", p->head_dim);
+  if (p->dtype == BSA_F32 && p->head_dim != 64 && p->head_dim != 128)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "f32 head_dim %lld: only 64 and 128 are implemented", p->head_dim);
+  const long long S = L / p->block;
+  if (S > 4096)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "S=%lld blocks per head exceeds 4096", S);
+  const long long bh = (long long)p->batch * p->heads;
+  if (L > (1LL << 30) || bh > (1LL << 30) || bh * S * S >= (1LL << 31))
+    return fail(msg, BSA_ERR_UNSUPPORTED, "batch*heads*S*S = %lld does not fit int32 CSR offsets", bh * S * S);
+  g->B = p->batch; g->nh = p->heads; g->T = p->T; g->H = p->H; g->W = p->W;
+  g->D = p->head_dim; g->P = p->patch; g->N = p->block;
+  g->L = (int32_t)L; g->S = (int32_t)S; g->Hp = p->H / p->patch; g->Wp = p->W / p->patch;
+  g->layout = p->layout; g->dtype = p->dtype; g->rows = bh * S;
+  return BSA_OK;
+}
+
+int check_mask_params(const Geom& g, const bsa_mask_params* mp, std::string* msg) {
+  if (!mp) return fail(msg, BSA_ERR_INVALID_ARG, "null mask params");
+  if (!(mp->thr >= 0.0 && mp->thr < 1.0) || std::isnan(mp->thr))
+    return fail(msg, BSA_ERR_INVALID_ARG, "thr must satisfy 0 <= thr < 1");
+  if (mp->reserved != 0) return fail(msg, BSA_ERR_INVALID_ARG, "reserved field must be 0");
+  const int neg = (mp->win_t < 0) + (mp->win_h < 0) + (mp->win_w < 0);
+  if (neg != 0 && neg != 3)
+    return fail(msg, BSA_ERR_INVALID_ARG, "window extents must be all >= 0 (on) or all < 0 (off)");
+  if (neg == 0 && g.P * g.P != g.N)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "the sliding-tile window needs N == P*P");
+  return BSA_OK;
+}
+
+static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+MaskWs mask_ws_layout(const Geom& g) {
+  MaskWs w{};
+  w.words = (g.S + 31) / 32;
+  int64_t off = 0;
+  w.qp = off; off = align256(off + g.rows * g.D * 8);
+  w.kp = off; off = align256(off + g.rows * g.D * 8);
+  w.z = off; off = align256(off + g.rows * (int64_t)g.S * 8);
+  w.counts = off; off = align256(off + g.rows * 4);
+  w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
+  w.total = off;
+  return w;
+}
+
+FwdWs fwd_ws_layout(const Geom& g) {
+  FwdWs w{};
+  int64_t off = 0;
+  w.counter = off; off = align256(off + 64);
+  w.vt = off;
+  if (g.dtype == BSA_BF16) off = align256(off + (int64_t)g.B * g.nh * g.L * g.D * 2);
+  w.total = off;
+  return w;
+}
+
+}  // namespace bsa

@@ -1,0 +1,25 @@
+// Host-side argument checks and workspace layout (plain C++, no HIP calls).
+#pragma once
+#include <stdint.h>
+#include <string>
+
+#include "bsa.h"
+#include "geom.h"
+
+namespace bsa {
+
+// Fills g from p; returns a bsa status and a message on failure.
+int make_geom(const bsa_problem* p, Geom* g, std::string* msg);
+int check_mask_params(const Geom& g, const bsa_mask_params* mp, std::string* msg);
+
+struct MaskWs {       // byte offsets into the mask workspace
+  int64_t qp, kp, z, counts, bitmap, total;
+  int32_t words;      // 32-bit words per bitmap row
+};
+struct FwdWs {
+  int64_t counter, vt, total;
+};
+MaskWs mask_ws_layout(const Geom& g);
+FwdWs fwd_ws_layout(const Geom& g);
+
+}  // namespace bsa

@@ -1,0 +1,176 @@
+/*
+ * bsa.h -- C ABI of libbsa: content-adaptive block-sparse self-attention over
+ * 3D video tokens on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the NABLA pipeline ("Resumen Tecnico: NABLA - Atencion de
+ * Bloque Adaptativa al Vecindario para la Generacion Eficiente de Video",
+ * gist.science/es/paper/2507.13546, section "Metodologia: NABLA"):
+ *   1. fractal flattening of the T x H x W tokens (item 1),
+ *   2. average pooling of Q and K into N-token blocks, a softmax map over the
+ *      pooled blocks and a per-row CDF cut at mass 1 - thr (item 2, bullets
+ *      "Submuestreo", "Atencion Reducida", "Umbralizacion CDF"),
+ *   3. optional union with a static sliding-tile window (item 3),
+ *   4. attention computed only on the kept N x N tiles (item 2, "Expansion").
+ * The CDF mask is emitted as a CSR list of key blocks per query block, the
+ * "skip list" form that the CalibAtt page ("Accelerating Text-to-Video
+ * Generation with Calibrated Sparse Attention", gist.science/es/paper/2603.05503,
+ * "Fase de Inferencia") feeds to its sparse kernel; any CSR, from any source,
+ * can be passed to bsa_forward.
+ *
+ * Conventions shared by every call
+ *   - Tensors Q, K, V, O are dense [batch, heads, L, head_dim], row-major,
+ *     L = T*H*W, in the problem's dtype.  With layout BSA_LAYOUT_ORIGINAL the
+ *     tokens are in (t, h, w) row-major order; with BSA_LAYOUT_FRACTAL they are
+ *     already in fractal order.
+ *   - Fractal order: position f = ((t*Hp + y/P)*Wp + x/P)*P*P + (y%P)*P + (x%P),
+ *     Hp = H/P, Wp = W/P: frames outermost, P x P patches row-major inside a
+ *     frame, tokens row-major inside a patch.  Block i = fractal tokens
+ *     [i*N, (i+1)*N); S = L/N blocks per head.
+ *   - CSR row r = (b*heads + h)*S + i lists the kept key blocks of query block i
+ *     of head (b, h), ascending, as block ids in fractal order.
+ *   - Every pointer argument except the problem/params structs and the
+ *     workspace size is a DEVICE pointer unless stated otherwise; the caller
+ *     owns all memory.  The library allocates nothing and keeps no state
+ *     besides cached device properties; calls are reentrant.
+ *   - Calls validate on the host, enqueue kernels on `stream` and return
+ *     without synchronising.  Errors detected on the host return a status
+ *     before anything is enqueued; a failed launch returns BSA_ERR_HIP.
+ *     Asynchronous device faults surface at the caller's next synchronisation.
+ *     No C++ exception crosses this interface.  bsa_last_error() returns a
+ *     thread-local message describing the last non-OK status.
+ *
+ * Supported shapes (else BSA_ERR_SHAPE / BSA_ERR_UNSUPPORTED):
+ *   N == 64; H % P == 0, W % P == 0, L % N == 0; layout ORIGINAL needs P*P == N;
+ *   head_dim in {64, 128} for f32, == 128 for bf16; S <= 4096;
+ *   batch*heads*S*S < 2^31 (int32 CSR offsets).
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, thr outside [0, 1) */
+  BSA_ERR_SHAPE = 2,         /* sizes that do not tile (L % N, H % P, ...) */
+  BSA_ERR_DTYPE = 3,         /* dtype not BSA_F32 / BSA_BF16 */
+  BSA_ERR_UNSUPPORTED = 4,   /* valid but not implemented (head_dim, N, S) */
+  BSA_ERR_CAPACITY = 5,      /* CSR col_idx capacity below batch*heads*S*S */
+  BSA_ERR_WORKSPACE = 6,     /* workspace null or smaller than bsa_query_sizes says */
+  BSA_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed */
+};
+
+enum { BSA_F32 = 0, BSA_BF16 = 1 };
+enum { BSA_LAYOUT_ORIGINAL = 0, BSA_LAYOUT_FRACTAL = 1 };
+
+/* Problem description (host struct). */
+typedef struct bsa_problem {
+  int32_t batch, heads;      /* B, nh */
+  int32_t T, H, W;           /* token grid; L = T*H*W */
+  int32_t head_dim;          /* D */
+  int32_t patch;             /* P, fractal patch side */
+  int32_t block;             /* N, tokens per block */
+  int32_t dtype;             /* BSA_F32 or BSA_BF16 */
+  int32_t layout;            /* BSA_LAYOUT_ORIGINAL or BSA_LAYOUT_FRACTAL */
+} bsa_problem;
+
+/* Mask parameters (host struct).  thr in [0, 1): per row keep the shortest
+ * prefix of key blocks, ordered by reduced-map probability descending (ties by
+ * block index ascending), whose mass reaches 1 - thr; thr == 0 keeps every
+ * block.  The sliding-tile window is enabled when win_t, win_h and win_w are
+ * all >= 0: query tile (t, y, x) then also keeps every key tile (t', y', x')
+ * with |t-t'| <= win_t, |y-y'| <= win_h, |x-x'| <= win_w (clipped, no wrap);
+ * it needs N == P*P.  All three < 0 disables it; mixed signs are an error. */
+typedef struct bsa_mask_params {
+  double thr;
+  int32_t win_t, win_h, win_w;
+  int32_t reserved;          /* must be 0 */
+} bsa_mask_params;
+
+/* CSR block mask (host struct holding device pointers). */
+typedef struct bsa_csr {
+  int32_t* row_ptr;          /* device, [rows + 1], row_ptr[0] = 0 */
+  int32_t* col_idx;          /* device, [capacity] */
+  int64_t capacity;          /* elements available in col_idx */
+  int32_t* nnz;              /* device scalar receiving row_ptr[rows]; may be NULL */
+} bsa_csr;
+
+/* Sizes for a problem (all outputs are host pointers; any may be NULL).
+ * rows = batch*heads*S; max_nnz = rows*S (the col_idx capacity bsa_build_mask
+ * requires); mask_ws / fwd_ws = workspace bytes for bsa_build_mask /
+ * bsa_forward.  Pure host computation; needs no GPU. */
+int bsa_query_sizes(const bsa_problem* p, int64_t* rows, int64_t* max_nnz,
+                    int64_t* mask_ws, int64_t* fwd_ws);
+
+/* Fractal flattening (NABLA page, Metodologia item 1) as a bit-exact copy:
+ * inverse == 0 maps original (t, h, w) order to fractal order, inverse != 0
+ * maps back.  x, y: [batch, heads, L, head_dim] of p->dtype; must not overlap.
+ * p->layout is ignored. */
+int bsa_permute(const bsa_problem* p, const void* x, void* y, int inverse, hipStream_t stream);
+
+/* Block average pooling (Metodologia item 2, "Submuestreo"): qp[b,h,i,:] is the
+ * mean of Q over the N tokens of fractal block i, likewise kp for K; outputs
+ * are float64 [batch, heads, S, head_dim].  Inputs in p->layout order.  The
+ * sums are accumulated in float64 (exact for bf16 inputs). */
+int bsa_pool(const bsa_problem* p, const void* q, const void* k, double* qp, double* kp,
+             hipStream_t stream);
+
+/* Reduced map (Metodologia item 2, "Atencion Reducida"): probs[b,h,i,j] =
+ * softmax_j(qp_i . kp_j / sqrt(head_dim)) in float64, from the outputs of
+ * bsa_pool.  probs: [batch, heads, S, S] float64.  An inspection entry point:
+ * bsa_build_mask never materialises this array. */
+int bsa_block_map(const bsa_problem* p, const double* qp, const double* kp, double* probs,
+                  hipStream_t stream);
+
+/* Whole mask stage: pooling, reduced map, CDF cut, optional window union and
+ * CSR compaction (Metodologia items 2 and 3).  q, k in p->layout order.
+ * out->row_ptr receives rows+1 offsets, out->col_idx the ascending kept block
+ * ids, out->nnz (if not NULL) the total.  ws: device workspace of at least
+ * mask_ws bytes (bsa_query_sizes), 256-byte aligned; its contents on entry do
+ * not matter and are clobbered. */
+int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* q, const void* k,
+                   const bsa_csr* out, void* ws, int64_t ws_bytes, hipStream_t stream);
+
+/* Block-sparse attention forward (Metodologia item 2, "Expansion"): every query
+ * token of block i attends, with scale 1/sqrt(head_dim), to all tokens of the
+ * key blocks listed in CSR row i of its head and to nothing else:
+ *   o_n = sum_k softmax_k(q_n . k_k / sqrt(D)) v_k,  lse_n = log sum_k exp(q_n . k_k / sqrt(D)).
+ * q, k, v, o: [batch, heads, L, head_dim] in p->layout order (o written in the
+ * same order as q); lse: float32 [batch, heads, L] in the same token order, or
+ * NULL.  mask->row_ptr / col_idx as produced by bsa_build_mask (capacity and
+ * nnz are not read).  Every CSR row must be non-empty with ids in [0, S).
+ * ws: device workspace of at least fwd_ws bytes, 256-byte aligned. */
+int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v,
+                const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes,
+                hipStream_t stream);
+
+/* The two halves of bsa_forward, for callers that time or reuse them separately.
+ * bsa_prepare_v (bf16 only; f32 returns BSA_ERR_UNSUPPORTED) writes V in the
+ * attention kernel's layout: fractal block order, each 64-token block stored
+ * transposed (head_dim rows of 64 keys), keys inside every group of 16 in the
+ * order 0-3, 8-11, 4-7, 12-15.  vt: device buffer of batch*heads*L*head_dim
+ * bf16 elements (the size of V), 16-byte aligned.
+ * bsa_attend runs the attention kernel; `vp` is the output of bsa_prepare_v for
+ * bf16, or the V tensor itself (p->layout order) for f32.  ws: at least
+ * fwd_ws bytes; only its first 256 bytes (a work counter) are used. */
+int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream);
+int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
+               void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
+
+/* Status code -> static string. */
+const char* bsa_status_str(int status);
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* bsa_last_error(void);
+/* ABI version (major*10000 + minor*100 + patch). */
+int bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

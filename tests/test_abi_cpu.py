@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/bsa.h declares, sizes its buffers as documented, and rejects bad
+arguments on the host before anything is enqueued (no kernel is launched here:
+every call below fails validation, so no device pointer is ever touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+bsa = pytest.importorskip("block_sparse_attention_fractal_amd")
+from block_sparse_attention_fractal_amd import _lib  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libbsa.so not built")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bsa_version() == 100
+    for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
+                       (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
+                       (7, "BSA_ERR_HIP")]:
+        assert lib.bsa_status_str(code).decode() == name
+
+
+def P(B=1, nh=8, T=8, H=32, W=32, D=128, Pp=8, N=64, dtype=1, layout=0):
+    return _lib.Problem(B, nh, T, H, W, D, Pp, N, dtype, layout)
+
+
+def sizes(lib, p):
+    vals = [ctypes.c_int64() for _ in range(4)]
+    st = lib.bsa_query_sizes(ctypes.byref(p), *[ctypes.byref(v) for v in vals])
+    return st, [v.value for v in vals]
+
+
+@pytest.mark.parametrize("B,nh,T,H,W", [(1, 8, 8, 32, 32), (1, 40, 21, 32, 48), (2, 24, 33, 48, 80), (1, 4, 4, 16, 16)])
+def test_query_sizes(lib, B, nh, T, H, W):
+    D = 128
+    st, (rows, max_nnz, mws, fws) = sizes(lib, P(B, nh, T, H, W, D))
+    assert st == 0
+    S = T * H * W // 64
+    assert rows == B * nh * S and max_nnz == rows * S
+    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap (each 256-aligned)
+    a = lambda x: (x + 255) // 256 * 256
+    assert mws == a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
+    assert fws == 256 + a(B * nh * T * H * W * D * 2)
+    assert mws % 256 == 0 and fws % 256 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 3),                         # dtype
+    (dict(layout=5), 1),                        # layout enum
+    (dict(H=30), 2),                            # H % P
+    (dict(W=20), 2),                            # W % P
+    (dict(T=0), 2),                             # non-positive
+    (dict(N=32), 4),                            # only N = 64
+    (dict(Pp=4, N=64), 4),                      # original layout needs P*P == N
+    (dict(D=64), 4),                            # bf16 needs D = 128
+    (dict(dtype=0, D=96), 4),                   # f32 D in {64, 128}
+    (dict(T=65, H=64, W=64), 4),                # S > 4096
+    (dict(T=1, H=8, W=12, Pp=4, N=64, layout=1), 2),   # L % N
+])
+def test_query_sizes_rejects(lib, kw, code):
+    st, _ = sizes(lib, P(**kw))
+    assert st == code, lib.bsa_last_error().decode()
+    assert lib.bsa_last_error().decode() != ""
+
+
+def test_fractal_layout_allows_other_patch_sizes(lib):
+    st, (rows, *_) = sizes(lib, P(T=2, H=16, W=16, Pp=4, N=64, layout=1))
+    assert st == 0 and rows == 8 * 8
+
+
+FAKE = 1 << 20          # never dereferenced: every call below fails validation first
+
+
+def _mask_call(lib, p, thr=0.1, win=(-1, -1, -1), reserved=0, cap=None, ws_bytes=None, q=FAKE, ws=FAKE):
+    st, (rows, max_nnz, mws, _) = sizes(lib, p)
+    mp = _lib.MaskParams(thr, win[0], win[1], win[2], reserved)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz if cap is None else cap, None)
+    return lib.bsa_build_mask(ctypes.byref(p), ctypes.byref(mp), q, FAKE, ctypes.byref(csr), ws,
+                              mws if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(thr=1.0), 1), (dict(thr=-0.1), 1), (dict(thr=float("nan")), 1), (dict(win=(1, -1, 1)), 1),
+    (dict(reserved=3), 1), (dict(cap=10), 5), (dict(ws_bytes=1000), 6), (dict(q=None), 1),
+    (dict(q=FAKE + 2), 1), (dict(ws=FAKE + 64), 6),
+])
+def test_build_mask_rejects_before_launch(lib, kw, code):
+    st = _mask_call(lib, P(), **kw)
+    assert st == code, lib.bsa_last_error().decode()
+
+
+def test_window_needs_square_patch_blocks(lib):
+    st = _mask_call(lib, P(T=2, H=16, W=16, Pp=4, N=64, layout=1), win=(1, 1, 1))
+    assert st == 4
+
+
+def test_forward_rejects_before_launch(lib):
+    p = P()
+    st, (rows, max_nnz, mws, fws) = sizes(lib, p)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None)
+    f = lib.bsa_forward
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws - 1, None) == 6
+    assert f(ctypes.byref(p), FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 1
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE + 2, FAKE, fws, None) == 1
+    bad = P(dtype=7)
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 3
+
+
+def test_permute_and_pool_reject_before_launch(lib):
+    p = P()
+    assert lib.bsa_permute(ctypes.byref(p), FAKE, FAKE, 0, None) == 1          # in place
+    assert lib.bsa_permute(ctypes.byref(p), FAKE, FAKE + 8, 0, None) == 1      # misaligned
+    assert lib.bsa_pool(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == 1
+    assert lib.bsa_block_map(ctypes.byref(P(H=31)), FAKE, FAKE, FAKE, None) == 2
