@@ -187,7 +187,7 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
     const int st = current_cu_count(&ncu);
     if (st != BSA_OK) return st;
     int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
-    e = launch_zero_i32(counter, 1, stream);
+    e = launch_zero_i32(counter, 8, stream);   // one work counter per XCD
     if (e == hipSuccess)
       e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter, ncu, stream);
   } else {

@@ -6,26 +6,35 @@
 // the block mask decides which N x N tiles are computed, all or nothing).
 //
 // Work decomposition
-//   * one work item = one CSR row = one 64-query block; a persistent grid of
-//     two-wave (128-thread) workgroups pulls items from an atomic counter;
-//   * wave w owns queries 32w..32w+31 and keeps its Q operand in registers;
-//   * per kept key block: K (64 x 128) and V^T (128 x 64) tiles are staged
-//     global -> registers -> LDS (XOR-swizzled), the next tile's global loads
-//     are issued before the current tile's math;
+//   * a work item is a PAIR of adjacent query blocks (i, i+1) of one head; the
+//     item walks the union of their two ascending key lists, so a key/value tile
+//     kept by both is fetched once and used by both (halves L2/MALL traffic on
+//     the common case where neighbouring blocks keep almost the same keys);
+//   * 256-thread workgroups: waves 0-1 own block i, waves 2-3 own block i+1,
+//     32 queries per wave, the Q operand held in registers;
+//   * persistent grid, two workgroups per CU; workgroup b runs on XCD b % 8 and
+//     pulls items from its XCD's own contiguous range (split by cumulative
+//     kept-tile count), so concurrently running items of one XCD share a head and
+//     its K/V tiles in that XCD's L2;
+//   * K (64 x 128) and V^T (128 x 64) tiles move global -> LDS with direct
+//     (VGPR-free) 16-byte loads into a double buffer; the next tile's loads are
+//     issued right after the barrier that publishes the current one;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
-//     columns from registers); the accumulator then holds, per lane, 32 keys
-//     of ONE query, so the online-softmax state (running max m, partial sum l)
-//     is per lane and only the max needs one cross-half exchange per tile;
+//     columns from registers): each lane's accumulator holds 32 keys of ONE
+//     query, so the online-softmax state is per lane;
+//   * the running max is refreshed lazily: exponentials use a reference max
+//     that is only raised (and O rescaled) when some lane's true max exceeds it
+//     by more than 2^8, which keeps every p <= 256 and skips the rescale of the
+//     64 output accumulators on almost every tile;
 //   * O^T += V^T P^T with the same MFMA: A = V^T rows from LDS (pre-transposed
-//     in HBM, keys stored in the accumulator's order), B = P^T taken straight
-//     from the S^T accumulator registers after conversion to bf16;
-//   * P is rounded to bf16 for the PV product; everything else is fp32.
+//     in HBM, keys stored in the accumulator's order), B = P^T straight from the
+//     S^T accumulator registers after rounding to bf16.
 //
-// MFMA operand conventions used (32x32x16, bf16): A lane l holds row l%32 and
-// eight consecutive k of half l/32; B lane l holds column l%32 likewise; the
-// accumulator register r of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).
-// Both contractions pair "element e of half h" of A and B, so the physical k
-// order inside the instruction is irrelevant.
+// MFMA operand conventions (32x32x16, bf16): A lane l holds row l%32 and eight
+// k of half l/32; B lane l holds column l%32 likewise; accumulator register r
+// of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).  Both contractions
+// pair "element e of half h" of A and B, so the physical k order inside the
+// instruction does not matter.
 #include <math.h>
 
 #include "kernels.h"
@@ -34,6 +43,8 @@ namespace bsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 struct AttnBf16Args {
   const uint16_t* q;
@@ -43,19 +54,23 @@ struct AttnBf16Args {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  int32_t* counter;
+  int32_t* counters;   // 8 per-XCD item counters
   Geom g;
-  float c_log2;   // log2(e) / sqrt(D)
+  float c_log2;        // log2(e) / sqrt(D)
+  int32_t pairs;       // query-block pairs per head = ceil(S/2)
+  int32_t items;       // B*heads*pairs
 };
 
 constexpr int kD = 128;
-constexpr int kVtOff = 16384;
+constexpr int kStage = 32768;          // one K tile (16 KB) + one V^T tile (16 KB)
+constexpr int kVt = 16384;             // V^T offset inside a stage
+constexpr float kLazy = 8.0f;          // log2 slack before the reference max is raised
 
-// K tile: 64 rows x 256 B, 16-byte chunk c of row k at chunk c ^ (k & 15).
+// K tile: 64 rows x 256 B, 16-byte chunk c of row k stored at chunk c ^ (k & 15).
 __device__ __forceinline__ int k_lds(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-// V^T tile: 128 rows x 128 B, chunk c of row d at c ^ ((d >> 1) & 7).
+// V^T tile: 128 rows x 128 B, chunk c of row d stored at c ^ ((d >> 1) & 7).
 __device__ __forceinline__ int v_lds(int row, int chunk) {
-  return kVtOff + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return kVt + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -72,29 +87,111 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
-__global__ void __launch_bounds__(128) attn_bf16_kernel(AttnBf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[32768];
+// First token row (in the tensor's own layout) of block j; token m of the block
+// sits rs*(m/8) + m%8 rows further (rs = W for original order, 8 for fractal).
+__device__ __forceinline__ int block_base_row(const Geom& g, int j) {
+  if (g.layout == 1) return j * 64;
+  const int px = j % g.Wp;
+  const int rest = j / g.Wp;
+  const int py = rest % g.Hp;
+  const int t = rest / g.Hp;
+  return (t * g.H + py * 8) * g.W + px * 8;
+}
+
+// Cumulative kept tiles of the rows before item t (items ordered head-major).
+__device__ __forceinline__ int64_t item_cost_prefix(const AttnBf16Args& a, int64_t t) {
+  const int64_t bh = t / a.pairs;
+  const int64_t p = t - bh * a.pairs;
+  int64_t row = bh * a.g.S + 2 * p;
+  if (row > a.g.rows) row = a.g.rows;
+  return a.row_ptr[row];
+}
+
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];   // double-buffered K + V^T
   __shared__ int s_item;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int qb = wave >> 1;      // which block of the pair
+  const int wq = wave & 1;       // which 32 queries of that block
   const Geom g = a.g;
   const float c_log2 = a.c_log2;
+  const int rs = g.layout == 1 ? 8 : g.W;
+
+  // per-thread byte offsets of this thread's direct-load chunks (independent of the tile)
+  int koff[4], voff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = (4 * wave + u) * 64 + lane;
+    const int m = c >> 4;                                   // key row in the tile
+    const int lc = (lane & 15) ^ (m & 15);                  // logical chunk stored at this slot
+    koff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
+    const int d = c >> 3;                                   // V^T row
+    const int lv = (lane & 7) ^ ((d >> 1) & 7);
+    voff[u] = d * 128 + lv * 16;
+  }
+
+  // this workgroup's XCD and its item range (balanced by cumulative kept tiles)
+  const int xcd = blockIdx.x & 7;
+  const int64_t total = a.row_ptr[g.rows];
+  int64_t lo_t, hi_t;
+  {
+    auto first_item_with_cost = [&](int64_t target) {
+      int64_t lo = 0, hi = a.items;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (item_cost_prefix(a, mid + 1) > target) hi = mid; else lo = mid + 1;
+      }
+      return lo;
+    };
+    lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
+    hi_t = xcd == 7 ? a.items : first_item_with_cost(total * (xcd + 1) / 8);
+  }
 
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(a.counter, 1);
+    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
     __syncthreads();
-    const int64_t r = s_item;
-    if (r >= g.rows) break;
-    const int64_t bh = r / g.S;
-    const int i = (int)(r - bh * g.S);
-    const int beg = a.row_ptr[r], end = a.row_ptr[r + 1];
-    const uint16_t* kh = a.k + (size_t)bh * g.L * kD;
-    const uint16_t* vth = a.vt + (size_t)bh * g.S * kD * 64;
+    const int64_t item = s_item;
+    if (item >= hi_t) break;
+    const int64_t bh = item / a.pairs;
+    const int i0 = 2 * (int)(item - bh * a.pairs);
+    const int64_t r0 = bh * g.S + i0;
+    const bool two = i0 + 1 < g.S;
+    const bool has_q = qb == 0 || two;
+    int pa = a.row_ptr[r0], ea = a.row_ptr[r0 + 1];
+    int pb = two ? a.row_ptr[r0 + 1] : 0, eb = two ? a.row_ptr[r0 + 2] : 0;
+
+    const uint8_t* kh = (const uint8_t*)(a.k + (size_t)bh * g.L * kD);
+    const uint8_t* vth = (const uint8_t*)(a.vt + (size_t)bh * g.S * kD * 64);
+
+    // union walk over the two ascending key lists (wave-uniform scalars)
+    auto next_tile = [&](int& j, bool& ka, bool& kb) {
+      const int ja = pa < ea ? a.col_idx[pa] : 0x7fffffff;
+      const int jb = pb < eb ? a.col_idx[pb] : 0x7fffffff;
+      j = min(ja, jb);
+      ka = ja == j;
+      kb = jb == j;
+      pa += ka;
+      pb += kb;
+    };
+    auto issue = [&](int j, int stage) {
+      const int jc = min(max(j, 0), g.S - 1);     // malformed ids stay in bounds
+      const uint8_t* kb_ = kh + (size_t)block_base_row(g, jc) * kD * 2;
+      const uint8_t* vb_ = vth + (size_t)jc * kD * 64 * 2;
+      uint8_t* st = smem + stage * kStage;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb_ + koff[u]), (lds_void*)(st + (4 * wave + u) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb_ + voff[u]), (lds_void*)(st + kVt + (4 * wave + u) * 1024), 16,
+                                         0, 0);
+      }
+    };
 
     bf16x8 qreg[8];
-    {
-      const uint16_t* qrow = a.q + ((size_t)bh * g.L + block_token_row(g, i, 32 * wave + l32)) * kD + 8 * h;
+    if (has_q) {
+      const int qtok = block_base_row(g, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
+      const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
 #pragma unroll
       for (int s = 0; s < 8; ++s) qreg[s] = *(const bf16x8*)(qrow + 16 * s);
     }
@@ -103,114 +200,120 @@ __global__ void __launch_bounds__(128) attn_bf16_kernel(AttnBf16Args a) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
 
-    uint4 kst[8], vst[8];
-    const int lrow = tid >> 4, lchunk = tid & 15;
-    auto load_tile = [&](int j) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        kst[u] = *(const uint4*)(kh + (size_t)block_token_row(g, j, lrow + 8 * u) * kD + lchunk * 8);
-      const uint16_t* vb = vth + (size_t)j * kD * 64;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) vst[u] = *(const uint4*)(vb + (tid + 128 * u) * 8);
-    };
-    // ids outside [0, S) are clamped: a malformed CSR gives wrong values, never a stray access
-    auto col = [&](int t) { return min(max(a.col_idx[t], 0), g.S - 1); };
-    if (beg < end) load_tile(col(beg));
-
-    for (int it = beg; it < end; ++it) {
+    int j;
+    bool ka, kb;
+    next_tile(j, ka, kb);
+    int stage = 0;
+    if (j != 0x7fffffff) issue(j, 0);
+    while (j != 0x7fffffff) {
+      int jn;
+      bool kan, kbn;
+      next_tile(jn, kan, kbn);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (jn != 0x7fffffff) issue(jn, stage ^ 1);
+      const bool mine = qb == 0 ? ka : kb;
+      if (mine) {
+        const uint8_t* st = smem + stage * kStage;
+        f32x16 sacc[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) *(uint4*)(smem + k_lds(lrow + 8 * u, lchunk)) = kst[u];
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int cc = tid + 128 * u;
-        *(uint4*)(smem + v_lds(cc >> 3, cc & 7)) = vst[u];
-      }
-      __syncthreads();
-      if (it + 1 < end) load_tile(col(it + 1));
-
-      f32x16 sacc[2];
+          for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+          for (int s = 0; s < 8; ++s) {
+            const bf16x8 ak = *(const bf16x8*)(st + k_lds(32 * t + l32, 2 * s + h));
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+          }
+        }
+        float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sacc[0][e], sacc[1][e]));
+        mx = pair_max(mx) * c_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          m_ref = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 ak = *(const bf16x8*)(smem + k_lds(32 * t + l32, 2 * s + h));
-          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
+        }
+        bf16x8 pbv[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -m_ref));
+            l_run += p;
+            pbv[2 * t + (e >> 3)][e & 7] = (__bf16)p;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bf16x8 av = *(const bf16x8*)(st + v_lds(32 * u + l32, 2 * s + h));
+            oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+          }
         }
       }
-
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[t][e]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
-
-      bf16x8 pb[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -m_new));
-          l_run += p;
-          pb[2 * t + (e >> 3)][e & 7] = (__bf16)p;
-        }
-      }
-
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 av = *(const bf16x8*)(smem + v_lds(32 * u + l32, 2 * s + h));
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[s], oacc[u], 0, 0, 0);
-        }
-      }
+      j = jn;
+      ka = kan;
+      kb = kbn;
+      stage ^= 1;
     }
 
-    l_run = pair_sum(l_run);
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // an empty row yields zeros
-    const int qrow = 32 * wave + l32;
+    // epilogue: normalise, stage O through LDS (block qb at qb * 16 KB), store coalesced
     __syncthreads();
-    // O tile [64 queries][128 d] bf16 in LDS, 8-byte unit x of row q at x ^ (q & 31)
+    const int qrow = 32 * wq + l32;
+    if (has_q) {
+      l_run = pair_sum(l_run);
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // an empty row yields zeros
+      uint8_t* ob = smem + qb * 16384;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int unit = 8 * u + 2 * rq + h;
-        uint2 w;
-        w.x = pack_bf16x2(oacc[u][4 * rq + 0] * inv, oacc[u][4 * rq + 1] * inv);
-        w.y = pack_bf16x2(oacc[u][4 * rq + 2] * inv, oacc[u][4 * rq + 3] * inv);
-        *(uint2*)(smem + qrow * 256 + ((unit ^ (qrow & 31)) << 3)) = w;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int unit = 8 * u + 2 * rq + h;
+          uint2 w;
+          w.x = pack_bf16x2(oacc[u][4 * rq + 0] * inv, oacc[u][4 * rq + 1] * inv);
+          w.y = pack_bf16x2(oacc[u][4 * rq + 2] * inv, oacc[u][4 * rq + 3] * inv);
+          *(uint2*)(ob + qrow * 256 + ((unit ^ (qrow & 31)) << 3)) = w;
+        }
+      }
+      if (a.lse && h == 0) {
+        const int tok = block_base_row(g, i0 + qb) + (qrow >> 3) * rs + (qrow & 7);
+        a.lse[(size_t)bh * g.L + tok] = (m_ref + log2f(l_run)) * 0.69314718055994531f;
       }
     }
-    if (a.lse && h == 0)
-      a.lse[(size_t)bh * g.L + block_token_row(g, i, qrow)] = (m_run + log2f(l_run)) * 0.69314718055994531f;
     __syncthreads();
-    uint16_t* oh = a.o + (size_t)bh * g.L * kD;
+    {
+      const int sb = tid >> 7;                 // block of the pair this thread stores
+      if (sb == 0 || two) {
+        const int t7 = tid & 127;
+        const int lchunk = t7 & 15;
+        const int base = block_base_row(g, i0 + sb);
+        uint16_t* oh = a.o + (size_t)bh * g.L * kD;
+        const uint8_t* ob = smem + sb * 16384;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = lrow + 8 * u;
-      const uint2 lo = *(const uint2*)(smem + row * 256 + (((2 * lchunk) ^ (row & 31)) << 3));
-      const uint2 hi = *(const uint2*)(smem + row * 256 + (((2 * lchunk + 1) ^ (row & 31)) << 3));
-      *(uint4*)(oh + (size_t)block_token_row(g, i, row) * kD + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int u = 0; u < 8; ++u) {
+          const int row = (t7 >> 4) + 8 * u;
+          const uint2 lo = *(const uint2*)(ob + row * 256 + (((2 * lchunk) ^ (row & 31)) << 3));
+          const uint2 hi = *(const uint2*)(ob + row * 256 + (((2 * lchunk + 1) ^ (row & 31)) << 3));
+          const int tok = base + (row >> 3) * rs + (row & 7);
+          *(uint4*)(oh + (size_t)tok * kD + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      }
     }
   }
 }
 
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counter, int num_cu,
+                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
                             hipStream_t s) {
   AttnBf16Args a;
   a.q = (const uint16_t*)q;
@@ -220,12 +323,13 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.lse = lse;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
-  a.counter = counter;
+  a.counters = counters;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-  int64_t grid = (int64_t)num_cu * 2;   // two resident workgroups per CU
-  if (grid > g.rows) grid = g.rows;
-  attn_bf16_kernel<<<(unsigned)grid, 128, 0, s>>>(a);
+  a.pairs = (g.S + 1) / 2;
+  a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
+  const int grid = ((num_cu * 2 + 7) / 8) * 8;   // two resident workgroups per CU, a multiple of 8 XCDs
+  attn_bf16_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, cons
                           int32_t* col_idx, hipStream_t s);
 // Block-sparse attention forward.
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counter, int num_cu,
+                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
                             hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s);
