@@ -210,7 +210,7 @@ def attend(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, 
     csr = mask.as_struct()
     check(lib().bsa_attend(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), vp.data_ptr(), ctypes.byref(csr),
                            o.data_ptr(), lse.data_ptr() if lse is not None else None,
-                           ws.data_ptr(), ws.numel() if workspace is not None else sz["fwd_ws"], _stream(q.device)))
+                           ws.data_ptr(), ws.numel(), _stream(q.device)))
     return (o, lse) if return_lse else o
 
 

@@ -164,7 +164,7 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
 
 static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const void* k, const void* v,
                              const bsa_csr* mask, const void* o, const float* lse, void* ws, int64_t ws_bytes,
-                             const char* who) {
+                             bool whole_forward, const char* who) {
   int st = geom_or_fail(p, g);
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !o || !mask || !mask->row_ptr || !mask->col_idx)
@@ -172,8 +172,9 @@ static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": misaligned pointer");
   const FwdWs w = fwd_ws_layout(*g);
-  if (!ws || ws_bytes < w.total)
-    return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(w.total) + " bytes");
+  const int64_t need = whole_forward ? w.total : w.vt;   // bsa_attend only uses the counter block
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(need) + " bytes");
   if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace must be 256-byte aligned");
   return BSA_OK;
 }
@@ -214,7 +215,7 @@ int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t str
 int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask, void* o,
                float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
   Geom g;
-  int st = check_attend_args(p, &g, q, k, vp, mask, o, lse, ws, ws_bytes, "bsa_attend");
+  int st = check_attend_args(p, &g, q, k, vp, mask, o, lse, ws, ws_bytes, false, "bsa_attend");
   if (st != BSA_OK) return st;
   return enqueue_attend(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream);
 }
@@ -222,7 +223,7 @@ int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask, void* o,
                 float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
   Geom g;
-  int st = check_attend_args(p, &g, q, k, v, mask, o, lse, ws, ws_bytes, "bsa_forward");
+  int st = check_attend_args(p, &g, q, k, v, mask, o, lse, ws, ws_bytes, true, "bsa_forward");
   if (st != BSA_OK) return st;
   char* base = static_cast<char*>(ws);
   const void* vp = v;

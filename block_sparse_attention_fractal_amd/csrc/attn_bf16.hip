@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   for (;;) {
     if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
     __syncthreads();
-    const int64_t item = s_item;
+    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= hi_t) break;
     const int64_t bh = item / a.pairs;
     const int i0 = 2 * (int)(item - bh * a.pairs);
@@ -165,10 +165,32 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     const uint8_t* kh = (const uint8_t*)(a.k + (size_t)bh * g.L * kD);
     const uint8_t* vth = (const uint8_t*)(a.vt + (size_t)bh * g.S * kD * 64);
 
+    // Each key list is read through a 64-entry window held one entry per lane and
+    // indexed with readlane, so the union walk costs no memory round trip per tile;
+    // a window is refilled (one coalesced load) every 64 entries.
+    int wa_base = pa, wb_base = pb;
+    int wa = wa_base + lane < ea ? a.col_idx[wa_base + lane] : 0x7fffffff;
+    int wb = wb_base + lane < eb ? a.col_idx[wb_base + lane] : 0x7fffffff;
+    auto peek_a = [&]() -> int {
+      if (pa >= ea) return 0x7fffffff;
+      if (pa - wa_base >= 64) {
+        wa_base = pa;
+        wa = wa_base + lane < ea ? a.col_idx[wa_base + lane] : 0x7fffffff;
+      }
+      return __builtin_amdgcn_readlane(wa, pa - wa_base);
+    };
+    auto peek_b = [&]() -> int {
+      if (pb >= eb) return 0x7fffffff;
+      if (pb - wb_base >= 64) {
+        wb_base = pb;
+        wb = wb_base + lane < eb ? a.col_idx[wb_base + lane] : 0x7fffffff;
+      }
+      return __builtin_amdgcn_readlane(wb, pb - wb_base);
+    };
     // union walk over the two ascending key lists (wave-uniform scalars)
     auto next_tile = [&](int& j, bool& ka, bool& kb) {
-      const int ja = pa < ea ? a.col_idx[pa] : 0x7fffffff;
-      const int jb = pb < eb ? a.col_idx[pb] : 0x7fffffff;
+      const int ja = peek_a();
+      const int jb = peek_b();
       j = min(ja, jb);
       ka = ja == j;
       kb = jb == j;

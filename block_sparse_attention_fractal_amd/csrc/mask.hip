@@ -5,9 +5,11 @@
 // Numerics: the cut must agree with a float64 evaluation except where the
 // cumulative mass sits within 1e-4 of 1 - thr.  Block logits reach |z| ~ 10^3
 // for strongly local heads, where float32 cannot even represent the 1e-4-level
-// differences that decide the ordering, so logits, exponentials, the sort keys
-// and the prefix sums are all float64.  MI355X issues float64 FMAs at the same
-// rate as unpacked float32 FMAs, so this costs no throughput.
+// differences that decide the ORDER of the blocks, so pooled means, logits and
+// the selection keys are float64 (MI355X issues float64 FMAs at the same rate
+// as unpacked float32 FMAs).  The masses compared with 1 - thr only need an
+// absolute accuracy well below the band, so they come from float32
+// exponentials summed exactly in fixed point.
 #include <float.h>
 
 #include "kernels.h"
@@ -160,98 +162,254 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 }
 
 // ---------------------------------------------------------------------------
-// CDF cut of one row per workgroup.
+// CDF cut of one row per workgroup, by radix selection instead of a sort.
+//
 //   p_j = exp(z_j - max) / sum; order blocks by (p desc, j asc); c_k = exclusive
-//   prefix of that order; keep position k iff k == 0 or c_k < 1 - thr; thr == 0
-//   keeps all.  Only "candidates" with z_j >= max - lambda enter the sort: each
-//   other block has p_j < exp(-lambda), and lambda (set by the host to
-//   40 + ln S - ln thr) makes their total mass < 1e-17 * thr, so the cut can
-//   never reach them and their omission cannot change the kept set.
+//   prefix mass of that order; keep position k iff k == 0 or c_k < 1 - thr;
+//   thr == 0 keeps all.
+//
+// The order is decided on the float64 logits (p is monotone in z), so it is as
+// exact as the logits.  Only the MASSES enter the comparison with 1 - thr, and
+// for those float32 exponentials (relative error ~1e-6) are far inside the 1e-4
+// band; they are accumulated as exact unsigned fixed-point integers (2^-50
+// units), so every partial sum is independent of summation order and the cut is
+// bitwise deterministic.
+//
+// Selection: the kept set is {key > K*} plus the block(s) with key K*, where K*
+// is the key of the block at which the cumulative mass first reaches 1 - thr.
+// K* is found MSB-first, 8 key bits per pass: a 256-bin histogram of (count,
+// mass) of the blocks still sharing the decided prefix, a suffix scan over the
+// bins, and the bin where the mass crosses the target.  Passes stop when that
+// bin holds a single block; equal keys (exact ties) are resolved by index.
+// Blocks with z < max - lambda are never candidates: lambda (set by the host to
+// 40 + ln S - ln thr) bounds their total mass below 1e-17 * thr, so the cut can
+// never reach them.
 // ---------------------------------------------------------------------------
 constexpr int kMaxS = 4096;
+constexpr int kPerThread = kMaxS / 256;
 
-__device__ __forceinline__ bool before(double ka, int ia, double kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
+// order-preserving map of a double to uint64 (larger value -> larger key);
+// -0.0 and +0.0 are equal values and must share one key
+__device__ __forceinline__ uint64_t order_key(double z) {
+  const uint64_t b = z == 0.0 ? 0ull : (uint64_t)__double_as_longlong(z);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int d) {
+  const uint32_t lo = __shfl_down((uint32_t)v, d, 64), hi = __shfl_down((uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 256-thread reductions: butterfly inside each wave, then the four wave results
+// in a fixed order (deterministic, one barrier).
+template <typename V, typename Op>
+__device__ __forceinline__ V wg_reduce(V v, V* slot4, Op op) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    if constexpr (sizeof(V) == 8) {
+      uint64_t u;
+      __builtin_memcpy(&u, &v, 8);
+      u = shfl_xor_u64(u, m);
+      V o;
+      __builtin_memcpy(&o, &u, 8);
+      v = op(v, o);
+    } else {
+      v = op(v, __shfl_xor(v, m, 64));
+    }
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) slot4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return op(op(slot4[0], slot4[1]), op(slot4[2], slot4[3]));
 }
 
 __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ z, Geom g, double thr, double lambda,
                                                      int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
                                                      int32_t* __restrict__ counts, int words) {
-  __shared__ double key[kMaxS];
-  __shared__ int idx[kMaxS];
-  __shared__ double red[256];
-  __shared__ int ired[256];
+  __shared__ uint64_t umass[256];
+  __shared__ uint32_t ucount[256];
   __shared__ uint32_t bm[kMaxS / 32];
-  const int tid = threadIdx.x;
+  __shared__ uint32_t tie[kMaxS / 32];
+  __shared__ double dslot[4];
+  __shared__ uint64_t uslot[4];
+  __shared__ uint64_t s_prefix, s_above;
+  __shared__ uint32_t s_cnt;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int S = g.S;
   const int64_t r = blockIdx.x;
   const int i = (int)(r % S);
   const double* zr = z + r * S;
 
-  for (int w = tid; w < words; w += 256) bm[w] = 0u;
+  for (int w = tid; w < kMaxS / 32; w += 256) bm[w] = 0u;
 
   if (thr == 0.0) {
     __syncthreads();
     for (int j = tid; j < S; j += 256) atomicOr(&bm[j >> 5], 1u << (j & 31));
   } else {
+    double zv[kPerThread];
     double m = -DBL_MAX;
-    for (int j = tid; j < S; j += 256) m = fmax(m, zr[j]);
-    m = block_reduce_max(m, red);
-    double s = 0.0;
-    int nc = 0;
-    for (int j = tid; j < S; j += 256) {
-      const double zj = zr[j];
-      s += exp(zj - m);
-      nc += (zj - m >= -lambda);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int j = tid + 256 * k;
+      zv[k] = j < S ? zr[j] : -DBL_MAX;
+      m = fmax(m, zv[k]);
     }
-    const double sum = block_reduce_sum(s, red);
-    int ntot;
-    int off = block_exclusive_scan<int>(nc, ired, &ntot);
-    for (int j = tid; j < S; j += 256) {
-      const double zj = zr[j];
-      if (zj - m >= -lambda) {
-        key[off] = exp(zj - m);
-        idx[off] = j;
-        ++off;
+    m = wg_reduce(m, dslot, [](double a, double b) { return fmax(a, b); });
+    // candidates: fixed-point masses (2^-50 units, S * 2^50 < 2^63) and order keys
+    uint64_t key[kPerThread], w[kPerThread];
+    uint64_t wsum = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const double d = zv[k] - m;
+      const bool cand = (tid + 256 * k < S) && d >= -lambda;
+      const float e = cand ? __builtin_amdgcn_exp2f((float)d * 1.44269504088896341f) : 0.f;
+      w[k] = cand ? (uint64_t)((double)e * 1125899906842624.0) : 0ull;
+      key[k] = cand ? order_key(zv[k]) : 0ull;
+      wsum += w[k];
+    }
+    const uint64_t total = wg_reduce(wsum, uslot, [](uint64_t a, uint64_t b) { return a + b; });
+    const double target = (1.0 - thr) * (double)total;        // keep while exclusive prefix < target
+    // Pass 0: 256 uniform buckets of d = z - max over [dmin, 0].  The bucket index
+    // is a monotone function of z, so it refines the order without breaking it,
+    // and it spreads even near-uniform rows thinly over the bins (few LDS atomic
+    // collisions).  Later passes use the exact key, inside the crossing bucket only.
+    double dmin = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+      if (w[k] != 0ull) dmin = fmin(dmin, zv[k] - m);
+    dmin = wg_reduce(dmin, dslot, [](double a, double b) { return fmin(a, b); });
+    const double bscale = dmin < 0.0 ? 255.999 / (-dmin) : 0.0;
+    int bucket[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) bucket[k] = (int)((zv[k] - m - dmin) * bscale);
+    ucount[tid] = 0u;
+    umass[tid] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+      if (w[k] != 0ull) {
+        atomicAdd(&ucount[bucket[k]], 1u);
+        atomicAdd((unsigned long long*)&umass[bucket[k]], (unsigned long long)w[k]);
+      }
+    __syncthreads();
+    auto crossing_bin = [&](uint64_t above_in, uint64_t prefix_in, int shift_in) {
+      // lane l owns bins 4l..4l+3; suffix sums over bins (bin 255 = largest keys)
+      uint64_t mb[4];
+      uint32_t cb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) { mb[x] = umass[4 * lane + x]; cb[x] = ucount[4 * lane + x]; }
+      const uint64_t lane_tot = mb[0] + mb[1] + mb[2] + mb[3];
+      uint64_t suf = lane_tot;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t o = shfl_down_u64(suf, d);
+        if (lane + d < 64) suf += o;
+      }
+      uint64_t run = suf - lane_tot;
+#pragma unroll
+      for (int x = 3; x >= 0; --x) {
+        const uint64_t excl = run;
+        run += mb[x];
+        if (cb[x] != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + run)) {
+          s_prefix = prefix_in | ((uint64_t)(4 * lane + x) << shift_in);
+          s_above = above_in + excl;
+          s_cnt = cb[x];
+        }
+      }
+    };
+    if (tid == 0) { s_prefix = 0; s_above = 0; s_cnt = 0; }   // unreachable target: keep every candidate
+    __syncthreads();
+    if (tid < 64) crossing_bin(0, 0, 0);
+    __syncthreads();
+    const int b0 = (int)s_prefix;
+    uint64_t above = s_above;
+    uint32_t cnt_bin = s_cnt;
+    // exact passes over the keys of the crossing bucket
+    uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const bool in = w[k] != 0ull && bucket[k] == b0;
+      if (!in) w[k] = w[k] != 0ull && bucket[k] > b0 ? w[k] : 0ull;  // keep "above" blocks, drop the rest
+      if (in) {
+        kmax = key[k] > kmax ? key[k] : kmax;
+        kmin = key[k] < kmin ? key[k] : kmin;
       }
     }
-    int n2 = 2;
-    while (n2 < ntot) n2 <<= 1;
-    for (int k = ntot + tid; k < n2; k += 256) {
-      key[k] = -1.0;
-      idx[k] = 0x7fffffff;
-    }
-    __syncthreads();
-    // bitonic sort, final order: "before" first
-    for (int size = 2; size <= n2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = tid; t < (n2 >> 1); t += 256) {
-          const int lo = 2 * stride * (t / stride) + (t % stride);
-          const int hi = lo + stride;
-          const double klo = key[lo], khi = key[hi];
-          const int ilo = idx[lo], ihi = idx[hi];
-          const bool up = (lo & size) == 0;
-          const bool sw = up ? before(khi, ihi, klo, ilo) : before(klo, ilo, khi, ihi);
-          if (sw) {
-            key[lo] = khi; key[hi] = klo;
-            idx[lo] = ihi; idx[hi] = ilo;
+    kmax = wg_reduce(kmax, uslot, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+    kmin = wg_reduce(kmin, uslot, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
+    const uint64_t diff = kmax ^ kmin;
+    int shift = diff == 0 ? 0 : ((63 - __clzll(diff)) & ~7);
+    uint64_t prefix = shift >= 56 ? 0ull : (kmax & (~0ull << (shift + 8)));
+    if (cnt_bin > 1u) {
+      if (tid == 0) { s_prefix = prefix; s_cnt = 0; }
+      for (;;) {
+        ucount[tid] = 0u;
+        umass[tid] = 0ull;
+        __syncthreads();
+        const uint64_t hi_mask = shift >= 56 ? 0ull : (~0ull << (shift + 8));
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+          if (w[k] != 0ull && bucket[k] == b0 && (key[k] & hi_mask) == prefix) {
+            const int d = (int)((key[k] >> shift) & 255);
+            atomicAdd(&ucount[d], 1u);
+            atomicAdd((unsigned long long*)&umass[d], (unsigned long long)w[k]);
           }
         }
         __syncthreads();
+        if (tid < 64) crossing_bin(above, prefix, shift);
+        __syncthreads();
+        prefix = s_prefix;
+        above = s_above;
+        cnt_bin = s_cnt;
+        if (cnt_bin <= 1u || shift == 0) break;
+        shift -= 8;
       }
+    } else {
+      prefix = cnt_bin == 0u ? 0ull : kmax;   // one block in the crossing bucket: its key; none: keep all
+      shift = 0;
     }
-    // exclusive prefix of p = key / sum over the sorted candidates
-    const int ept = (ntot + 255) / 256;           // contiguous elements per thread
-    const int k0 = tid * ept;
-    const int k1 = min(k0 + ept, ntot);
-    double loc = 0.0;
-    for (int k = k0; k < k1; ++k) loc += key[k] / sum;
-    double tot;
-    double c = block_exclusive_scan<double>(loc, red, &tot);
-    const double target = 1.0 - thr;
-    for (int k = k0; k < k1; ++k) {
-      if (k == 0 || c < target) atomicOr(&bm[idx[k] >> 5], 1u << (idx[k] & 31));
-      c += key[k] / sum;
+    // keep: keys above the final bin, and the final bin itself when it holds one block
+    const uint64_t lo_key = prefix;
+    const uint64_t hi_key = shift == 0 ? prefix : (prefix | ((1ull << shift) - 1));
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      if (w[k] == 0ull) continue;
+      const int j = tid + 256 * k;
+      if (bucket[k] > b0 || key[k] > hi_key || (cnt_bin <= 1u && key[k] >= lo_key))
+        atomicOr(&bm[j >> 5], 1u << (j & 31));
+    }
+    if (cnt_bin > 1u) {
+      // exact ties at K* = prefix: keep the lowest-index ones until the mass reaches the target
+      for (int x = tid; x < kMaxS / 32; x += 256) tie[x] = 0u;
+      __syncthreads();
+      uint64_t wt = 0;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k)
+        if (w[k] != 0ull && bucket[k] == b0 && key[k] == prefix) {
+          atomicOr(&tie[(tid + 256 * k) >> 5], 1u << ((tid + 256 * k) & 31));
+          wt = w[k];
+        }
+      if (wt != 0ull) umass[0] = wt;            // all ties share one mass
+      __syncthreads();
+      if (tid == 0) {
+        const uint64_t wtie = umass[0];
+        uint64_t acc = above;
+        for (int x = 0; x < (S + 31) / 32; ++x) {
+          uint32_t bits = tie[x];
+          while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if ((double)acc < target) {
+              bm[x] |= 1u << b;
+              acc += wtie;
+            }
+          }
+        }
+      }
     }
   }
   if (win_t >= 0) {
@@ -264,15 +422,14 @@ __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ 
     }
   }
   __syncthreads();
-  int pc = 0;
-  for (int w = tid; w < words; w += 256) {
-    const uint32_t v = bm[w];
-    bitmap[r * words + w] = v;
+  uint32_t pc = 0;
+  for (int w2 = tid; w2 < words; w2 += 256) {
+    const uint32_t v = bm[w2];
+    bitmap[r * words + w2] = v;
     pc += __popc(v);
   }
-  int total;
-  block_exclusive_scan<int>(pc, ired, &total);
-  if (tid == 0) counts[r] = total;
+  pc = wg_reduce(pc, ucount, [](uint32_t a, uint32_t b) { return a + b; });
+  if (tid == 0) counts[r] = (int32_t)pc;
 }
 
 hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h, int win_w,

@@ -157,8 +157,8 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
  * order 0-3, 8-11, 4-7, 12-15.  vt: device buffer of batch*heads*L*head_dim
  * bf16 elements (the size of V), 16-byte aligned.
  * bsa_attend runs the attention kernel; `vp` is the output of bsa_prepare_v for
- * bf16, or the V tensor itself (p->layout order) for f32.  ws: at least
- * fwd_ws bytes; only its first 256 bytes (work counters) are used. */
+ * bf16, or the V tensor itself (p->layout order) for f32.  ws: at least 256
+ * bytes, 256-byte aligned (work counters; contents on entry do not matter). */
 int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream);
 int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
                void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);

@@ -2,7 +2,7 @@
 
 Small cases (configs 0 and 1 and hand-made edge cases) are compared element by
 element; the full Wan2.1/HunyuanVideo-scale configurations compare the whole
-CSR mask and a sample of attention rows (see test_gpu_fullsize.py)."""
+CSR mask and a sample of attention rows (see test_gpu_scale.py)."""
 import numpy as np
 import pytest
 import torch
@@ -242,3 +242,51 @@ def test_max_blocks_per_head():
     ro = oracle_attention_rows(inputs, cfg, res["row_ptr"], res["col_idx"], rows)
     go = gpu_rows_fractal(res["o"], None, cfg, rows, 1)
     compare_outputs(np.stack([go[r][0] for r in rows]), np.stack([ro[r][0] for r in rows]), "bf16")
+
+
+@pytest.mark.parametrize("thr", [0.1, 0.25, 0.5, 0.05])
+def test_mask_exact_ties_uniform_rows(thr):
+    """Every key block identical -> every reduced-map row is exactly uniform: the kept
+    set is the ceil((1-thr)*S) lowest block ids (ties by index), as in the oracle."""
+    cfg = small_cfg(nh=2, T=2, H=16, W=32, thr=thr, seed=21)
+    inputs = make_inputs(cfg)
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    kb = inputs["k_bits"][:, :, src[:64]]                      # first block, fractal order
+    k_bits = np.empty_like(inputs["k_bits"])
+    k_bits[:, :, src] = np.tile(kb, (1, 1, cfg.S, 1))         # every block = block 0
+    inputs["k_bits"] = k_bits
+    from workloads import bf16_bits_to_f32
+    inputs["k"] = bf16_bits_to_f32(k_bits)
+    g = grid_of(cfg)
+    q, k = to_device(inputs, "q", "bf16"), to_device(inputs, "k", "bf16")
+    mask = bsa.build_mask(q, k, g, thr)
+    rp = mask.row_ptr.cpu().numpy()
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    ref = oracle_mask(cfg, inputs, thr)
+    assert np.all(ref["A"] == ref["A"][..., :1])               # the oracle sees exact ties too
+    compare_masks(rp, ci, ref, thr, cfg.S)
+    K = int(np.ceil((1 - thr) * cfg.S))
+    assert np.all(np.diff(rp) == K)
+    assert np.array_equal(ci.reshape(-1, K), np.tile(np.arange(K), (len(rp) - 1, 1)))
+
+
+def test_mask_partial_ties():
+    """Half of the key blocks duplicate another block: many exact ties at varying ranks."""
+    cfg = small_cfg(nh=2, T=3, H=24, W=40, thr=0.2, amp=0.5, seed=22)
+    inputs = make_inputs(cfg)
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    kf = inputs["k_bits"][:, :, src].copy()
+    rng = np.random.default_rng(5)
+    for b in range(0, cfg.S, 2):
+        o = int(rng.integers(0, cfg.S))
+        kf[:, :, b * 64:(b + 1) * 64] = kf[:, :, o * 64:(o + 1) * 64]
+    k_bits = np.empty_like(kf)
+    k_bits[:, :, src] = kf
+    from workloads import bf16_bits_to_f32
+    inputs["k_bits"], inputs["k"] = k_bits, bf16_bits_to_f32(k_bits)
+    g = grid_of(cfg)
+    q, k = to_device(inputs, "q", "bf16"), to_device(inputs, "k", "bf16")
+    mask = bsa.build_mask(q, k, g, cfg.thr)
+    rp = mask.row_ptr.cpu().numpy()
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    compare_masks(rp, ci, oracle_mask(cfg, inputs), cfg.thr, cfg.S)
