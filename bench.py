@@ -28,24 +28,30 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_hunyuan_hybrid_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", "attn_bf16.hip")
 
 
 def kernel_sha() -> str:
+    """Fingerprint of the attention kernel: its source plus the flags it is built with."""
+    from block_sparse_attention_fractal_amd import build as _b
+    h = hashlib.sha256()
     with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        h.update(f.read())
+    h.update(repr(_b._flags()[:-4] + _b.EXTRA.get("attn_bf16.hip", [])).encode())
+    return h.hexdigest()[:16]
 
 
-def traffic_for_current_kernel():
+def traffic_for_current_kernel(cfg_idx: int):
     """HBM bytes per attention launch from the committed PMC summary, or None when the
-    kernel source changed since the counters were taken."""
+    kernel (source or flags) changed since the counters were taken, or the counters
+    were taken on another workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel_sha") != kernel_sha() or t.get("config") != cfg_idx:
         return None
     return t.get("bytes_per_launch")
 
@@ -223,7 +229,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_for_current_kernel(),
+            "traffic": traffic_for_current_kernel(cfg.idx),
             "kernel": "attn_bf16_kernel",
             "flops_per_launch": exec_flops,
             "avg_launch_ms": round(attn_ms, 4),
