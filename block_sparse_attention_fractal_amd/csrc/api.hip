@@ -156,7 +156,8 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
   if (e == hipSuccess)
     e = launch_select(g, z, mp->thr, lambda, win ? mp->win_t : -1, win ? mp->win_h : -1, win ? mp->win_w : -1,
                       bitmap, counts, w.words, stream);
-  if (e == hipSuccess) e = launch_scan(g, counts, out->row_ptr, out->nnz, stream);
+  if (e == hipSuccess)
+    e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
   if (e == hipSuccess) e = launch_compact(g, bitmap, w.words, out->row_ptr, out->col_idx, stream);
   if (e != hipSuccess) return hip_fail(e, "bsa_build_mask launch");
   return BSA_OK;

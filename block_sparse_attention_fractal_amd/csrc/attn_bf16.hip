@@ -57,6 +57,7 @@ struct AttnBf16Args {
   int32_t* counters;   // 8 per-XCD item counters
   Geom g;
   float c_log2;        // log2(e) / sqrt(D)
+  uint32_t magic_wp, magic_hp;   // floor(2^32/d)+1: exact n/d = (n*magic)>>32 for n, d < 2^16
   int32_t pairs;       // query-block pairs per head = ceil(S/2)
   int32_t items;       // B*heads*pairs
 };
@@ -87,14 +88,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic) {
+  return (uint32_t)(((uint64_t)n * magic) >> 32);
+}
+
 // First token row (in the tensor's own layout) of block j; token m of the block
 // sits rs*(m/8) + m%8 rows further (rs = W for original order, 8 for fractal).
-__device__ __forceinline__ int block_base_row(const Geom& g, int j) {
+// Block ids and patch counts are < 2^16, so the divisions use multiply-high.
+__device__ __forceinline__ int block_base_row(const AttnBf16Args& a, int j) {
+  const Geom& g = a.g;
   if (g.layout == 1) return j * 64;
-  const int px = j % g.Wp;
-  const int rest = j / g.Wp;
-  const int py = rest % g.Hp;
-  const int t = rest / g.Hp;
+  const int rest = (int)div_magic((uint32_t)j, a.magic_wp);
+  const int px = j - rest * g.Wp;
+  const int t = (int)div_magic((uint32_t)rest, a.magic_hp);
+  const int py = rest - t * g.Hp;
   return (t * g.H + py * 8) * g.W + px * 8;
 }
 
@@ -199,7 +206,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     };
     auto issue = [&](int j, int stage) {
       const int jc = min(max(j, 0), g.S - 1);     // malformed ids stay in bounds
-      const uint8_t* kb_ = kh + (size_t)block_base_row(g, jc) * kD * 2;
+      const uint8_t* kb_ = kh + (size_t)block_base_row(a, jc) * kD * 2;
       const uint8_t* vb_ = vth + (size_t)jc * kD * 64 * 2;
       uint8_t* st = smem + stage * kStage;
 #pragma unroll
@@ -212,7 +219,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 
     bf16x8 qreg[8];
     if (has_q) {
-      const int qtok = block_base_row(g, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
+      const int qtok = block_base_row(a, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
       const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
 #pragma unroll
       for (int s = 0; s < 8; ++s) qreg[s] = *(const bf16x8*)(qrow + 16 * s);
@@ -308,7 +315,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         }
       }
       if (a.lse && h == 0) {
-        const int tok = block_base_row(g, i0 + qb) + (qrow >> 3) * rs + (qrow & 7);
+        const int tok = block_base_row(a, i0 + qb) + (qrow >> 3) * rs + (qrow & 7);
         a.lse[(size_t)bh * g.L + tok] = (m_ref + log2f(l_run)) * 0.69314718055994531f;
       }
     }
@@ -318,7 +325,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       if (sb == 0 || two) {
         const int t7 = tid & 127;
         const int lchunk = t7 & 15;
-        const int base = block_base_row(g, i0 + sb);
+        const int base = block_base_row(a, i0 + sb);
         uint16_t* oh = a.o + (size_t)bh * g.L * kD;
         const uint8_t* ob = smem + sb * 16384;
 #pragma unroll
@@ -348,6 +355,8 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.counters = counters;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
+  a.magic_wp = (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
   const int grid = ((num_cu * 2 + 7) / 8) * 8;   // two resident workgroups per CU, a multiple of 8 XCDs

@@ -23,7 +23,9 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h,
                          int win_w, uint32_t* bitmap, int32_t* counts, int words, hipStream_t s);
 // Exclusive scan of counts -> row_ptr [rows+1]; row_ptr[rows] also copied to nnz (if not null).
-hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* nnz, hipStream_t s);
+// chunk_sums: ceil(rows/1024) ints of scratch.
+hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* chunk_sums, int32_t* nnz,
+                       hipStream_t s);
 // Bitmap -> ascending col_idx at row_ptr offsets.
 hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr,
                           int32_t* col_idx, hipStream_t s);

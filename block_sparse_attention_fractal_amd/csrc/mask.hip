@@ -439,76 +439,106 @@ hipError_t launch_select(const Geom& g, const double* z, double thr, double lamb
 }
 
 // ---------------------------------------------------------------------------
-// row_ptr = exclusive scan of counts (one 1024-thread workgroup).
+// row_ptr = exclusive scan of counts, in two launches: per-chunk totals, then
+// every chunk scans its own counts after summing the totals of the chunks
+// before it (at most rows/1024 of them).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr,
-                                                    int32_t* __restrict__ nnz, int64_t rows) {
-  __shared__ int32_t buf[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (rows + 1023) / 1024;
-  const int64_t a = tid * per;
-  const int64_t b = a + per < rows ? a + per : rows;
-  int32_t loc = 0;
-  for (int64_t k = a; k < b; ++k) loc += counts[k];
-  buf[tid] = loc;
+constexpr int kScanChunk = 1024;
+
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// 1024-thread exclusive scan of one value per thread; returns (exclusive, total)
+__device__ __forceinline__ int32_t wg1024_excl_scan(int32_t v, int32_t* wsum, int32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t incl = wave_incl_scan(v, lane);
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  if (w == 0) {
+    const int32_t x = lane < 16 ? wsum[lane] : 0;
+    const int32_t xi = wave_incl_scan(x, lane);
+    if (lane < 16) wsum[lane] = xi - x;
+    if (lane == 15) wsum[16] = xi;
   }
-  int32_t run = buf[tid] - loc;
-  for (int64_t k = a; k < b; ++k) {
-    row_ptr[k] = run;
-    run += counts[k];
+  __syncthreads();
+  *total = wsum[16];
+  return wsum[w] + incl - v;
+}
+
+__global__ void __launch_bounds__(1024) chunk_sum_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ sums,
+                                                         int64_t rows) {
+  __shared__ int32_t wsum[17];
+  const int64_t r = (int64_t)blockIdx.x * kScanChunk + threadIdx.x;
+  int32_t tot;
+  wg1024_excl_scan(r < rows ? counts[r] : 0, wsum, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+__global__ void __launch_bounds__(1024) chunk_scan_kernel(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ sums, int32_t* __restrict__ row_ptr,
+                                                          int32_t* __restrict__ nnz, int64_t rows, int nchunks) {
+  __shared__ int32_t wsum[17];
+  __shared__ int32_t s_base;
+  const int tid = threadIdx.x;
+  // offset of this chunk: sum of the chunk totals before it (fixed order)
+  if (tid < 64) {
+    int32_t acc = 0;
+    for (int c = tid; c < (int)blockIdx.x; c += 64) acc += sums[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (tid == 0) s_base = acc;
   }
-  if (tid == 1023) {
-    row_ptr[rows] = buf[1023];
-    if (nnz) *nnz = buf[1023];
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * kScanChunk + tid;
+  const int32_t v = r < rows ? counts[r] : 0;
+  int32_t tot;
+  const int32_t ex = wg1024_excl_scan(v, wsum, &tot) + s_base;
+  if (r < rows) row_ptr[r] = ex;
+  if (blockIdx.x == (unsigned)(nchunks - 1) && tid == 0) {
+    row_ptr[rows] = s_base + tot;
+    if (nnz) *nnz = s_base + tot;
   }
 }
 
-hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* nnz, hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(counts, row_ptr, nnz, g.rows);
+hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* chunk_sums, int32_t* nnz,
+                       hipStream_t s) {
+  const int nchunks = (int)((g.rows + kScanChunk - 1) / kScanChunk);
+  chunk_sum_kernel<<<nchunks, kScanChunk, 0, s>>>(counts, chunk_sums, g.rows);
+  chunk_scan_kernel<<<nchunks, kScanChunk, 0, s>>>(counts, chunk_sums, row_ptr, nnz, g.rows, nchunks);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Bitmap -> ascending column list; one wavefront per row.
+// Bitmap -> ascending column list; one wavefront per row.  Each lane tests one
+// block id per step and a ballot turns the bits into coalesced output slots.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) compact_kernel(const uint32_t* __restrict__ bitmap, int words,
                                                       const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-                                                      int64_t rows) {
+                                                      int64_t rows, int S) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const uint32_t* bm = bitmap + r * words;
   int32_t base = row_ptr[r];
-  for (int w0 = 0; w0 < words; w0 += 64) {
-    const int w = w0 + lane;
-    const uint32_t v = w < words ? bm[w] : 0u;
-    const int pc = __popc(v);
-    int incl = pc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    int pos = base + incl - pc;
-    uint32_t bits = v;
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      col_idx[pos++] = w * 32 + b;
-      bits &= bits - 1;
-    }
-    base += __shfl(incl, 63, 64);
+  for (int j0 = 0; j0 < S; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t wv = bm[min(j >> 5, words - 1)];
+    const bool on = j < S && ((wv >> (j & 31)) & 1u);
+    const uint64_t mask = __ballot(on);
+    if (on) col_idx[base + __popcll(mask & ((1ull << lane) - 1))] = j;
+    base += __popcll(mask);
   }
 }
 
 hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr, int32_t* col_idx,
                           hipStream_t s) {
-  compact_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, s>>>(bitmap, words, row_ptr, col_idx, g.rows);
+  compact_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, s>>>(bitmap, words, row_ptr, col_idx, g.rows, g.S);
   return hipGetLastError();
 }
 

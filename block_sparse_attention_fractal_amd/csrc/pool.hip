@@ -31,7 +31,8 @@ __device__ __forceinline__ void add_chunk<float>(double* acc, const uint4& c) {
   acc[3] += (double)__uint_as_float(c.w);
 }
 
-// grid.x = rows (bh*S + i), grid.y = 2 (0: Q, 1: K); 256 threads.
+// grid.x = rows (bh*S + i); one 256-thread workgroup pools block i of both Q
+// and K, so every thread has 2*RPT independent 16-byte loads in flight.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    double* __restrict__ qp, double* __restrict__ kp, Geom g) {
@@ -39,38 +40,44 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
   constexpr int CPR = D / EPC;             // chunks per row
   constexpr int RG = 256 / CPR;            // row groups
   constexpr int RPT = 64 / RG;             // rows per thread
-  __shared__ double part[RG][D + 1];
+  __shared__ double part[2][RG][D + 1];
   const int64_t r = blockIdx.x;
   const int64_t bh = r / g.S;
   const int32_t i = (int32_t)(r - bh * g.S);
-  const T* x = (blockIdx.y == 0 ? q : k) + (size_t)bh * g.L * D;
-  double* out = (blockIdx.y == 0 ? qp : kp) + (size_t)r * D;
   const int tid = threadIdx.x;
   const int c = tid % CPR, rg = tid / CPR;
-  double acc[EPC];
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  uint4 buf[RPT];
+  uint4 bq[RPT], bk[RPT];
 #pragma unroll
   for (int it = 0; it < RPT; ++it) {
-    const int m = rg + it * RG;
-    buf[it] = *(const uint4*)(x + (size_t)block_token_row(g, i, m) * D + c * EPC);
+    const size_t off = ((size_t)bh * g.L + block_token_row(g, i, rg + it * RG)) * D + c * EPC;
+    bq[it] = *(const uint4*)(q + off);
+    bk[it] = *(const uint4*)(k + off);
+  }
+  double aq[EPC], ak[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) aq[e] = ak[e] = 0.0;
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    add_chunk<T>(aq, bq[it]);
+    add_chunk<T>(ak, bk[it]);
   }
 #pragma unroll
-  for (int it = 0; it < RPT; ++it) add_chunk<T>(acc, buf[it]);
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) part[rg][c * EPC + e] = acc[e];
+  for (int e = 0; e < EPC; ++e) {
+    part[0][rg][c * EPC + e] = aq[e];
+    part[1][rg][c * EPC + e] = ak[e];
+  }
   __syncthreads();
-  for (int d = tid; d < D; d += 256) {
+  for (int x = tid; x < 2 * D; x += 256) {
+    const int t = x / D, d = x - t * D;
     double s = 0.0;
 #pragma unroll
-    for (int j = 0; j < RG; ++j) s += part[j][d];
-    out[d] = s * (1.0 / 64.0);
+    for (int j = 0; j < RG; ++j) s += part[t][j][d];
+    (t == 0 ? qp : kp)[(size_t)r * D + d] = s * (1.0 / 64.0);
   }
 }
 
 hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, double* kp, hipStream_t s) {
-  dim3 grid((unsigned)g.rows, 2);
+  dim3 grid((unsigned)g.rows);
   if (g.dtype == 1)
     pool_kernel<uint16_t, 128><<<grid, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, qp, kp, g);
   else if (g.D == 64)

@@ -75,6 +75,7 @@ MaskWs mask_ws_layout(const Geom& g) {
   w.z = off; off = align256(off + g.rows * (int64_t)g.S * 8);
   w.counts = off; off = align256(off + g.rows * 4);
   w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
+  w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
   w.total = off;
   return w;
 }

@@ -60,9 +60,10 @@ def test_query_sizes(lib, B, nh, T, H, W):
     assert st == 0
     S = T * H * W // 64
     assert rows == B * nh * S and max_nnz == rows * S
-    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap (each 256-aligned)
+    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap, scan chunk sums (each 256-aligned)
     a = lambda x: (x + 255) // 256 * 256
-    assert mws == a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
+    assert mws == (a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
+                   + a((rows + 1023) // 1024 * 4))
     assert fws == 256 + a(B * nh * T * H * W * D * 2)
     assert mws % 256 == 0 and fws % 256 == 0
 
