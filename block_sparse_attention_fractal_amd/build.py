@@ -36,9 +36,10 @@ def _flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
-# per-file extras: the attention kernel never sees NaNs in its max reductions,
-# which lets the compiler drop the NaN-quieting v_max x,x before every fmaxf
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"]}
+# per-file extras: the attention and mask kernels never see NaNs in their max/min
+# reductions (finite inputs), which lets the compiler drop the NaN-quieting
+# v_max x,x before every fmax
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"], "mask.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -17,8 +17,11 @@
 //     kept-tile count), so concurrently running items of one XCD share a head and
 //     its K/V tiles in that XCD's L2;
 //   * K (64 x 128) and V^T (128 x 64) tiles move global -> LDS with direct
-//     (VGPR-free) 16-byte loads into a double buffer; the next tile's loads are
-//     issued right after the barrier that publishes the current one;
+//     (VGPR-free) 16-byte buffer loads into a double buffer: the per-lane part
+//     of each address is a constant register, the tile part a scalar offset;
+//     the next tile's loads are issued right after the barrier that publishes
+//     the current one, and the loop is unrolled over the two stages so every
+//     LDS address is a per-lane constant plus an immediate;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
 //     columns from registers): each lane's accumulator holds 32 keys of ONE
 //     query, so the online-softmax state is per lane;
@@ -36,6 +39,8 @@
 // pair "element e of half h" of A and B, so the physical k order inside the
 // instruction does not matter.
 #include <math.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -204,16 +209,24 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       pa += ka;
       pb += kb;
     };
-    auto issue = [&](int j, int stage) {
+    // K and V^T of this head as raw buffers: the per-lane part of each 16-byte load
+    // is a constant VGPR offset, the tile part a scalar offset; loads past the
+    // head's extent return zeros instead of touching other memory
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vth, (short)0, g.S * kD * 64 * 2, 0x00020000);
+    auto issue = [&](int j, auto stage_c) {
+      constexpr int stage = decltype(stage_c)::value;
       const int jc = min(max(j, 0), g.S - 1);     // malformed ids stay in bounds
-      const uint8_t* kb_ = kh + (size_t)block_base_row(a, jc) * kD * 2;
-      const uint8_t* vb_ = vth + (size_t)jc * kD * 64 * 2;
+      const int ks = block_base_row(a, jc) * kD * 2;
+      const int vs = jc * kD * 64 * 2;
       uint8_t* st = smem + stage * kStage;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_global_load_lds((gbl_void*)(kb_ + koff[u]), (lds_void*)(st + (4 * wave + u) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(vb_ + voff[u]), (lds_void*)(st + kVt + (4 * wave + u) * 1024), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + (4 * wave + u) * 1024), 16, koff[u], ks, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kVt + (4 * wave + u) * 1024), 16, voff[u], vs,
+                                                 0, 0);
       }
     };
 
@@ -234,15 +247,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     int j;
     bool ka, kb;
     next_tile(j, ka, kb);
-    int stage = 0;
-    if (j != 0x7fffffff) issue(j, 0);
-    while (j != 0x7fffffff) {
+    if (j != 0x7fffffff) issue(j, std::integral_constant<int, 0>{});
+    // one tile: publish stage `stage`, prefetch the next tile into the other
+    // stage, then both contractions and the softmax update; the loop is unrolled
+    // twice so every LDS address is a per-lane constant plus an immediate
+    auto step = [&](auto stage_c) {
+      constexpr int stage = decltype(stage_c)::value;
       int jn;
       bool kan, kbn;
       next_tile(jn, kan, kbn);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (jn != 0x7fffffff) issue(jn, stage ^ 1);
+      if (jn != 0x7fffffff) issue(jn, std::integral_constant<int, stage ^ 1>{});
       const bool mine = qb == 0 ? ka : kb;
       if (mine) {
         const uint8_t* st = smem + stage * kStage;
@@ -257,9 +273,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
-        float mx = fmaxf(sacc[0][0], sacc[1][0]);
+        float m3[8];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sacc[0][e], sacc[1][e]));
+        for (int x = 0; x < 8; ++x)
+          m3[x] = fmaxf(fmaxf(sacc[x >> 2][4 * (x & 3)], sacc[x >> 2][4 * (x & 3) + 1]),
+                        fmaxf(sacc[x >> 2][4 * (x & 3) + 2], sacc[x >> 2][4 * (x & 3) + 3]));
+        float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])), fmaxf(fmaxf(m3[4], m3[5]), fmaxf(m3[6], m3[7])));
         mx = pair_max(mx) * c_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
           const float m_new = fmaxf(m_ref, mx);
@@ -293,7 +312,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       j = jn;
       ka = kan;
       kb = kbn;
-      stage ^= 1;
+    };
+    while (j != 0x7fffffff) {
+      step(std::integral_constant<int, 0>{});
+      if (j == 0x7fffffff) break;
+      step(std::integral_constant<int, 1>{});
     }
 
     // epilogue: normalise, stage O through LDS (block qb at qb * 16 KB), store coalesced

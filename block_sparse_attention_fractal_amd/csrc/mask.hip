@@ -162,7 +162,8 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 }
 
 // ---------------------------------------------------------------------------
-// CDF cut of one row per workgroup, by radix selection instead of a sort.
+// CDF cut, one wavefront per row (four rows per 256-thread workgroup, no
+// workgroup barriers), by radix selection instead of a sort.
 //
 //   p_j = exp(z_j - max) / sum; order blocks by (p desc, j asc); c_k = exclusive
 //   prefix mass of that order; keep position k iff k == 0 or c_k < 1 - thr;
@@ -171,22 +172,32 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 // The order is decided on the float64 logits (p is monotone in z), so it is as
 // exact as the logits.  Only the MASSES enter the comparison with 1 - thr, and
 // for those float32 exponentials (relative error ~1e-6) are far inside the 1e-4
-// band; they are accumulated as exact unsigned fixed-point integers (2^-50
-// units), so every partial sum is independent of summation order and the cut is
-// bitwise deterministic.
+// band; they are accumulated as unsigned fixed-point integers in units of 2^-30
+// of the row maximum (every partial sum exact, so the cut does not depend on
+// summation order and is bitwise deterministic; the rounding of all masses
+// together moves a prefix by less than S * 2^-30 < 4e-6).
 //
-// Selection: the kept set is {key > K*} plus the block(s) with key K*, where K*
-// is the key of the block at which the cumulative mass first reaches 1 - thr.
-// K* is found MSB-first, 8 key bits per pass: a 256-bin histogram of (count,
-// mass) of the blocks still sharing the decided prefix, a suffix scan over the
-// bins, and the bin where the mass crosses the target.  Passes stop when that
-// bin holds a single block; equal keys (exact ties) are resolved by index.
-// Blocks with z < max - lambda are never candidates: lambda (set by the host to
-// 40 + ln S - ln thr) bounds their total mass below 1e-17 * thr, so the cut can
-// never reach them.
+// Selection: the kept set is every block ordered before the block at which the
+// cumulative mass first reaches 1 - thr, and that block.  It is found in three
+// steps, each exact with respect to the order above:
+//   1. a 24-bit key t = (z - max - dmin) * (2^24 - 1) / (-dmin) in float32
+//      (dmin = smallest candidate offset) -- a monotone function of z, so it
+//      refines the order without breaking it, and it spreads even near-uniform
+//      rows over the bins -- is radix-selected MSB-first, 8 bits and one
+//      (count, mass) histogram per pass, until the crossing bin holds at most 64
+//      blocks; blocks in higher bins are kept, blocks in lower bins dropped;
+//   2. the crossing bin's blocks are compacted one per lane, their exact float64
+//      logits gathered, and each lane sums the mass of the bin's blocks ordered
+//      before its own (larger logit, or equal logit and smaller id): the exact
+//      exclusive prefix;
+//   3. only if more than 64 blocks share one 24-bit key (logits equal to ~1e-7
+//      relative): MSB-first passes over the exact order-preserving key of the
+//      logit, then exact ties by block id.
+// Blocks whose mass is below 2^-30 of the maximum, or with z < max - lambda
+// (lambda = 40 + ln S - ln thr, set by the host), are never candidates: the cut
+// cannot reach them unless thr < 4e-6, and then they lie inside the band.
 // ---------------------------------------------------------------------------
 constexpr int kMaxS = 4096;
-constexpr int kPerThread = kMaxS / 256;
 
 // order-preserving map of a double to uint64 (larger value -> larger key);
 // -0.0 and +0.0 are equal values and must share one key
@@ -195,218 +206,322 @@ __device__ __forceinline__ uint64_t order_key(double z) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int d) {
-  const uint32_t lo = __shfl_down((uint32_t)v, d, 64), hi = __shfl_down((uint32_t)(v >> 32), d, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// 256-thread reductions: butterfly inside each wave, then the four wave results
-// in a fixed order (deterministic, one barrier).
-template <typename V, typename Op>
-__device__ __forceinline__ V wg_reduce(V v, V* slot4, Op op) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    if constexpr (sizeof(V) == 8) {
-      uint64_t u;
-      __builtin_memcpy(&u, &v, 8);
-      u = shfl_xor_u64(u, m);
-      V o;
-      __builtin_memcpy(&o, &u, 8);
-      v = op(v, o);
-    } else {
-      v = op(v, __shfl_xor(v, m, 64));
-    }
+// Wavefront-wide reduction with DPP moves inside each row of 16 lanes and lane
+// swaps across rows and halves; every lane ends with the result.
+__device__ __forceinline__ uint32_t dpp_step(uint32_t v, int step) {
+  switch (step) {
+    case 0: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);   // lanes ^ 1
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);   // lanes ^ 2
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+    default: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false); // row mirror
   }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) slot4[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return op(op(slot4[0], slot4[1]), op(slot4[2], slot4[3]));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, int lane, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  constexpr int kWords = sizeof(T) / 4;
+  auto as_words = [](T x, uint32_t* w) { __builtin_memcpy(w, &x, sizeof(T)); };
+  auto from_words = [](const uint32_t* w) {
+    T x;
+    __builtin_memcpy(&x, w, sizeof(T));
+    return x;
+  };
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) w[q] = dpp_step(w[q], st);
+    v = op(v, from_words(w));
+  }
+  {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const auto r = __builtin_amdgcn_permlane16_swap(w[q], w[q], false, false);
+      w[q] = (lane & 16) ? r[0] : r[1];   // the other row of the pair
+    }
+    v = op(v, from_words(w));
+  }
+  {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const auto r = __builtin_amdgcn_permlane32_swap(w[q], w[q], false, false);
+      w[q] = (lane & 32) ? r[0] : r[1];   // the other half
+    }
+    v = op(v, from_words(w));
+  }
+  return v;
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NS>
 __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ z, Geom g, double thr, double lambda,
                                                      int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
                                                      int32_t* __restrict__ counts, int words) {
-  __shared__ uint64_t umass[256];
-  __shared__ uint32_t ucount[256];
-  __shared__ uint32_t bm[kMaxS / 32];
-  __shared__ uint32_t tie[kMaxS / 32];
-  __shared__ double dslot[4];
-  __shared__ uint64_t uslot[4];
-  __shared__ uint64_t s_prefix, s_above;
-  __shared__ uint32_t s_cnt;
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint64_t umass_all[4][256];
+  __shared__ uint32_t ucount_all[4][256];
+  __shared__ uint32_t bm_all[4][kMaxS / 32];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= g.rows) return;                     // whole wavefront; nothing below waits on other waves
+  uint64_t* umass = umass_all[wv];
+  uint32_t* ucount = ucount_all[wv];
+  uint32_t* bm = bm_all[wv];
   const int S = g.S;
-  const int64_t r = blockIdx.x;
   const int i = (int)(r % S);
   const double* zr = z + r * S;
-
-  for (int w = tid; w < kMaxS / 32; w += 256) bm[w] = 0u;
+  auto u64max = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  auto u64min = [](uint64_t a, uint64_t b) { return a < b ? a : b; };
+  auto u64add = [](uint64_t a, uint64_t b) { return a + b; };
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+  auto set_bit = [&](int j) { atomicOr(&bm[j >> 5], 1u << (j & 31)); };
+  // the lane index through an opaque copy: block ids l + 64 k are then recomputed
+  // where used instead of being kept live in NS registers for the whole kernel
+  auto lane_id = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
 
   if (thr == 0.0) {
-    __syncthreads();
-    for (int j = tid; j < S; j += 256) atomicOr(&bm[j >> 5], 1u << (j & 31));
+    for (int x = lane; x < words; x += 64) {
+      const int left = S - 32 * x;
+      bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    }
   } else {
-    double zv[kPerThread];
-    double m = -DBL_MAX;
+    for (int x = lane; x < words; x += 64) bm[x] = 0u;
+    // slot k of lane l is block l + 64 k: mass in 2^-30 units of the row maximum
+    // (0 = not a candidate) and the 24-bit monotone key
+    uint32_t w[NS], t[NS];
+    uint64_t total;
+    {
+      double zv[NS];
+      double m = -DBL_MAX;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int j = tid + 256 * k;
-      zv[k] = j < S ? zr[j] : -DBL_MAX;
-      m = fmax(m, zv[k]);
-    }
-    m = wg_reduce(m, dslot, [](double a, double b) { return fmax(a, b); });
-    // candidates: fixed-point masses (2^-50 units, S * 2^50 < 2^63) and order keys
-    uint64_t key[kPerThread], w[kPerThread];
-    uint64_t wsum = 0;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const double d = zv[k] - m;
-      const bool cand = (tid + 256 * k < S) && d >= -lambda;
-      const float e = cand ? __builtin_amdgcn_exp2f((float)d * 1.44269504088896341f) : 0.f;
-      w[k] = cand ? (uint64_t)((double)e * 1125899906842624.0) : 0ull;
-      key[k] = cand ? order_key(zv[k]) : 0ull;
-      wsum += w[k];
-    }
-    const uint64_t total = wg_reduce(wsum, uslot, [](uint64_t a, uint64_t b) { return a + b; });
-    const double target = (1.0 - thr) * (double)total;        // keep while exclusive prefix < target
-    // Pass 0: 256 uniform buckets of d = z - max over [dmin, 0].  The bucket index
-    // is a monotone function of z, so it refines the order without breaking it,
-    // and it spreads even near-uniform rows thinly over the bins (few LDS atomic
-    // collisions).  Later passes use the exact key, inside the crossing bucket only.
-    double dmin = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-      if (w[k] != 0ull) dmin = fmin(dmin, zv[k] - m);
-    dmin = wg_reduce(dmin, dslot, [](double a, double b) { return fmin(a, b); });
-    const double bscale = dmin < 0.0 ? 255.999 / (-dmin) : 0.0;
-    int bucket[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) bucket[k] = (int)((zv[k] - m - dmin) * bscale);
-    ucount[tid] = 0u;
-    umass[tid] = 0ull;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-      if (w[k] != 0ull) {
-        atomicAdd(&ucount[bucket[k]], 1u);
-        atomicAdd((unsigned long long*)&umass[bucket[k]], (unsigned long long)w[k]);
+      for (int k = 0; k < NS; ++k) {
+        const int j = lane + 64 * k;
+        const double v = zr[min(j, S - 1)];   // unconditional, so all loads are in flight at once
+        zv[k] = j < S ? v : -DBL_MAX;
+        m = fmax(m, zv[k]);
       }
-    __syncthreads();
-    auto crossing_bin = [&](uint64_t above_in, uint64_t prefix_in, int shift_in) {
-      // lane l owns bins 4l..4l+3; suffix sums over bins (bin 255 = largest keys)
+      m = wave_reduce(m, lane, [](double a, double b) { return fmax(a, b); });
+      float df[NS];
+      uint64_t wsum = 0;
+      float dmin = 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const double d = zv[k] - m;
+        const bool cand = (lane + 64 * k < S) && d >= -lambda;
+        df[k] = (float)d;
+        const float e = cand ? __builtin_amdgcn_exp2f(df[k] * 1.44269504088896341f) : 0.f;
+        w[k] = (uint32_t)(e * 1073741824.0f);   // e <= 1, so at most 2^30; e * 2^30 is exact
+        wsum += w[k];
+        if (w[k] != 0u) dmin = fminf(dmin, df[k]);
+      }
+      total = wave_reduce(wsum, lane, u64add);
+      dmin = wave_reduce(dmin, lane, [](float a, float b) { return fminf(a, b); });
+      const float tscale = dmin < 0.f ? 16777215.0f / (-dmin) : 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) t[k] = w[k] != 0u ? (uint32_t)fminf((df[k] - dmin) * tscale, 16777215.0f) : 0u;
+    }
+    const double target = (1.0 - thr) * (double)total;        // keep while exclusive prefix < target
+
+    // Histogram of (count, mass) of the blocks with bin(k) >= 0, then the bin in
+    // which the cumulative mass from the top (bin 255 first) reaches the target.
+    // Returns false when no bin does (the target lies beyond every candidate).
+    auto crossing = [&](auto bin, uint64_t above_in, int& b_out, uint64_t& above_out, uint32_t& cnt_out) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        ucount[4 * lane + x] = 0u;
+        umass[4 * lane + x] = 0ull;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int b = w[k] != 0u ? bin(k) : -1;
+        if (b >= 0) {
+          atomicAdd(&ucount[b], 1u);
+          atomicAdd((unsigned long long*)&umass[b], (unsigned long long)w[k]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
       uint64_t mb[4];
       uint32_t cb[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) { mb[x] = umass[4 * lane + x]; cb[x] = ucount[4 * lane + x]; }
+      for (int x = 0; x < 4; ++x) {
+        mb[x] = umass[4 * lane + x];
+        cb[x] = ucount[4 * lane + x];
+      }
       const uint64_t lane_tot = mb[0] + mb[1] + mb[2] + mb[3];
-      uint64_t suf = lane_tot;
+      uint64_t suf = lane_tot;                 // inclusive suffix sum over lanes
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t o = shfl_down_u64(suf, d);
-        if (lane + d < 64) suf += o;
+        const uint32_t lo = __shfl_down((uint32_t)suf, d, 64), hi = __shfl_down((uint32_t)(suf >> 32), d, 64);
+        if (lane + d < 64) suf += ((uint64_t)hi << 32) | lo;
       }
       uint64_t run = suf - lane_tot;
+      int found = -1;
+      uint64_t f_above = 0;
+      uint32_t f_cnt = 0;
 #pragma unroll
       for (int x = 3; x >= 0; --x) {
         const uint64_t excl = run;
         run += mb[x];
         if (cb[x] != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + run)) {
-          s_prefix = prefix_in | ((uint64_t)(4 * lane + x) << shift_in);
-          s_above = above_in + excl;
-          s_cnt = cb[x];
+          found = 4 * lane + x;
+          f_above = above_in + excl;
+          f_cnt = cb[x];
         }
       }
+      __builtin_amdgcn_wave_barrier();         // the arrays are reused right after
+      const uint64_t ball = __ballot(found >= 0);
+      if (ball == 0ull) return false;
+      const int src = __ffsll((unsigned long long)ball) - 1;
+      b_out = __builtin_amdgcn_readlane(found, src);
+      cnt_out = (uint32_t)__builtin_amdgcn_readlane((int)f_cnt, src);
+      above_out = readlane_u64(f_above, src);
+      return true;
     };
-    if (tid == 0) { s_prefix = 0; s_above = 0; s_cnt = 0; }   // unreachable target: keep every candidate
-    __syncthreads();
-    if (tid < 64) crossing_bin(0, 0, 0);
-    __syncthreads();
-    const int b0 = (int)s_prefix;
-    uint64_t above = s_above;
-    uint32_t cnt_bin = s_cnt;
-    // exact passes over the keys of the crossing bucket
-    uint64_t kmax = 0, kmin = ~0ull;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const bool in = w[k] != 0ull && bucket[k] == b0;
-      if (!in) w[k] = w[k] != 0ull && bucket[k] > b0 ? w[k] : 0ull;  // keep "above" blocks, drop the rest
-      if (in) {
-        kmax = key[k] > kmax ? key[k] : kmax;
-        kmin = key[k] < kmin ? key[k] : kmin;
+
+    // step 1: radix selection on the 24-bit key
+    uint32_t tpre = 0;                         // decided high bits of the crossing key
+    int tsh = 24;                              // bits below the decided prefix
+    uint64_t above = 0;
+    uint32_t cnt = 0;
+    bool reach = true;
+    while (tsh > 0) {
+      const int sh = tsh - 8;
+      const uint32_t pf = tpre;
+      int b;
+      uint64_t ab;
+      uint32_t cb;
+      if (!crossing([&](int k) { return (t[k] >> tsh) == pf ? (int)((t[k] >> sh) & 255u) : -1; }, above, b, ab, cb)) {
+        reach = false;                         // only possible on the first pass
+        break;
       }
+      tpre = (pf << 8) | (uint32_t)b;
+      tsh = sh;
+      above = ab;
+      cnt = cb;
+      if (cnt <= 64u) break;
     }
-    kmax = wg_reduce(kmax, uslot, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
-    kmin = wg_reduce(kmin, uslot, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
-    const uint64_t diff = kmax ^ kmin;
-    int shift = diff == 0 ? 0 : ((63 - __clzll(diff)) & ~7);
-    uint64_t prefix = shift >= 56 ? 0ull : (kmax & (~0ull << (shift + 8)));
-    if (cnt_bin > 1u) {
-      if (tid == 0) { s_prefix = prefix; s_cnt = 0; }
-      for (;;) {
-        ucount[tid] = 0u;
-        umass[tid] = 0ull;
-        __syncthreads();
-        const uint64_t hi_mask = shift >= 56 ? 0ull : (~0ull << (shift + 8));
+    if (!reach) {                              // every candidate is kept
+      const int ln = lane_id();
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-          if (w[k] != 0ull && bucket[k] == b0 && (key[k] & hi_mask) == prefix) {
-            const int d = (int)((key[k] >> shift) & 255);
-            atomicAdd(&ucount[d], 1u);
-            atomicAdd((unsigned long long*)&umass[d], (unsigned long long)w[k]);
-          }
-        }
-        __syncthreads();
-        if (tid < 64) crossing_bin(above, prefix, shift);
-        __syncthreads();
-        prefix = s_prefix;
-        above = s_above;
-        cnt_bin = s_cnt;
-        if (cnt_bin <= 1u || shift == 0) break;
-        shift -= 8;
-      }
+      for (int k = 0; k < NS; ++k)
+        if (w[k] != 0u) set_bit(ln + 64 * k);
     } else {
-      prefix = cnt_bin == 0u ? 0ull : kmax;   // one block in the crossing bucket: its key; none: keep all
-      shift = 0;
-    }
-    // keep: keys above the final bin, and the final bin itself when it holds one block
-    const uint64_t lo_key = prefix;
-    const uint64_t hi_key = shift == 0 ? prefix : (prefix | ((1ull << shift) - 1));
+      auto in_bin = [&](int k) { return w[k] != 0u && (t[k] >> tsh) == tpre; };
+      {
+        const int ln = lane_id();
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      if (w[k] == 0ull) continue;
-      const int j = tid + 256 * k;
-      if (bucket[k] > b0 || key[k] > hi_key || (cnt_bin <= 1u && key[k] >= lo_key))
-        atomicOr(&bm[j >> 5], 1u << (j & 31));
-    }
-    if (cnt_bin > 1u) {
-      // exact ties at K* = prefix: keep the lowest-index ones until the mass reaches the target
-      for (int x = tid; x < kMaxS / 32; x += 256) tie[x] = 0u;
-      __syncthreads();
-      uint64_t wt = 0;
+        for (int k = 0; k < NS; ++k)
+          if (w[k] != 0u && (t[k] >> tsh) > tpre) set_bit(ln + 64 * k);
+      }
+      if (cnt <= 64u) {
+        // step 2: one block of the crossing bin per lane, exact logits gathered
+        uint32_t* cj = ucount;
+        uint32_t* cw = ucount + 64;
+        uint32_t base = 0;
+        const int ln = lane_id();
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k)
-        if (w[k] != 0ull && bucket[k] == b0 && key[k] == prefix) {
-          atomicOr(&tie[(tid + 256 * k) >> 5], 1u << ((tid + 256 * k) & 31));
-          wt = w[k];
+        for (int k = 0; k < NS; ++k) {
+          const bool in = in_bin(k);
+          const uint64_t ball = __ballot(in);
+          if (in) {
+            const uint32_t rank = base + (uint32_t)__popcll(ball & lt_mask);
+            cj[rank] = (uint32_t)(ln + 64 * k);
+            cw[rank] = w[k];
+          }
+          base += (uint32_t)__popcll(ball);
         }
-      if (wt != 0ull) umass[0] = wt;            // all ties share one mass
-      __syncthreads();
-      if (tid == 0) {
-        const uint64_t wtie = umass[0];
-        uint64_t acc = above;
-        for (int x = 0; x < (S + 31) / 32; ++x) {
-          uint32_t bits = tie[x];
-          while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            if ((double)acc < target) {
-              bm[x] |= 1u << b;
-              acc += wtie;
+        __builtin_amdgcn_wave_barrier();
+        const bool have = (uint32_t)lane < cnt;
+        const uint32_t my_j = have ? cj[lane] : 0u;
+        const uint32_t my_w = have ? cw[lane] : 0u;
+        const uint64_t my_key = have ? order_key(zr[my_j]) : 0ull;
+        uint64_t before = 0;
+        for (uint32_t y = 0; y < cnt; ++y) {
+          const uint64_t ky = readlane_u64(my_key, (int)y);
+          const uint32_t jy = (uint32_t)__builtin_amdgcn_readlane((int)my_j, (int)y);
+          const uint32_t wy = (uint32_t)__builtin_amdgcn_readlane((int)my_w, (int)y);
+          if (ky > my_key || (ky == my_key && jy < my_j)) before += wy;
+        }
+        if (have && (double)(above + before) < target) set_bit((int)my_j);
+      } else {
+        // step 3 (more than 64 blocks share one 24-bit key): exact keys, re-read
+        // from the logits where needed (rare, so registers are not spent on them)
+        auto key_of = [&](int k) {
+          const double* zl = zr;
+          asm volatile("" : "+s"(zl));        // re-issue the load at each use
+          return order_key(zl[lane + 64 * k]);
+        };
+        uint64_t kmax = 0, kmin = ~0ull;
+        for (int k = 0; k < NS; ++k)
+          if (in_bin(k)) {
+            const uint64_t key = key_of(k);
+            kmax = u64max(kmax, key);
+            kmin = u64min(kmin, key);
+          }
+        kmax = wave_reduce(kmax, lane, u64max);
+        kmin = wave_reduce(kmin, lane, u64min);
+        const uint64_t diff = kmax ^ kmin;
+        int shift = diff == 0 ? 0 : ((63 - __clzll(diff)) & ~7);
+        uint64_t prefix = shift >= 56 ? 0ull : (kmax & (~0ull << (shift + 8)));
+        for (;;) {
+          const uint64_t hi_mask = shift >= 56 ? 0ull : (~0ull << (shift + 8));
+          const int sh = shift;
+          const uint64_t pf = prefix;
+          int b;
+          uint64_t ab;
+          uint32_t cb;
+          // the crossing block lies in this bin and shares the decided prefix, so
+          // a bin is always found
+          crossing(
+              [&](int k) {
+                if (!in_bin(k)) return -1;
+                const uint64_t key = key_of(k);
+                return (key & hi_mask) == pf ? (int)((key >> sh) & 255u) : -1;
+              },
+              above, b, ab, cb);
+          prefix |= (uint64_t)b << shift;
+          above = ab;
+          cnt = cb;
+          if (cnt <= 1u || shift == 0) break;
+          shift -= 8;
+        }
+        const uint64_t hi_key = shift == 0 ? prefix : (prefix | ((1ull << shift) - 1));
+        uint64_t tie_bits = 0;                 // bit k: slot k of this lane ties at the cut
+        uint32_t wt = 0;
+        for (int k = 0; k < NS; ++k)
+          if (in_bin(k)) {
+            const uint64_t key = key_of(k);
+            if (key > hi_key || (cnt <= 1u && key >= prefix)) set_bit(lane + 64 * k);
+            if (cnt > 1u && key == prefix) {
+              tie_bits |= 1ull << k;
+              wt = w[k];
             }
+          }
+        if (cnt > 1u) {
+          // exact ties at the cut: the lowest block ids, until the mass reaches the
+          // target; slots then lanes run in block-id order, and ties share one mass
+          wt = wave_reduce(wt, lane, [](uint32_t a, uint32_t b2) { return a > b2 ? a : b2; });
+          uint64_t acc = above;
+          for (int k = 0; k < NS; ++k) {
+            const uint64_t tb = __ballot((tie_bits >> k) & 1ull);
+            if (((tie_bits >> k) & 1ull) && (double)(acc + (uint64_t)__popcll(tb & lt_mask) * wt) < target)
+              set_bit(lane + 64 * k);
+            acc += (uint64_t)__popcll(tb) * wt;
           }
         }
       }
@@ -415,26 +530,33 @@ __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ 
   if (win_t >= 0) {
     const int HW = g.Hp * g.Wp;
     const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
-    for (int j = tid; j < S; j += 256) {
+    for (int j = lane; j < S; j += 64) {
       const int tj = j / HW, yj = (j / g.Wp) % g.Hp, xj = j % g.Wp;
-      if (abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w)
-        atomicOr(&bm[j >> 5], 1u << (j & 31));
+      if (abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w) set_bit(j);
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   uint32_t pc = 0;
-  for (int w2 = tid; w2 < words; w2 += 256) {
-    const uint32_t v = bm[w2];
-    bitmap[r * words + w2] = v;
+  for (int x = lane; x < words; x += 64) {
+    const uint32_t v = bm[x];
+    bitmap[r * words + x] = v;
     pc += __popc(v);
   }
-  pc = wg_reduce(pc, ucount, [](uint32_t a, uint32_t b) { return a + b; });
-  if (tid == 0) counts[r] = (int32_t)pc;
+  pc = wave_reduce(pc, lane, [](uint32_t a, uint32_t b) { return a + b; });
+  if (lane == 0) counts[r] = (int32_t)pc;
 }
 
 hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h, int win_w,
                          uint32_t* bitmap, int32_t* counts, int words, hipStream_t s) {
-  select_kernel<<<(unsigned)g.rows, 256, 0, s>>>(z, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, words);
+  const unsigned grid = (unsigned)((g.rows + 3) / 4);
+#define BSA_SELECT(NS_) \
+  select_kernel<NS_><<<grid, 256, 0, s>>>(z, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, words)
+  if (g.S <= 128) BSA_SELECT(2);
+  else if (g.S <= 512) BSA_SELECT(8);
+  else if (g.S <= 1024) BSA_SELECT(16);
+  else if (g.S <= 2048) BSA_SELECT(32);
+  else BSA_SELECT(64);
+#undef BSA_SELECT
   return hipGetLastError();
 }
 
