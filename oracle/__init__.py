@@ -14,7 +14,13 @@ per-function citations and the readings taken where the page is silent.
 Pinned (checked against closed forms, brute force or library routines in
 tests/test_oracle_pins.py): fractal_positions, permute, inverse_permute,
 pool_blocks, reduced_map, cdf_keep, sta_window, csr_from_keep,
-block_sparse_attention, dense_attention.  No function is "parity unpinned".
+block_sparse_attention, dense_attention.
+
+`sip.py` adds the sampled selection with inclusion-probability weights of the
+AB-Attention page (news.hamidun.com/es/news/14960, "Los tres recursos de
+AB-Attention", second resource), pinned in tests/test_oracle_sip_pins.py against
+numpy's Philox4x64-10, a bisection solve of the sampling design and Monte-Carlo
+unbiasedness.  No function is "parity unpinned".
 """
 from .nabla import (
     fractal_positions,
