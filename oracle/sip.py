@@ -16,9 +16,11 @@ Readings taken where the page is silent (also listed with the design notes):
   S1  the score of key block j for query block i is the reduced-map probability
       A[i, j] of the NABLA pipeline (the same map the CDF cut uses).
   S2  "proportional to its score, the most important always taken" is the
-      capped proportional design pi_j = min(1, c * A[i, j]) with c chosen so
-      that sum_j pi_j equals the row's budget k; blocks with c * A >= 1 get
-      pi = 1.
+      capped proportional design: the row's top block (largest A, lowest index
+      on ties) is always taken (pi = 1), which also keeps every row non-empty;
+      every other block gets pi_j = min(1, c * A[i, j]) with c chosen so that
+      the probabilities of all blocks sum to the row's budget k (so blocks with
+      c * A >= 1 are always taken too).
   S3  the budget k of a row is the number of blocks the CDF cut keeps for that
       row (SIP spends the same number of tiles as the cut it replaces, in
       expectation); thr = 0 keeps every block with pi = 1.
@@ -84,23 +86,32 @@ def uniforms(rows: np.ndarray, S: int, seed: int) -> np.ndarray:
 
 
 def inclusion_probabilities(a: np.ndarray, k: int) -> np.ndarray:
-    """pi_j = min(1, c * a_j) with sum_j pi_j = k (reading S2).  a: one row of
-    nonnegative scores.  Written out from the definition: with the scores sorted
-    in descending order, the first t are capped at 1 and the rest share k - t in
-    proportion to their score, for the smallest t at which no uncapped block
-    would exceed 1."""
+    """Inclusion probabilities of one row with budget k >= 1 (reading S2): the top
+    block gets 1; the others get min(1, c * a_j) summing to k - 1.  a: one row of
+    nonnegative scores.  Written out from the definition: with the other scores
+    sorted in descending order, the first t are capped at 1 and the rest share
+    k - 1 - t in proportion to their score, for the smallest t at which no
+    uncapped block would exceed 1."""
     a = np.asarray(a, np.float64)
-    positive = int(np.count_nonzero(a > 0))
-    if k >= positive:
-        return (a > 0).astype(np.float64)
-    order = np.argsort(-a, kind="stable")
-    s = a[order]
-    for t in range(k):
-        rest = s[t:].sum()
-        c = (k - t) / rest
+    top = int(np.argmax(a))                      # first maximum: lowest index on ties
+    pi = np.zeros(len(a))
+    pi[top] = 1.0
+    others = np.delete(np.arange(len(a)), top)
+    b = a[others]
+    kk = k - 1
+    if kk <= 0:
+        return pi
+    positive = int(np.count_nonzero(b > 0))
+    if kk >= positive:
+        pi[others] = (b > 0).astype(np.float64)
+        return pi
+    s = np.sort(b)[::-1]
+    for t in range(kk):
+        c = (kk - t) / s[t:].sum()
         if c * s[t] < 1.0:
-            return np.minimum(1.0, c * a)
-    raise AssertionError("unreachable: t = k - 1 always leaves an uncapped block below 1")
+            pi[others] = np.minimum(1.0, c * b)
+            return pi
+    raise AssertionError("unreachable: t = k - 2 always leaves an uncapped block below 1")
 
 
 def sip_row(a: np.ndarray, k: int, u: np.ndarray, thr: float):

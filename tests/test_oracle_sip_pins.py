@@ -43,17 +43,20 @@ def test_uniforms_range_and_mean():
 
 # ------------------------------------------------------------------ inclusion probabilities
 def _bisect_pi(a, k):
-    """Independent solve: bisection on c of sum_j min(1, c a_j) = k."""
+    """Independent solve: the top block at 1, then bisection on c of
+    1 + sum_{j != top} min(1, c a_j) = k."""
+    top = int(np.argmax(a))
+    rest = np.delete(a, top)
     lo, hi = 0.0, 1.0
-    while np.minimum(1.0, hi * a).sum() < k:
+    while np.minimum(1.0, hi * rest).sum() < k - 1:
         hi *= 2
     for _ in range(200):
         mid = 0.5 * (lo + hi)
-        if np.minimum(1.0, mid * a).sum() < k:
+        if np.minimum(1.0, mid * rest).sum() < k - 1:
             lo = mid
         else:
             hi = mid
-    return np.minimum(1.0, hi * a)
+    return np.insert(np.minimum(1.0, hi * rest), top, 1.0)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -62,27 +65,33 @@ def test_inclusion_probabilities_solve_the_design(seed):
     S = 50
     a = rng.exponential(size=S) ** 3          # heavy-tailed: several capped blocks
     a /= a.sum()
-    for k in (1, 3, 10, 25, 49):
+    for k in (1, 2, 3, 10, 25, 49):
         pi = sip.inclusion_probabilities(a, k)
         assert abs(pi.sum() - k) < 1e-12
         assert pi.min() >= 0 and pi.max() <= 1.0
-        assert np.allclose(pi, _bisect_pi(a, k), rtol=0, atol=1e-12)
+        assert pi[np.argmax(a)] == 1.0
+        if k > 1:
+            assert np.allclose(pi, _bisect_pi(a, k), rtol=0, atol=1e-12)
         capped = pi == 1.0
         if capped.any() and (~capped).any():
             assert a[capped].min() >= a[~capped].max()
         free = ~capped
-        ratio = pi[free] / a[free]
-        assert np.allclose(ratio, ratio[0], rtol=1e-12)
+        if free.any():
+            ratio = pi[free] / a[free]
+            assert np.allclose(ratio, ratio[0], rtol=1e-12)
 
 
 def test_inclusion_probabilities_closed_forms():
-    assert np.allclose(sip.inclusion_probabilities(np.full(16, 1 / 16), 4), 0.25)
+    # uniform scores: the top block (lowest index on the tie) plus (k-1)/(S-1) each
+    pi = sip.inclusion_probabilities(np.full(16, 1 / 16), 4)
+    assert pi[0] == 1.0 and np.allclose(pi[1:], 3 / 15)
     assert np.allclose(sip.inclusion_probabilities(np.array([0.9, 0.05, 0.05]), 2), [1.0, 0.5, 0.5])
+    assert np.array_equal(sip.inclusion_probabilities(np.array([0.2, 0.5, 0.3]), 1), [0.0, 1.0, 0.0])
     # budget at or above the number of positive scores: every positive block, with certainty
     assert np.array_equal(sip.inclusion_probabilities(np.array([0.5, 0.5, 0.0]), 2), [1.0, 1.0, 0.0])
     # the page's example weight: inclusion probability 25 % counts four times
-    pi = sip.inclusion_probabilities(np.full(8, 1 / 8), 2)
-    assert np.allclose(1 / pi, 4.0)
+    pi = sip.inclusion_probabilities(np.full(9, 1 / 9), 3)
+    assert np.allclose(1 / pi[1:], 4.0)
 
 
 # ------------------------------------------------------------------ Horvitz-Thompson unbiasedness
