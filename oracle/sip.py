@@ -109,9 +109,12 @@ def inclusion_probabilities(a: np.ndarray, k: int) -> np.ndarray:
     for t in range(kk):
         c = (kk - t) / s[t:].sum()
         if c * s[t] < 1.0:
-            pi[others] = np.minimum(1.0, c * b)
-            return pi
-    raise AssertionError("unreachable: t = k - 2 always leaves an uncapped block below 1")
+            break
+    # Falling through means the mass after the first kk - 1 others is below the
+    # rounding unit of their sum: then c * s[kk - 1] rounds to 1, the first kk
+    # others are all taken and the rest keep their vanishing probabilities.
+    pi[others] = np.minimum(1.0, c * b)
+    return pi
 
 
 def sip_row(a: np.ndarray, k: int, u: np.ndarray, thr: float):
