@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 BSA_OK = 0
 BSA_F32, BSA_BF16 = 0, 1
 BSA_LAYOUT_ORIGINAL, BSA_LAYOUT_FRACTAL = 0, 1
+BSA_MASK_CDF, BSA_MASK_SIP = 0, 1
 
 # every symbol declared in include/bsa.h
 EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_pool", "bsa_block_map", "bsa_build_mask",
@@ -28,12 +29,12 @@ class Problem(ctypes.Structure):
 
 class MaskParams(ctypes.Structure):
     _fields_ = [("thr", ctypes.c_double), ("win_t", ctypes.c_int32), ("win_h", ctypes.c_int32),
-                ("win_w", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("win_w", ctypes.c_int32), ("mode", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class CSR(ctypes.Structure):
     _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-                ("capacity", ctypes.c_int64), ("nnz", ctypes.c_void_p)]
+                ("capacity", ctypes.c_int64), ("nnz", ctypes.c_void_p), ("shift", ctypes.c_void_p)]
 
 
 class BSAError(RuntimeError):

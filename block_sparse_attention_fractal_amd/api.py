@@ -37,12 +37,15 @@ class VideoGrid:
 @dataclass
 class BlockMask:
     """CSR block mask on the device: row r = (b*heads + h)*S + i lists the kept key
-    blocks of query block i, ascending.  col_idx has capacity batch*heads*S*S."""
+    blocks of query block i, ascending.  col_idx has capacity batch*heads*S*S.
+    shift (optional, aligned with col_idx) holds each entry's logit shift, as a
+    sampled (SIP) mask produces it."""
     row_ptr: torch.Tensor     # int32 [rows + 1]
     col_idx: torch.Tensor     # int32 [capacity]
     nnz_dev: torch.Tensor     # int32 [1]
     rows: int
     S: int
+    shift: Optional[torch.Tensor] = None   # float32 [capacity] or None
 
     def nnz(self) -> int:
         return int(self.nnz_dev.item())
@@ -52,7 +55,7 @@ class BlockMask:
 
     def as_struct(self) -> _lib.CSR:
         return _lib.CSR(self.row_ptr.data_ptr(), self.col_idx.data_ptr(), self.col_idx.numel(),
-                        self.nnz_dev.data_ptr())
+                        self.nnz_dev.data_ptr(), None if self.shift is None else self.shift.data_ptr())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -137,8 +140,10 @@ def block_map(qp: torch.Tensor, kp: torch.Tensor, grid: VideoGrid, dtype=torch.b
 
 def build_mask(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, thr: float,
                window: Optional[Tuple[int, int, int]] = None, layout: str = "original",
-               workspace: Optional[torch.Tensor] = None) -> BlockMask:
-    """Pool -> reduced map -> CDF cut at 1-thr (-> union with +-window tiles) -> CSR."""
+               workspace: Optional[torch.Tensor] = None, sip_seed: Optional[int] = None) -> BlockMask:
+    """Pool -> reduced map -> CDF cut at 1-thr (-> union with +-window tiles) -> CSR.
+    With sip_seed set, the cut is replaced by SIP sampling (same budget per row,
+    Philox key = sip_seed) and the mask carries per-entry logit shifts."""
     _check_qkv(q, k)
     prob = make_problem(q, grid, layout)
     sz = query_sizes(prob)
@@ -146,23 +151,30 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, thr: float,
     row_ptr = torch.empty(sz["rows"] + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(sz["max_nnz"], dtype=torch.int32, device=dev)
     nnz = torch.empty(1, dtype=torch.int32, device=dev)
-    mask = BlockMask(row_ptr, col_idx, nnz, sz["rows"], grid.S)
+    shift = torch.empty(sz["max_nnz"], dtype=torch.float32, device=dev) if sip_seed is not None else None
+    mask = BlockMask(row_ptr, col_idx, nnz, sz["rows"], grid.S, shift)
     ws = _workspace(sz["mask_ws"], dev, workspace)
     wt, wh, ww = window if window is not None else (-1, -1, -1)
-    mp = _lib.MaskParams(float(thr), wt, wh, ww, 0)
+    mode = _lib.BSA_MASK_SIP if sip_seed is not None else _lib.BSA_MASK_CDF
+    mp = _lib.MaskParams(float(thr), wt, wh, ww, mode, 0 if sip_seed is None else int(sip_seed) % 2**64)
     csr = mask.as_struct()
     check(lib().bsa_build_mask(ctypes.byref(prob), ctypes.byref(mp), q.data_ptr(), k.data_ptr(),
                                ctypes.byref(csr), ws.data_ptr(), ws.numel(), _stream(dev)))
     return mask
 
 
-def mask_from_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int) -> BlockMask:
-    """Wrap a caller-made CSR (int32 device tensors) for forward()."""
+def mask_from_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int,
+                  shift: Optional[torch.Tensor] = None) -> BlockMask:
+    """Wrap a caller-made CSR (int32 device tensors, optional float32 per-entry
+    logit shifts aligned with col_idx) for forward()."""
     if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
         raise TypeError("row_ptr and col_idx must be int32")
+    if shift is not None and (shift.dtype != torch.float32 or shift.numel() < col_idx.numel()):
+        raise TypeError("shift must be float32 with one entry per col_idx entry")
     rows = row_ptr.numel() - 1
     nnz = row_ptr[-1:].clone()
-    return BlockMask(row_ptr.contiguous(), col_idx.contiguous(), nnz, rows, S)
+    return BlockMask(row_ptr.contiguous(), col_idx.contiguous(), nnz, rows, S,
+                     None if shift is None else shift.contiguous())
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,

@@ -55,7 +55,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 100; }
+int bsa_version(void) { return 200; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -134,6 +134,9 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
     return fail(BSA_ERR_INVALID_ARG, "bsa_build_mask: null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out->row_ptr, 4) || !aligned(out->col_idx, 4))
     return fail(BSA_ERR_INVALID_ARG, "bsa_build_mask: misaligned pointer");
+  const bool sip = mp->mode == BSA_MASK_SIP;
+  if (sip && (!out->shift || !aligned(out->shift, 4)))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_build_mask: SIP mode needs a 4-byte aligned shift array");
   if (out->capacity < g.rows * g.S)
     return fail(BSA_ERR_CAPACITY, "bsa_build_mask: col_idx capacity " + std::to_string(out->capacity) +
                                       " < batch*heads*S*S = " + std::to_string(g.rows * g.S));
@@ -151,14 +154,23 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
   // Candidates for the sort: blocks within lambda of the row's max logit.  The
   // rest carry total mass < S * exp(-lambda) = 1e-17 * thr (see select_kernel).
   const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)g.S) - std::log(mp->thr) : 0.0;
+  const int wt = win ? mp->win_t : -1, wh = win ? mp->win_h : -1, ww = win ? mp->win_w : -1;
+  double* rowstat = reinterpret_cast<double*>(base + w.rowstat);
   hipError_t e = launch_pool(g, q, k, qp, kp, stream);
   if (e == hipSuccess) e = launch_block_logits(g, qp, kp, z, stream);
+  // SIP: the CDF cut without the window gives each row's budget, then the
+  // sampling replaces the bitmap and unions the window
   if (e == hipSuccess)
-    e = launch_select(g, z, mp->thr, lambda, win ? mp->win_t : -1, win ? mp->win_h : -1, win ? mp->win_w : -1,
-                      bitmap, counts, w.words, stream);
+    e = launch_select(g, z, mp->thr, lambda, sip ? -1 : wt, sip ? -1 : wh, sip ? -1 : ww, bitmap, counts, w.words,
+                      stream);
+  if (e == hipSuccess && sip)
+    e = launch_sip(g, z, mp->thr, mp->seed, wt, wh, ww, bitmap, counts, rowstat, w.words, stream);
   if (e == hipSuccess)
     e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
-  if (e == hipSuccess) e = launch_compact(g, bitmap, w.words, out->row_ptr, out->col_idx, stream);
+  if (e == hipSuccess && !sip) e = launch_compact(g, bitmap, w.words, out->row_ptr, out->col_idx, stream);
+  if (e == hipSuccess && sip)
+    e = launch_compact_sip(g, bitmap, w.words, out->row_ptr, out->col_idx, out->shift, z, rowstat, mp->thr, wt, wh,
+                           ww, stream);
   if (e != hipSuccess) return hip_fail(e, "bsa_build_mask launch");
   return BSA_OK;
 }
@@ -170,7 +182,8 @@ static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !o || !mask || !mask->row_ptr || !mask->col_idx)
     return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": null pointer");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(mask->shift, 4))
     return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": misaligned pointer");
   const FwdWs w = fwd_ws_layout(*g);
   const int64_t need = whole_forward ? w.total : w.vt;   // bsa_attend only uses the counter block
@@ -191,10 +204,10 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
     int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
     e = launch_zero_i32(counter, 8, stream);   // one work counter per XCD
     if (e == hipSuccess)
-      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter, ncu, stream);
+      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, ncu, stream);
   } else {
     e = launch_attn_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
-                        mask->col_idx, stream);
+                        mask->col_idx, mask->shift, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return BSA_OK;

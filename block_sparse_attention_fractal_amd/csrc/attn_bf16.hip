@@ -3,7 +3,9 @@
 // Computes, for every query token of block i, softmax attention over exactly
 // the tokens of the key blocks listed in CSR row i (NABLA page,
 // gist.science/es/paper/2507.13546, Metodologia item 2, bullet "Expansion":
-// the block mask decides which N x N tiles are computed, all or nothing).
+// the block mask decides which N x N tiles are computed, all or nothing), with
+// an optional per-entry logit shift (the inclusion-probability weights of a SIP
+// mask, AB-Attention page, "Los tres recursos de AB-Attention").
 //
 // Work decomposition
 //   * a work item is a PAIR of adjacent query blocks (i, i+1) of one head; the
@@ -59,6 +61,7 @@ struct AttnBf16Args {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
+  const float* shift;  // per-entry natural-log logit shift, or null
   int32_t* counters;   // 8 per-XCD item counters
   Geom g;
   float c_log2;        // log2(e) / sqrt(D)
@@ -119,6 +122,7 @@ __device__ __forceinline__ int64_t item_cost_prefix(const AttnBf16Args& a, int64
   return a.row_ptr[row];
 }
 
+template <bool kShift>   // whether the CSR carries per-entry logit shifts
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];   // double-buffered K + V^T
   __shared__ int s_item;
@@ -181,13 +185,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     // indexed with readlane, so the union walk costs no memory round trip per tile;
     // a window is refilled (one coalesced load) every 64 entries.
     int wa_base = pa, wb_base = pb;
+    constexpr bool has_shift = kShift;
+    auto shift_at = [&](int idx, int end) -> int {   // the shift of entry idx, as float bits, one per lane
+      return has_shift && idx < end ? __float_as_int(a.shift[idx]) : 0;
+    };
     int wa = wa_base + lane < ea ? a.col_idx[wa_base + lane] : 0x7fffffff;
     int wb = wb_base + lane < eb ? a.col_idx[wb_base + lane] : 0x7fffffff;
+    int sa = shift_at(wa_base + lane, ea), sb = shift_at(wb_base + lane, eb);
     auto peek_a = [&]() -> int {
       if (pa >= ea) return 0x7fffffff;
       if (pa - wa_base >= 64) {
         wa_base = pa;
         wa = wa_base + lane < ea ? a.col_idx[wa_base + lane] : 0x7fffffff;
+        sa = shift_at(wa_base + lane, ea);
       }
       return __builtin_amdgcn_readlane(wa, pa - wa_base);
     };
@@ -196,16 +206,24 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       if (pb - wb_base >= 64) {
         wb_base = pb;
         wb = wb_base + lane < eb ? a.col_idx[wb_base + lane] : 0x7fffffff;
+        sb = shift_at(wb_base + lane, eb);
       }
       return __builtin_amdgcn_readlane(wb, pb - wb_base);
     };
-    // union walk over the two ascending key lists (wave-uniform scalars)
-    auto next_tile = [&](int& j, bool& ka, bool& kb) {
+    // union walk over the two ascending key lists (wave-uniform scalars); shl is
+    // the logit shift of this wave's block for the tile, in log2 units
+    auto next_tile = [&](int& j, bool& ka, bool& kb, float& shl) {
       const int ja = peek_a();
       const int jb = peek_b();
       j = min(ja, jb);
       ka = ja == j;
       kb = jb == j;
+      shl = 0.f;
+      if (has_shift) {
+        const float sha = ka ? __int_as_float(__builtin_amdgcn_readlane(sa, pa - wa_base)) : 0.f;
+        const float shb = kb ? __int_as_float(__builtin_amdgcn_readlane(sb, pb - wb_base)) : 0.f;
+        shl = (qb == 0 ? sha : shb) * 1.44269504088896341f;
+      }
       pa += ka;
       pb += kb;
     };
@@ -246,7 +264,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 
     int j;
     bool ka, kb;
-    next_tile(j, ka, kb);
+    float shl;
+    next_tile(j, ka, kb, shl);
     if (j != 0x7fffffff) issue(j, std::integral_constant<int, 0>{});
     // one tile: publish stage `stage`, prefetch the next tile into the other
     // stage, then both contractions and the softmax update; the loop is unrolled
@@ -255,7 +274,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       constexpr int stage = decltype(stage_c)::value;
       int jn;
       bool kan, kbn;
-      next_tile(jn, kan, kbn);
+      float shln;
+      next_tile(jn, kan, kbn, shln);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (jn != 0x7fffffff) issue(jn, std::integral_constant<int, stage ^ 1>{});
@@ -279,7 +299,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           m3[x] = fmaxf(fmaxf(sacc[x >> 2][4 * (x & 3)], sacc[x >> 2][4 * (x & 3) + 1]),
                         fmaxf(sacc[x >> 2][4 * (x & 3) + 2], sacc[x >> 2][4 * (x & 3) + 3]));
         float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])), fmaxf(fmaxf(m3[4], m3[5]), fmaxf(m3[6], m3[7])));
-        mx = pair_max(mx) * c_log2;
+        mx = pair_max(mx) * c_log2 + shl;
         if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
           const float m_new = fmaxf(m_ref, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -295,7 +315,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -m_ref));
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
             l_run += p;
             pbv[2 * t + (e >> 3)][e & 7] = (__bf16)p;
           }
@@ -312,6 +332,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       j = jn;
       ka = kan;
       kb = kbn;
+      shl = shln;
     };
     while (j != 0x7fffffff) {
       step(std::integral_constant<int, 0>{});
@@ -365,8 +386,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 }
 
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
-                            hipStream_t s) {
+                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
+                            int num_cu, hipStream_t s) {
   AttnBf16Args a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -375,6 +396,7 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.lse = lse;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
+  a.shift = shift;
   a.counters = counters;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
@@ -383,7 +405,10 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
   const int grid = ((num_cu * 2 + 7) / 8) * 8;   // two resident workgroups per CU, a multiple of 8 XCDs
-  attn_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  if (shift)
+    attn_bf16_kernel<true><<<grid, 256, 0, s>>>(a);
+  else
+    attn_bf16_kernel<false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

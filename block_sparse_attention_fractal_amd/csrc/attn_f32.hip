@@ -1,7 +1,8 @@
 // Block-sparse attention forward for float32 tensors (any CSR; head_dim 64 or 128).
 //
 // Same operation as the bf16 kernel (NABLA page, gist.science/es/paper/2507.13546,
-// Metodologia item 2, bullet "Expansion"), written for accuracy rather than
+// Metodologia item 2, bullet "Expansion"; an optional per-entry logit shift
+// carries the sampling weights of the SIP mask mode), written for accuracy rather than
 // speed: logits, the online softmax and the output accumulation are float64
 // (fp32 products are exact in float64), so the result stays within 1e-5 of a
 // float64 evaluation even when logits reach ~10^2.  One workgroup per CSR row;
@@ -17,7 +18,8 @@ template <int D>
 __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                        const float* __restrict__ v, float* __restrict__ o,
                                                        float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
-                                                       const int32_t* __restrict__ col_idx, Geom g, double scale) {
+                                                       const int32_t* __restrict__ col_idx,
+                                                       const float* __restrict__ shift, Geom g, double scale) {
   constexpr int DS = D / 4;
   __shared__ float Qs[64][D + 1];
   __shared__ float Ks[64][D + 1];
@@ -39,6 +41,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__
   const int beg = row_ptr[r], end = row_ptr[r + 1];
   for (int it = beg; it < end; ++it) {
     const int j = min(max(col_idx[it], 0), g.S - 1);
+    const double sh = shift ? (double)shift[it] : 0.0;   // the entry's logit shift, if any
     __syncthreads();
     for (int e = tid; e < 64 * D; e += 256) {
       const int row = e / D, d = e % D;
@@ -55,7 +58,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__
       double acc = 0.0;
 #pragma unroll 4
       for (int d = 0; d < D; ++d) acc = __fma_rn((double)Qs[qi][d], (double)Ks[kk][d], acc);
-      s[c] = acc * scale;
+      s[c] = acc * scale + sh;
       mt = fmax(mt, s[c]);
     }
     mt = fmax(mt, __shfl_xor(mt, 1));
@@ -89,12 +92,12 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__
 }
 
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
-                           const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s) {
+                           const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s) {
   const double scale = 1.0 / sqrt((double)g.D);
   if (g.D == 64)
-    attn_f32_kernel<64><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, g, scale);
+    attn_f32_kernel<64><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
   else
-    attn_f32_kernel<128><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, g, scale);
+    attn_f32_kernel<128><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
   return hipGetLastError();
 }
 

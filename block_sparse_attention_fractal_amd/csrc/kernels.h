@@ -22,6 +22,10 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 // CDF cut + window union per row -> bitmap [rows, words] and kept counts [rows].
 hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h,
                          int win_w, uint32_t* bitmap, int32_t* counts, int words, hipStream_t s);
+// SIP sampling per row (budget = counts on entry, the CDF cut's counts) -> bitmap,
+// counts and (max, sum, c, top block) per row in rowstat [rows, 4].
+hipError_t launch_sip(const Geom& g, const double* z, double thr, uint64_t seed, int win_t, int win_h, int win_w,
+                      uint32_t* bitmap, int32_t* counts, double* rowstat, int words, hipStream_t s);
 // Exclusive scan of counts -> row_ptr [rows+1]; row_ptr[rows] also copied to nnz (if not null).
 // chunk_sums: ceil(rows/1024) ints of scratch.
 hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, int32_t* chunk_sums, int32_t* nnz,
@@ -29,12 +33,16 @@ hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, i
 // Bitmap -> ascending col_idx at row_ptr offsets.
 hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr,
                           int32_t* col_idx, hipStream_t s);
-// Block-sparse attention forward.
+// Compaction of a SIP bitmap, also writing each entry's logit shift log(1/pi).
+hipError_t launch_compact_sip(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr,
+                              int32_t* col_idx, float* shift, const double* z, const double* rowstat, double thr,
+                              int win_t, int win_h, int win_w, hipStream_t s);
+// Block-sparse attention forward (shift: per-CSR-entry natural-log logit shift, or null).
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
-                            hipStream_t s);
+                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
+                            int num_cu, hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
-                           const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s);
+                           const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s);
 // Zero a small device counter (a fill kernel, safe under stream capture).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 

@@ -263,6 +263,16 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Sliding-tile window (NABLA page, Metodologia item 3): block ids are tiles
+// (t, y, x) of Hp x Wp patches per frame; ids i and j are within the window when
+// every coordinate differs by at most the given extent.
+__device__ __forceinline__ bool in_window(const Geom& g, int i, int j, int win_t, int win_h, int win_w) {
+  const int HW = g.Hp * g.Wp;
+  const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
+  const int tj = j / HW, yj = (j / g.Wp) % g.Hp, xj = j % g.Wp;
+  return abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w;
+}
+
 template <int NS>
 __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ z, Geom g, double thr, double lambda,
                                                      int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
@@ -527,14 +537,9 @@ __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ 
       }
     }
   }
-  if (win_t >= 0) {
-    const int HW = g.Hp * g.Wp;
-    const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
-    for (int j = lane; j < S; j += 64) {
-      const int tj = j / HW, yj = (j / g.Wp) % g.Hp, xj = j % g.Wp;
-      if (abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w) set_bit(j);
-    }
-  }
+  if (win_t >= 0)
+    for (int j = lane; j < S; j += 64)
+      if (in_window(g, i, j, win_t, win_h, win_w)) set_bit(j);
   __builtin_amdgcn_wave_barrier();
   uint32_t pc = 0;
   for (int x = lane; x < words; x += 64) {
@@ -557,6 +562,182 @@ hipError_t launch_select(const Geom& g, const double* z, double thr, double lamb
   else if (g.S <= 2048) BSA_SELECT(32);
   else BSA_SELECT(64);
 #undef BSA_SELECT
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SIP: sampling with inclusion-probability weights (AB-Attention page, "Los tres
+// recursos de AB-Attention", second resource), one wavefront per row.
+//
+//   p_j  = exp(z_j - max) / sum                       (the reduced map, float64)
+//   pi_top = 1 for the row's top block (largest p, lowest id on ties), and for
+//   the others pi_j = min(1, c p_j),  sum_j pi_j = k  (k = the row's CDF-cut count)
+//   take j iff u_rj < pi_j,  u_rj from Philox4x64-10 at counter (r, j, 0, 0),
+//   key (seed, 0): u = (word0 >> 11) * 2^-53
+//
+// c is found by capping: c = (k - t) / (mass of the uncapped blocks), then every
+// uncapped block with c p_j >= 1 is capped (pi = 1) and c recomputed, until none
+// is; c only grows along the way, so the capped blocks are exactly those with
+// c p_j >= 1 for the final c.  The row's (max, sum, c) are kept so that the
+// compaction recomputes pi of every taken block bit for bit and writes its
+// logit shift log(1 / pi); the top block's id is kept with them.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double block_prob(double z, double m, double sum) { return exp(z - m) / sum; }
+__device__ __forceinline__ double incl_prob(double p, double c) { return p > 0.0 ? fmin(1.0, c * p) : 0.0; }
+
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw: "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011): word 0 of the block at counter (c0, c1, 0, 0),
+// key (k0, 0).
+__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t k0) {
+  uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0, key0 = k0, key1 = 0;
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    const uint64_t hi0 = __umul64hi(x0, 0xD2E7470EE14C6C93ull), lo0 = x0 * 0xD2E7470EE14C6C93ull;
+    const uint64_t hi1 = __umul64hi(x2, 0xCA5A826395121157ull), lo1 = x2 * 0xCA5A826395121157ull;
+    x0 = hi1 ^ x1 ^ key0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ key1;
+    x3 = lo0;
+    key0 += 0x9E3779B97F4A7C15ull;
+    key1 += 0xBB67AE8584CAA73Bull;
+  }
+  return x0;
+}
+
+template <int NS>
+__global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, Geom g, double thr, uint64_t seed,
+                                                  int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
+                                                  int32_t* __restrict__ counts, double* __restrict__ rowstat,
+                                                  int words) {
+  __shared__ uint32_t bm_all[4][kMaxS / 32];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= g.rows) return;                     // whole wavefront; nothing below waits on other waves
+  uint32_t* bm = bm_all[wv];
+  const int S = g.S;
+  const int i = (int)(r % S);
+  const double* zr = z + r * S;
+  auto set_bit = [&](int j) { atomicOr(&bm[j >> 5], 1u << (j & 31)); };
+  auto dsum = [&](double v) { return wave_reduce(v, lane, [](double a, double b) { return a + b; }); };
+  auto isum = [&](int v) {
+    return (int)wave_reduce((uint32_t)v, lane, [](uint32_t a, uint32_t b) { return a + b; });
+  };
+  const int budget = counts[r];                // the CDF cut's count for this row
+
+  double m = 0.0, sum = 1.0, c = HUGE_VAL;
+  int top = -1;
+  if (thr == 0.0) {
+    for (int x = lane; x < words; x += 64) {
+      const int left = S - 32 * x;
+      bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    }
+  } else {
+    for (int x = lane; x < words; x += 64) bm[x] = 0u;
+    double p[NS];
+    m = -DBL_MAX;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int j = lane + 64 * k;
+      const double v = zr[min(j, S - 1)];
+      p[k] = j < S ? v : -DBL_MAX;
+      m = fmax(m, p[k]);
+    }
+    m = wave_reduce(m, lane, [](double a, double b) { return fmax(a, b); });
+    double part = 0.0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      p[k] = lane + 64 * k < S ? exp(p[k] - m) : 0.0;
+      part += p[k];
+    }
+    sum = dsum(part);
+    int pos = 0;
+    double pmax = 0.0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      p[k] = lane + 64 * k < S ? block_prob(zr[lane + 64 * k], m, sum) : 0.0;   // the compaction's formula
+      pos += p[k] > 0.0;
+      pmax = fmax(pmax, p[k]);
+    }
+    pos = isum(pos);
+    pmax = wave_reduce(pmax, lane, [](double a, double b) { return fmax(a, b); });
+    // the row's top block (largest probability, lowest id on ties) is always taken
+    int tj = S;
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      if (p[k] == pmax) tj = min(tj, lane + 64 * k);
+    top = (int)wave_reduce((uint32_t)tj, lane, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    // the others share budget - 1: min(1, c p_j), capped blocks found by iteration
+    const int kk = budget - 1;
+    if (kk <= 0) {
+      c = 0.0;
+    } else if (kk < pos - 1) {
+      uint64_t capped = 0;                     // bit k: slot k of this lane is capped (or the top block)
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        if (lane + 64 * k == top) capped |= 1ull << k;
+      int t = 0;
+      for (int it = 0; it <= S; ++it) {        // every pass caps at least one block
+        double rest = 0.0;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          if (!((capped >> k) & 1ull)) rest += p[k];
+        c = (double)(kk - t) / dsum(rest);
+        int fresh = 0;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          if (!((capped >> k) & 1ull) && p[k] > 0.0 && c * p[k] >= 1.0) {
+            capped |= 1ull << k;
+            ++fresh;
+          }
+        fresh = isum(fresh);
+        if (fresh == 0) break;
+        t += fresh;
+        // the budget is spent on capped blocks only when every other block has
+        // zero mass; keep the last c (> 0), for which the capped blocks give pi = 1
+        if (t >= kk) break;
+      }
+    }                                          // else c stays +inf: every positive block is taken
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int j = lane + 64 * k;
+      if (j < S) {
+        const double u = (double)(philox4x64_w0((uint64_t)r, (uint64_t)j, seed) >> 11) * 0x1p-53;
+        if (u < (j == top ? 1.0 : incl_prob(p[k], c))) set_bit(j);
+      }
+    }
+  }
+  if (win_t >= 0)
+    for (int j = lane; j < S; j += 64)
+      if (in_window(g, i, j, win_t, win_h, win_w)) set_bit(j);
+  __builtin_amdgcn_wave_barrier();
+  uint32_t pc = 0;
+  for (int x = lane; x < words; x += 64) {
+    const uint32_t v = bm[x];
+    bitmap[r * words + x] = v;
+    pc += __popc(v);
+  }
+  pc = wave_reduce(pc, lane, [](uint32_t a, uint32_t b) { return a + b; });
+  if (lane == 0) {
+    counts[r] = (int32_t)pc;
+    rowstat[4 * r + 0] = m;
+    rowstat[4 * r + 1] = sum;
+    rowstat[4 * r + 2] = c;
+    rowstat[4 * r + 3] = (double)top;
+  }
+}
+
+hipError_t launch_sip(const Geom& g, const double* z, double thr, uint64_t seed, int win_t, int win_h, int win_w,
+                      uint32_t* bitmap, int32_t* counts, double* rowstat, int words, hipStream_t s) {
+  const unsigned grid = (unsigned)((g.rows + 3) / 4);
+#define BSA_SIP(NS_) \
+  sip_kernel<NS_><<<grid, 256, 0, s>>>(z, g, thr, seed, win_t, win_h, win_w, bitmap, counts, rowstat, words)
+  if (g.S <= 128) BSA_SIP(2);
+  else if (g.S <= 512) BSA_SIP(8);
+  else if (g.S <= 1024) BSA_SIP(16);
+  else if (g.S <= 2048) BSA_SIP(32);
+  else BSA_SIP(64);
+#undef BSA_SIP
   return hipGetLastError();
 }
 
@@ -661,6 +842,49 @@ __global__ void __launch_bounds__(256) compact_kernel(const uint32_t* __restrict
 hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr, int32_t* col_idx,
                           hipStream_t s) {
   compact_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, s>>>(bitmap, words, row_ptr, col_idx, g.rows, g.S);
+  return hipGetLastError();
+}
+
+// The same compaction for a SIP mask, which also writes each entry's logit shift
+// log(1 / pi), pi recomputed from the row's (max, sum, c) exactly as sip_kernel
+// computed it; window blocks and thr == 0 rows carry shift 0.
+__global__ void __launch_bounds__(256) compact_sip_kernel(const uint32_t* __restrict__ bitmap, int words,
+                                                          const int32_t* __restrict__ row_ptr,
+                                                          int32_t* __restrict__ col_idx, float* __restrict__ shift,
+                                                          const double* __restrict__ z,
+                                                          const double* __restrict__ rowstat, Geom g, double thr,
+                                                          int win_t, int win_h, int win_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= g.rows) return;
+  const int S = g.S;
+  const int i = (int)(r % S);
+  const uint32_t* bm = bitmap + r * words;
+  const double m = rowstat[4 * r], sum = rowstat[4 * r + 1], c = rowstat[4 * r + 2];
+  const int top = (int)rowstat[4 * r + 3];
+  int32_t base = row_ptr[r];
+  for (int j0 = 0; j0 < S; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t wv = bm[min(j >> 5, words - 1)];
+    const bool on = j < S && ((wv >> (j & 31)) & 1u);
+    const uint64_t mask = __ballot(on);
+    if (on) {
+      const int32_t slot = base + __popcll(mask & ((1ull << lane) - 1));
+      col_idx[slot] = j;
+      float sh = 0.f;
+      if (thr != 0.0 && j != top && !(win_t >= 0 && in_window(g, i, j, win_t, win_h, win_w)))
+        sh = (float)(-log(incl_prob(block_prob(z[r * S + j], m, sum), c)));
+      shift[slot] = sh;
+    }
+    base += __popcll(mask);
+  }
+}
+
+hipError_t launch_compact_sip(const Geom& g, const uint32_t* bitmap, int words, const int32_t* row_ptr,
+                              int32_t* col_idx, float* shift, const double* z, const double* rowstat, double thr,
+                              int win_t, int win_h, int win_w, hipStream_t s) {
+  compact_sip_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, s>>>(bitmap, words, row_ptr, col_idx, shift, z, rowstat,
+                                                                  g, thr, win_t, win_h, win_w);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ int check_mask_params(const Geom& g, const bsa_mask_params* mp, std::string* msg
   if (!mp) return fail(msg, BSA_ERR_INVALID_ARG, "null mask params");
   if (!(mp->thr >= 0.0 && mp->thr < 1.0) || std::isnan(mp->thr))
     return fail(msg, BSA_ERR_INVALID_ARG, "thr must satisfy 0 <= thr < 1");
-  if (mp->reserved != 0) return fail(msg, BSA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (mp->mode != BSA_MASK_CDF && mp->mode != BSA_MASK_SIP)
+    return fail(msg, BSA_ERR_INVALID_ARG, "mode must be BSA_MASK_CDF or BSA_MASK_SIP");
   const int neg = (mp->win_t < 0) + (mp->win_h < 0) + (mp->win_w < 0);
   if (neg != 0 && neg != 3)
     return fail(msg, BSA_ERR_INVALID_ARG, "window extents must be all >= 0 (on) or all < 0 (off)");
@@ -76,6 +77,7 @@ MaskWs mask_ws_layout(const Geom& g) {
   w.counts = off; off = align256(off + g.rows * 4);
   w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
   w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
+  w.rowstat = off; off = align256(off + g.rows * 4 * 8);
   w.total = off;
   return w;
 }

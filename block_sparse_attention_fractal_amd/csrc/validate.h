@@ -13,7 +13,7 @@ int make_geom(const bsa_problem* p, Geom* g, std::string* msg);
 int check_mask_params(const Geom& g, const bsa_mask_params* mp, std::string* msg);
 
 struct MaskWs {       // byte offsets into the mask workspace
-  int64_t qp, kp, z, counts, bitmap, chunk_sums, total;
+  int64_t qp, kp, z, counts, bitmap, chunk_sums, rowstat, total;   // rowstat: SIP (max, sum, c, top) per row
   int32_t words;      // 32-bit words per bitmap row
 };
 struct FwdWs {

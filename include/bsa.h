@@ -86,19 +86,43 @@ typedef struct bsa_problem {
  * block.  The sliding-tile window is enabled when win_t, win_h and win_w are
  * all >= 0: query tile (t, y, x) then also keeps every key tile (t', y', x')
  * with |t-t'| <= win_t, |y-y'| <= win_h, |x-x'| <= win_w (clipped, no wrap);
- * it needs N == P*P.  All three < 0 disables it; mixed signs are an error. */
+ * it needs N == P*P.  All three < 0 disables it; mixed signs are an error.
+ *
+ * mode BSA_MASK_SIP replaces the cut by sampling with inclusion-probability
+ * weights (the SIP resource of the AB-Attention page, "AB-Attention acelera la
+ * generacion de video hasta 2,23x y omite el 92% de la atencion",
+ * news.hamidun.com/es/news/14960, section "Los tres recursos de AB-Attention"):
+ * row i always takes its top block (largest reduced-map probability A_ij,
+ * lowest j on ties) and samples every other block j independently with
+ * probability
+ *   pi_ij = min(1, c_i * A_ij),  c_i such that 1 + sum_{j != top} pi_ij = k_i,
+ * where the budget k_i is the number of blocks the CDF cut above keeps for that
+ * row (so the blocks with c_i * A_ij >= 1 are always taken too, and no row is
+ * empty).  The Bernoulli draw uses u = (w >> 11) * 2^-53, w = word 0 of
+ * Philox4x64-10 (Salmon et al., SC 2011) at counter (row, block, 0, 0) and key
+ * (seed, 0); the block is taken iff u < pi.  Each taken block carries the
+ * Horvitz-Thompson logit shift log(1 / pi) in the CSR's shift array, which
+ * makes the attention numerator and normaliser unbiased.  Window blocks are
+ * unioned afterwards with shift 0; thr == 0 keeps every block with shift 0. */
+enum { BSA_MASK_CDF = 0, BSA_MASK_SIP = 1 };
 typedef struct bsa_mask_params {
   double thr;
   int32_t win_t, win_h, win_w;
-  int32_t reserved;          /* must be 0 */
+  int32_t mode;              /* BSA_MASK_CDF or BSA_MASK_SIP */
+  uint64_t seed;             /* Philox key word 0 (BSA_MASK_SIP only) */
 } bsa_mask_params;
 
 /* CSR block mask (host struct holding device pointers). */
 typedef struct bsa_csr {
   int32_t* row_ptr;          /* device, [rows + 1], row_ptr[0] = 0 */
   int32_t* col_idx;          /* device, [capacity] */
-  int64_t capacity;          /* elements available in col_idx */
+  int64_t capacity;          /* elements available in col_idx (and shift) */
   int32_t* nnz;              /* device scalar receiving row_ptr[rows]; may be NULL */
+  float* shift;              /* device, [capacity], aligned with col_idx: natural-log
+                                shift added to every logit of that tile.  Written by
+                                bsa_build_mask in BSA_MASK_SIP mode (required there;
+                                with BSA_MASK_CDF it is left untouched); read by
+                                bsa_forward / bsa_attend when not NULL. */
 } bsa_csr;
 
 /* Sizes for a problem (all outputs are host pointers; any may be NULL).
@@ -128,10 +152,11 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, double* qp, dou
 int bsa_block_map(const bsa_problem* p, const double* qp, const double* kp, double* probs,
                   hipStream_t stream);
 
-/* Whole mask stage: pooling, reduced map, CDF cut, optional window union and
- * CSR compaction (Metodologia items 2 and 3).  q, k in p->layout order.
- * out->row_ptr receives rows+1 offsets, out->col_idx the ascending kept block
- * ids, out->nnz (if not NULL) the total.  ws: device workspace of at least
+/* Whole mask stage: pooling, reduced map, CDF cut (or SIP sampling, see
+ * bsa_mask_params), optional window union and CSR compaction (Metodologia
+ * items 2 and 3).  q, k in p->layout order.  out->row_ptr receives rows+1
+ * offsets, out->col_idx the ascending kept block ids, out->nnz (if not NULL)
+ * the total, and in SIP mode out->shift the per-entry logit shifts.  ws: device workspace of at least
  * mask_ws bytes (bsa_query_sizes), 256-byte aligned; its contents on entry do
  * not matter and are clobbered. */
 int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* q, const void* k,
@@ -140,11 +165,12 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
 /* Block-sparse attention forward (Metodologia item 2, "Expansion"): every query
  * token of block i attends, with scale 1/sqrt(head_dim), to all tokens of the
  * key blocks listed in CSR row i of its head and to nothing else:
- *   o_n = sum_k softmax_k(q_n . k_k / sqrt(D)) v_k,  lse_n = log sum_k exp(q_n . k_k / sqrt(D)).
- * q, k, v, o: [batch, heads, L, head_dim] in p->layout order (o written in the
- * same order as q); lse: float32 [batch, heads, L] in the same token order, or
- * NULL.  mask->row_ptr / col_idx as produced by bsa_build_mask (capacity and
- * nnz are not read).  Every CSR row must be non-empty with ids in [0, S).
+ *   o_n = sum_k softmax_k(q_n . k_k / sqrt(D) + s_k) v_k,  lse_n = log sum_k exp(q_n . k_k / sqrt(D) + s_k),
+ * where s_k is the shift of the CSR entry of k's block (0 when mask->shift is
+ * NULL).  q, k, v, o: [batch, heads, L, head_dim] in p->layout order (o written
+ * in the same order as q); lse: float32 [batch, heads, L] in the same token
+ * order, or NULL.  mask->row_ptr / col_idx (/ shift) as produced by
+ * bsa_build_mask (capacity and nnz are not read).  Every CSR row must be non-empty with ids in [0, S).
  * ws: device workspace of at least fwd_ws bytes, 256-byte aligned. */
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v,
                 const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes,
@@ -167,7 +193,7 @@ int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v
 const char* bsa_status_str(int status);
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* bsa_last_error(void);
-/* ABI version (major*10000 + minor*100 + patch). */
+/* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts. */
 int bsa_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 100
+    assert lib.bsa_version() == 200
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -60,10 +60,11 @@ def test_query_sizes(lib, B, nh, T, H, W):
     assert st == 0
     S = T * H * W // 64
     assert rows == B * nh * S and max_nnz == rows * S
-    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap, scan chunk sums (each 256-aligned)
+    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap, scan chunk sums,
+    # SIP row statistics (4 float64 per row), each 256-aligned
     a = lambda x: (x + 255) // 256 * 256
     assert mws == (a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
-                   + a((rows + 1023) // 1024 * 4))
+                   + a((rows + 1023) // 1024 * 4) + a(rows * 32))
     assert fws == 256 + a(B * nh * T * H * W * D * 2)
     assert mws % 256 == 0 and fws % 256 == 0
 
@@ -95,18 +96,20 @@ def test_fractal_layout_allows_other_patch_sizes(lib):
 FAKE = 1 << 20          # never dereferenced: every call below fails validation first
 
 
-def _mask_call(lib, p, thr=0.1, win=(-1, -1, -1), reserved=0, cap=None, ws_bytes=None, q=FAKE, ws=FAKE):
+def _mask_call(lib, p, thr=0.1, win=(-1, -1, -1), mode=0, cap=None, ws_bytes=None, q=FAKE, ws=FAKE, shift=None):
     st, (rows, max_nnz, mws, _) = sizes(lib, p)
-    mp = _lib.MaskParams(thr, win[0], win[1], win[2], reserved)
-    csr = _lib.CSR(FAKE, FAKE, max_nnz if cap is None else cap, None)
+    mp = _lib.MaskParams(thr, win[0], win[1], win[2], mode, 7)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz if cap is None else cap, None, shift)
     return lib.bsa_build_mask(ctypes.byref(p), ctypes.byref(mp), q, FAKE, ctypes.byref(csr), ws,
                               mws if ws_bytes is None else ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(thr=1.0), 1), (dict(thr=-0.1), 1), (dict(thr=float("nan")), 1), (dict(win=(1, -1, 1)), 1),
-    (dict(reserved=3), 1), (dict(cap=10), 5), (dict(ws_bytes=1000), 6), (dict(q=None), 1),
+    (dict(mode=3), 1), (dict(mode=-1), 1), (dict(cap=10), 5), (dict(ws_bytes=1000), 6), (dict(q=None), 1),
     (dict(q=FAKE + 2), 1), (dict(ws=FAKE + 64), 6),
+    (dict(mode=1), 1),                                   # SIP without a shift array
+    (dict(mode=1, shift=FAKE + 2), 1),                   # misaligned shift array
 ])
 def test_build_mask_rejects_before_launch(lib, kw, code):
     st = _mask_call(lib, P(), **kw)
@@ -121,13 +124,21 @@ def test_window_needs_square_patch_blocks(lib):
 def test_forward_rejects_before_launch(lib):
     p = P()
     st, (rows, max_nnz, mws, fws) = sizes(lib, p)
-    csr = _lib.CSR(FAKE, FAKE, max_nnz, None)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
     f = lib.bsa_forward
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws - 1, None) == 6
     assert f(ctypes.byref(p), FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 1
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE + 2, FAKE, fws, None) == 1
     bad = P(dtype=7)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 3
+    shifted = _lib.CSR(FAKE, FAKE, max_nnz, None, FAKE + 2)          # misaligned shift array
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(shifted), FAKE, None, FAKE, fws, None) == 1
+
+
+def test_struct_layouts_match_the_header():
+    # bsa_mask_params: double, 4 x int32, uint64 -> 32 bytes; bsa_csr: 5 pointer-sized fields
+    assert ctypes.sizeof(_lib.MaskParams) == 32 and _lib.MaskParams.seed.offset == 24
+    assert ctypes.sizeof(_lib.CSR) == 40 and _lib.CSR.shift.offset == 32
 
 
 def test_permute_and_pool_reject_before_launch(lib):
