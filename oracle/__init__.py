@@ -20,7 +20,11 @@ block_sparse_attention, dense_attention.
 AB-Attention page (news.hamidun.com/es/news/14960, "Los tres recursos de
 AB-Attention", second resource), pinned in tests/test_oracle_sip_pins.py against
 numpy's Philox4x64-10, a bisection solve of the sampling design and Monte-Carlo
-unbiasedness.  No function is "parity unpinned".
+unbiasedness.  `orders.py` adds the tile-major (TRA page) and 3D Hilbert
+(DFSAttn page) token orders, pinned in tests/test_oracle_orders_pins.py by
+bijection, equality with the fractal order for one-frame tiles, cube-shaped
+blocks and the unit-step walk of the Hilbert curve over a full 2^b cube.
+No function is "parity unpinned".
 """
 from .nabla import (
     fractal_positions,
