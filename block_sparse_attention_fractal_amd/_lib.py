@@ -14,10 +14,12 @@ BSA_OK = 0
 BSA_F32, BSA_BF16 = 0, 1
 BSA_LAYOUT_ORIGINAL, BSA_LAYOUT_FRACTAL = 0, 1
 BSA_MASK_CDF, BSA_MASK_SIP = 0, 1
+BSA_ORDER_FRACTAL, BSA_ORDER_TILE_MAJOR, BSA_ORDER_HILBERT = 0, 1, 2
 
 # every symbol declared in include/bsa.h
-EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_pool", "bsa_block_map", "bsa_build_mask",
-            "bsa_forward", "bsa_prepare_v", "bsa_attend", "bsa_status_str", "bsa_last_error", "bsa_version"]
+EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
+            "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_attend", "bsa_status_str",
+            "bsa_last_error", "bsa_version"]
 
 
 class Problem(ctypes.Structure):
@@ -59,6 +61,8 @@ def lib():
     P = ctypes.POINTER
     l.bsa_query_sizes.argtypes = [P(Problem), P(i64), P(i64), P(i64), P(i64)]
     l.bsa_permute.argtypes = [P(Problem), vp, vp, ctypes.c_int, vp]
+    l.bsa_order_table.argtypes = [P(Problem), ctypes.c_int, vp]
+    l.bsa_permute_table.argtypes = [P(Problem), vp, vp, vp, ctypes.c_int, vp]
     l.bsa_pool.argtypes = [P(Problem), vp, vp, vp, vp, vp]
     l.bsa_block_map.argtypes = [P(Problem), vp, vp, vp, vp]
     l.bsa_build_mask.argtypes = [P(Problem), P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
@@ -70,8 +74,8 @@ def lib():
     l.bsa_last_error.argtypes = []
     l.bsa_last_error.restype = ctypes.c_char_p
     l.bsa_version.argtypes = []
-    for name in ("bsa_query_sizes", "bsa_permute", "bsa_pool", "bsa_block_map", "bsa_build_mask",
-                 "bsa_forward", "bsa_prepare_v", "bsa_attend", "bsa_version"):
+    for name in ("bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
+                 "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_attend", "bsa_version"):
         getattr(l, name).restype = ctypes.c_int
     _lib = l
     return l

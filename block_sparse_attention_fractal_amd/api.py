@@ -113,6 +113,37 @@ def permute(x: torch.Tensor, grid: VideoGrid, inverse: bool = False) -> torch.Te
     return y
 
 
+ORDERS = {"fractal": _lib.BSA_ORDER_FRACTAL, "tile_major": _lib.BSA_ORDER_TILE_MAJOR,
+          "hilbert": _lib.BSA_ORDER_HILBERT}
+
+
+def order_table(grid: VideoGrid, order: str, head_dim: int = 128, dtype=torch.bfloat16) -> torch.Tensor:
+    """int32 [L] CPU tensor: the original (t,h,w) index of the token at each position
+    of the given order ("fractal", "tile_major" or "hilbert"), computed by the library."""
+    if order not in ORDERS:
+        raise ValueError(f"order must be one of {sorted(ORDERS)}")
+    x = torch.empty((1, 1, 0, head_dim), dtype=dtype)          # shape carrier only
+    prob = _lib.Problem(1, 1, grid.T, grid.H, grid.W, head_dim, grid.patch, grid.block, _dtype_code(x),
+                        BSA_LAYOUT_FRACTAL)   # the layout does not enter the table; this one accepts any P
+    table = torch.empty(grid.T * grid.H * grid.W, dtype=torch.int32)
+    check(lib().bsa_order_table(ctypes.byref(prob), ORDERS[order], table.data_ptr()))
+    return table
+
+
+def permute_table(x: torch.Tensor, grid: VideoGrid, table: torch.Tensor, inverse: bool = False) -> torch.Tensor:
+    """Rows of x into the order given by `table` (inverse=False) or back; bit-exact copy.
+    table: int32 permutation of [0, L) (moved to x's device if needed)."""
+    _check_qkv(x)
+    if table.dtype != torch.int32 or table.numel() != x.shape[2]:
+        raise ValueError("table must be int32 with one entry per token")
+    t = table.to(x.device).contiguous()
+    y = torch.empty_like(x)
+    prob = make_problem(x, grid, "fractal")     # the layout does not enter a table copy
+    check(lib().bsa_permute_table(ctypes.byref(prob), t.data_ptr(), x.data_ptr(), y.data_ptr(), int(inverse),
+                                  _stream(x.device)))
+    return y
+
+
 def pool(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, layout: str = "original") -> Tuple[torch.Tensor, torch.Tensor]:
     """Block means of q and k, float64 [batch, heads, S, head_dim]."""
     _check_qkv(q, k)

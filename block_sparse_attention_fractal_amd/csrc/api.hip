@@ -6,6 +6,7 @@
 
 #include "bsa.h"
 #include "kernels.h"
+#include "order.h"
 #include "validate.h"
 
 using namespace bsa;
@@ -93,6 +94,31 @@ int bsa_permute(const bsa_problem* p, const void* x, void* y, int inverse, hipSt
   if (x == y) return fail(BSA_ERR_INVALID_ARG, "bsa_permute: in-place permutation is not supported");
   hipError_t e = launch_permute(g, x, y, inverse, stream);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return BSA_OK;
+}
+
+int bsa_order_table(const bsa_problem* p, int order, int32_t* table) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!table) return fail(BSA_ERR_INVALID_ARG, "bsa_order_table: null table");
+  std::string msg;
+  st = order_table(g, order, table, &msg);
+  if (st != BSA_OK) return fail(st, "bsa_order_table: " + msg);
+  return BSA_OK;
+}
+
+int bsa_permute_table(const bsa_problem* p, const int32_t* table, const void* x, void* y, int inverse,
+                      hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!table || !x || !y) return fail(BSA_ERR_INVALID_ARG, "bsa_permute_table: null pointer");
+  if (!aligned(table, 4) || !aligned(x, 16) || !aligned(y, 16))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_permute_table: misaligned pointer");
+  if (x == y) return fail(BSA_ERR_INVALID_ARG, "bsa_permute_table: in-place permutation is not supported");
+  hipError_t e = launch_permute_table(g, table, x, y, inverse, stream);
+  if (e != hipSuccess) return hip_fail(e, "permute_table launch");
   return BSA_OK;
 }
 

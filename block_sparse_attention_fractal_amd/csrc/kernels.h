@@ -10,6 +10,9 @@ namespace bsa {
 
 // Fractal flattening as a bit-exact copy of [B*nh, L, D] rows.
 hipError_t launch_permute(const Geom& g, const void* x, void* y, int inverse, hipStream_t s);
+// Bit-exact row copy through a device permutation table (any token order).
+hipError_t launch_permute_table(const Geom& g, const int32_t* table, const void* x, void* y, int inverse,
+                                hipStream_t s);
 // V in the tensor's layout -> Vt [B*nh, S, D, 64] bf16: block-major, each
 // block transposed to d-major with keys in MFMA operand order.
 hipError_t launch_prep_vt(const Geom& g, const void* v, void* vt, hipStream_t s);

@@ -36,6 +36,37 @@ hipError_t launch_permute(const Geom& g, const void* x, void* y, int inverse, hi
   return hipGetLastError();
 }
 
+// Any other token order, from a device table: y[bh, f] = x[bh, table[f]] (or the
+// reverse scatter).  Entries are clamped into [0, L), so a malformed table
+// copies wrong rows but never leaves the tensors.
+__global__ void __launch_bounds__(256) permute_table_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                            const int32_t* __restrict__ table, Geom g, int inverse,
+                                                            int cpr, int64_t total_chunks) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
+    const int64_t row = c / cpr;
+    const int32_t part = (int32_t)(c - row * cpr);
+    const int64_t bh = row / g.L;
+    const int32_t f = (int32_t)(row - bh * g.L);
+    const int64_t orow = bh * g.L + min(max(table[f], 0), g.L - 1);
+    if (!inverse)
+      y[row * cpr + part] = x[orow * cpr + part];
+    else
+      y[orow * cpr + part] = x[row * cpr + part];
+  }
+}
+
+hipError_t launch_permute_table(const Geom& g, const int32_t* table, const void* x, void* y, int inverse,
+                                hipStream_t s) {
+  const int elt = g.dtype == 1 ? 2 : 4;
+  const int cpr = g.D * elt / 16;
+  const int64_t total = (int64_t)g.B * g.nh * g.L * cpr;
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 65536 * 8 ? want : 65536 * 8);
+  permute_table_kernel<<<grid, 256, 0, s>>>((const uint4*)x, (uint4*)y, table, g, inverse, cpr, total);
+  return hipGetLastError();
+}
+
 // Vt[bh][j][d][p] = V[bh][token(j, key(p))][d] with D = 128, 64 keys per block.
 // Inside every group of 16 keys, stored position p holds key perm(p) with
 // perm = 0,1,2,3, 8,9,10,11, 4,5,6,7, 12,13,14,15: the key order in which the

@@ -138,6 +138,37 @@ int bsa_query_sizes(const bsa_problem* p, int64_t* rows, int64_t* max_nnz,
  * p->layout is ignored. */
 int bsa_permute(const bsa_problem* p, const void* x, void* y, int inverse, hipStream_t stream);
 
+/* Alternative token orders (drop-in variants of the fractal flattening).  A
+ * caller permutes Q, K, V with bsa_permute_table into any of these orders and
+ * runs the rest of the path with layout BSA_LAYOUT_FRACTAL, which means "block
+ * i = positions [i*N, (i+1)*N) of the given order"; O comes back in that order
+ * (bsa_permute_table with inverse != 0 restores (t, h, w) order).  The sliding-
+ * tile window assumes the fractal order's block geometry and is meaningless in
+ * the other orders.
+ *   BSA_ORDER_FRACTAL    the NABLA fractal order (the same permutation as
+ *                        bsa_permute);
+ *   BSA_ORDER_TILE_MAJOR tiles of (N/P^2) x P x P tokens spanning N/P^2 frames
+ *                        (tile-major layout of the TRA page, "Atencion de
+ *                        Radio de Tokens", gist.science/es/paper/2608.02504,
+ *                        "El Pipeline de TRA", item 3), tiles and
+ *                        tokens row-major in (t, y, x); needs T % (N/P^2) == 0;
+ *                        equals the fractal order when N == P*P;
+ *   BSA_ORDER_HILBERT    increasing index along the 3D Hilbert curve of the
+ *                        smallest 2^b cube holding the grid, axes (t, y, x),
+ *                        Skilling's transpose form (DFSAttn page,
+ *                        gist.science/es/paper/2605.23445, section 1).
+ * bsa_order_table fills the HOST array table[L] with the original (t, h, w)
+ * row-major index of the token at each position (pure host computation).
+ * bsa_permute_table copies rows bit-exactly: inverse == 0 gives
+ * y[b,h,f,:] = x[b,h,table[f],:], inverse != 0 the reverse scatter.  table is a
+ * DEVICE array of L int32 that must be a permutation of [0, L) (entries are
+ * clamped into range, so a malformed table yields wrong rows but no fault);
+ * x, y must not overlap. */
+enum { BSA_ORDER_FRACTAL = 0, BSA_ORDER_TILE_MAJOR = 1, BSA_ORDER_HILBERT = 2 };
+int bsa_order_table(const bsa_problem* p, int order, int32_t* table);
+int bsa_permute_table(const bsa_problem* p, const int32_t* table, const void* x, void* y, int inverse,
+                      hipStream_t stream);
+
 /* Block average pooling (Metodologia item 2, "Submuestreo"): qp[b,h,i,:] is the
  * mean of Q over the N tokens of fractal block i, likewise kp for K; outputs
  * are float64 [batch, heads, S, head_dim].  Inputs in p->layout order.  The
