@@ -14,7 +14,8 @@ per-function citations and the readings taken where the page is silent.
 Pinned (checked against closed forms, brute force or library routines in
 tests/test_oracle_pins.py): fractal_positions, permute, inverse_permute,
 pool_blocks, reduced_map, cdf_keep, sta_window, csr_from_keep,
-block_sparse_attention, dense_attention.
+block_sparse_attention, block_sparse_attention_backward (finite differences
+and torch autograd in float64), dense_attention.
 
 `sip.py` adds the sampled selection with inclusion-probability weights of the
 AB-Attention page (news.hamidun.com/es/news/14960, "Los tres recursos de
@@ -38,6 +39,7 @@ from .nabla import (
     head_mask,
     build_mask,
     block_sparse_attention,
+    block_sparse_attention_backward,
     dense_attention,
     attention_pipeline,
     tile_coords,
@@ -46,5 +48,6 @@ from .nabla import (
 __all__ = [
     "fractal_positions", "permute", "inverse_permute", "pool_blocks", "reduced_map",
     "cdf_keep", "sta_window", "csr_from_keep", "head_mask", "build_mask",
-    "block_sparse_attention", "dense_attention", "attention_pipeline", "tile_coords",
+    "block_sparse_attention", "block_sparse_attention_backward", "dense_attention", "attention_pipeline",
+    "tile_coords",
 ]

@@ -241,3 +241,47 @@ def attention_pipeline(q, k, v, T, H, W, P, N, thr, window=None):
     LSE = np.empty_like(LSEf)
     LSE[..., src] = LSEf
     return O, LSE, mask
+
+
+# --------------------------------------------------------------------------
+# backward of the block-sparse attention (the training use of the mask)
+# --------------------------------------------------------------------------
+def block_sparse_attention_backward(qf, kf, vf, row_ptr, col_idx, dO, N: int, rows=None):
+    """Gradients of sum(O * dO) for the attention above, float64, written out from
+    the chain rule of softmax attention (the NABLA page's method is trained with
+    this mask, Metodologia item 2 "Expansion"; the gradient of the kept-tile
+    attention is the dense one restricted to the kept tiles):
+        P = softmax(Z),  Z = q k^T / sqrt(D)           (over the kept keys only)
+        dV_k += sum_n P[n,k] dO_n
+        dP[n,k] = dO_n . v_k
+        dZ[n,k] = P[n,k] (dP[n,k] - sum_k' P[n,k'] dP[n,k'])
+        dQ_n = sum_k dZ[n,k] k_k / sqrt(D),   dK_k += sum_n dZ[n,k] q_n / sqrt(D).
+    qf, kf, vf, dO: [B, nh, L, D] in fractal order; CSR as in block_sparse_attention.
+    Returns (dQ, dK, dV) [B, nh, L, D] float64; `rows` restricts the query blocks
+    whose contributions are summed (the full gradient needs every row)."""
+    B, nh, L, D = qf.shape
+    S = L // N
+    dQ = np.zeros((B, nh, L, D))
+    dK = np.zeros((B, nh, L, D))
+    dV = np.zeros((B, nh, L, vf.shape[-1]))
+    scale = 1.0 / math.sqrt(D)
+    rows = range(B * nh * S) if rows is None else rows
+    for r in rows:
+        bh, i = divmod(int(r), S)
+        b, h = divmod(bh, nh)
+        cols = np.asarray(col_idx[row_ptr[r]:row_ptr[r + 1]], dtype=np.int64)
+        keys = (cols[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+        qs = slice(i * N, (i + 1) * N)
+        q = np.asarray(qf[b, h, qs], np.float64)
+        kk = np.asarray(kf[b, h, keys], np.float64)
+        vv = np.asarray(vf[b, h, keys], np.float64)
+        do = np.asarray(dO[b, h, qs], np.float64)
+        z = (q @ kk.T) * scale
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dp = do @ vv.T
+        dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dQ[b, h, qs] = dz @ kk * scale
+        np.add.at(dK[b, h], keys, dz.T @ q * scale)
+        np.add.at(dV[b, h], keys, p.T @ do)
+    return dQ, dK, dV

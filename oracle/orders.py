@@ -3,11 +3,13 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Sources:
-  * tile-major order -- TRA page ("gist.science/es/paper/2605.23445"), section
+  * tile-major order -- TRA page ("Resumen Tecnico: Atencion de Radio de Tokens para la Generacion
+    Eficiente de Video", gist.science/es/paper/2608.02504), section
     "El Pipeline de TRA", item 3 "Ejecucion Eficiente", bullet "Disposicion
     Tile-Major": video tokens are laid out so that spatial neighbours inside a
     tile are contiguous in the sequence;
-  * 3D Hilbert order -- DFSAttn page ("gist.science/es/paper/2608.02504"),
+  * 3D Hilbert order -- DFSAttn page ("DFSAttn: Dynamic Fine-grained Sparse Attention for Efficient
+    Video Generation", gist.science/es/paper/2605.23445),
     section 1, the "Curva de Hilbert" shuffle: tokens are ordered along a 3D
     Hilbert curve so that neighbours in the sequence are neighbours in space and
     time, and every block holds a coherent region.
