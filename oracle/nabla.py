@@ -246,7 +246,7 @@ def attention_pipeline(q, k, v, T, H, W, P, N, thr, window=None):
 # --------------------------------------------------------------------------
 # backward of the block-sparse attention (the training use of the mask)
 # --------------------------------------------------------------------------
-def block_sparse_attention_backward(qf, kf, vf, row_ptr, col_idx, dO, N: int, rows=None):
+def block_sparse_attention_backward(qf, kf, vf, row_ptr, col_idx, dO, N: int, rows=None, O=None):
     """Gradients of sum(O * dO) for the attention above, float64, written out from
     the chain rule of softmax attention (the NABLA page's method is trained with
     this mask, Metodologia item 2 "Expansion"; the gradient of the kept-tile
@@ -257,6 +257,10 @@ def block_sparse_attention_backward(qf, kf, vf, row_ptr, col_idx, dO, N: int, ro
         dZ[n,k] = P[n,k] (dP[n,k] - sum_k' P[n,k'] dP[n,k'])
         dQ_n = sum_k dZ[n,k] k_k / sqrt(D),   dK_k += sum_n dZ[n,k] q_n / sqrt(D).
     qf, kf, vf, dO: [B, nh, L, D] in fractal order; CSR as in block_sparse_attention.
+    sum_k' P[n,k'] dP[n,k'] equals dO_n . o_n for the exact output o; when the
+    forward's output O (fractal order) is given, the row term is taken as
+    dO_n . O_n from it -- the form a kernel that stores O and not P uses -- so a
+    rounded O enters the gradient exactly as it does there.
     Returns (dQ, dK, dV) [B, nh, L, D] float64; `rows` restricts the query blocks
     whose contributions are summed (the full gradient needs every row)."""
     B, nh, L, D = qf.shape
@@ -280,7 +284,11 @@ def block_sparse_attention_backward(qf, kf, vf, row_ptr, col_idx, dO, N: int, ro
         e = np.exp(z - z.max(axis=1, keepdims=True))
         p = e / e.sum(axis=1, keepdims=True)
         dp = do @ vv.T
-        dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        if O is None:
+            delta = (p * dp).sum(axis=1, keepdims=True)
+        else:
+            delta = (do * np.asarray(O[b, h, qs], np.float64)).sum(axis=1, keepdims=True)
+        dz = p * (dp - delta)
         dQ[b, h, qs] = dz @ kk * scale
         np.add.at(dK[b, h], keys, dz.T @ q * scale)
         np.add.at(dV[b, h], keys, p.T @ do)

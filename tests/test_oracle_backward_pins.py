@@ -72,3 +72,15 @@ def test_dense_mask_matches_torch_autograd():
     (p @ tv * torch.tensor(do)).sum().backward()
     for mine, ref in ((dQ, tq.grad), (dK, tk.grad), (dV, tv.grad)):
         assert np.allclose(mine, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_row_term_from_the_exact_output_changes_nothing():
+    q, k, v, do, rp, ci, N = _sparse_problem(11)
+    O, _ = oracle.block_sparse_attention(q, k, v, rp, ci, N)
+    a = oracle.block_sparse_attention_backward(q, k, v, rp, ci, do, N)
+    b = oracle.block_sparse_attention_backward(q, k, v, rp, ci, do, N, O=O)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-12)
+    # a perturbed output moves dQ and dK but never dV
+    c = oracle.block_sparse_attention_backward(q, k, v, rp, ci, do, N, O=O * 1.01)
+    assert not np.allclose(a[0], c[0]) and np.array_equal(a[2], c[2])
