@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also print per-stage details on stderr")
+    ap.add_argument("--sip-seed", type=int, default=None,
+                    help="build the mask by SIP sampling with this Philox seed instead of the CDF cut")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path shards by (batch, head) "
@@ -163,7 +165,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window, workspace=mask_ws)
+        mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window, workspace=mask_ws, sip_seed=args.sip_seed)
         if ev is not None:
             ev[1].record(stream)
         vt = bsa.prepare_v(v, g)
@@ -238,6 +240,7 @@ def main():
         "mask_stage": {"algorithmic_bytes": mask_bytes, "gbs": round(mask_gbs, 1),
                        "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4)},
         "prepare_v": {"gbs": round(prep_gbs, 1), "hbm_frac": round(prep_gbs / HBM_PEAK_GBS, 4)},
+        "mask_mode": "cdf" if args.sip_seed is None else f"sip(seed={args.sip_seed})",
         "density": round(density, 5),
         "nnz": nnz,
         "executed_tflop": round(exec_flops / 1e12, 3),

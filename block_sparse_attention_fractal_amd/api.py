@@ -263,3 +263,22 @@ def attention(q, k, v, grid: VideoGrid, thr: float, window=None, layout: str = "
     mask = build_mask(q, k, grid, thr, window, layout)
     out = forward(q, k, v, mask, grid, layout, return_lse)
     return (out, mask)
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+             o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, layout: str = "original",
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for forward(q, k, v, mask) with its o and lse."""
+    _check_qkv(q, k, v, o, dout)
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [batch, heads, L] as forward(return_lse=True) gives it")
+    prob = make_problem(q, grid, layout)
+    nbytes = ctypes.c_int64()
+    check(lib().bsa_query_backward_ws(ctypes.byref(prob), ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, q.device, workspace)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    csr = mask.as_struct()
+    check(lib().bsa_backward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
+                             o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return dq, dk, dv

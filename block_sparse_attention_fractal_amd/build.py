@@ -20,8 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "validate.cpp",
-           "order.cpp"]
+SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "bwd.hip",
+           "validate.cpp", "order.cpp"]
 
 
 def hipcc() -> str:

@@ -239,6 +239,62 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
   return BSA_OK;
 }
 
+int bsa_query_backward_ws(const bsa_problem* p, int64_t* bwd_ws) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!bwd_ws) return fail(BSA_ERR_INVALID_ARG, "bsa_query_backward_ws: null output");
+  *bwd_ws = bwd_ws_layout(g).total;
+  return BSA_OK;
+}
+
+int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                 int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !mask || !mask->row_ptr || !mask->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: null pointer");
+  const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* t : t16)
+    if (!aligned(t, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: tensors must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: misaligned lse");
+  if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: masks with logit shifts are not supported");
+  const BwdWs w = bwd_ws_layout(g);
+  if (!ws || ws_bytes < w.total)
+    return fail(BSA_ERR_WORKSPACE, "bsa_backward: workspace needs " + std::to_string(w.total) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, "bsa_backward: workspace must be 256-byte aligned");
+  int ncu = 0;
+  if (g.dtype == BSA_BF16) {
+    st = current_cu_count(&ncu);
+    if (st != BSA_OK) return st;
+  }
+  char* base = static_cast<char*>(ws);
+  float2* ld = reinterpret_cast<float2*>(base + w.delta);
+  int32_t* counters = reinterpret_cast<int32_t*>(base + w.counter);
+  int32_t* tcounts = reinterpret_cast<int32_t*>(base + w.tcounts);
+  uint32_t* tbits = reinterpret_cast<uint32_t*>(base + w.tbitmap);
+  int32_t* tcolptr = reinterpret_cast<int32_t*>(base + w.tcolptr);
+  int32_t* trowidx = reinterpret_cast<int32_t*>(base + w.trowidx);
+  hipError_t e = launch_backward_prep(g, o, dout, lse, ld, mask->row_ptr, mask->col_idx, tbits, w.words, tcounts,
+                                      stream);
+  if (e == hipSuccess)
+    e = launch_scan(g, tcounts, tcolptr, reinterpret_cast<int32_t*>(base + w.tchunks), nullptr, stream);
+  if (e == hipSuccess) e = launch_compact(g, tbits, w.words, tcolptr, trowidx, stream);
+  if (e == hipSuccess && g.dtype == BSA_BF16) {
+    e = launch_prep_vt(g, k, base + w.kt, stream);
+    if (e == hipSuccess) e = launch_prep_vt(g, q, base + w.qt, stream);
+    if (e == hipSuccess) e = launch_prep_vt(g, dout, base + w.dot, stream);
+  }
+  if (e == hipSuccess) e = launch_zero_i32(counters, 16, stream);
+  if (e == hipSuccess)
+    e = launch_backward(g, q, k, v, dout, base + w.kt, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
+                        mask->col_idx, tcolptr, trowidx, counters, ncu, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return BSA_OK;
+}
+
 int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream) {
   Geom g;
   int st = geom_or_fail(p, &g);

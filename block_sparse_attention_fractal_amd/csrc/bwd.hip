@@ -1,0 +1,758 @@
+// Backward of the block-sparse attention, for training with the mask (NABLA
+// page, gist.science/es/paper/2507.13546, Metodologia item 2, "Expansion": the
+// attention runs on the kept N x N tiles only, and so does its gradient).
+//
+//   P = softmax over the kept keys of z = q.k / sqrt(D)   (recomputed from lse)
+//   dV_k = sum_n P[n,k] dO_n          dP[n,k] = dO_n . v_k
+//   dZ[n,k] = P[n,k] (dP[n,k] - Delta_n),   Delta_n = dO_n . o_n
+//   dQ_n = sum_k dZ[n,k] k_k / sqrt(D)      dK_k = sum_n dZ[n,k] q_n / sqrt(D)
+//
+// Two passes, no atomics on the gradients (deterministic):
+//   * dQ: query-major over the CSR, a pair of query blocks per workgroup (the
+//     forward kernel's schedule): S^T = K Q^T and dP^T = V dO^T with the
+//     32x32x16 bf16 MFMA (each lane holds 32 keys of one query), dZ^T in
+//     registers, then dQ^T += K^T dZ^T with K^T pre-transposed in HBM in the
+//     same key order as the forward's V^T;
+//   * dK, dV: key-major over the transposed mask (built here: a bitmap per key
+//     block, counted, scanned and compacted), a pair of key blocks per
+//     workgroup: S = Q K^T and dP = dO V^T with the key fragments in registers
+//     (each lane holds 32 queries of one key), then dV^T += dO^T P and
+//     dK^T += Q^T dZ with Q^T and dO^T pre-transposed.
+// float32 tensors take two plain kernels with float64 arithmetic (accuracy
+// rather than speed, as in the forward's float32 path).
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "bsa.h"
+#include "kernels.h"
+
+namespace bsa {
+namespace bwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kD = 128;
+constexpr int kTile = 16384;          // one 64 x 128 bf16 tile (natural or transposed)
+
+// natural tile (64 rows x 256 B), chunk c of row r at c ^ (r & 15)
+__device__ __forceinline__ int nat_lds(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// transposed tile (128 rows x 128 B), chunk c of row d at c ^ ((d >> 1) & 7)
+__device__ __forceinline__ int tr_lds(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+struct Args {
+  const uint16_t* q;       // natural [B*nh, L, D] (tensor layout)
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const uint16_t* kt;      // prepared transposes [B*nh, S, D, 64]
+  const uint16_t* qt;
+  const uint16_t* dot;
+  const float2* ld;        // per token: (lse * log2 e, Delta)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* ptr;      // CSR (dQ pass) or transposed CSR (dK/dV pass)
+  const int32_t* idx;
+  int32_t* counters;       // 8 per-XCD item counters
+  Geom g;
+  float c_log2;            // log2(e) / sqrt(D)
+  float inv_sqrt_d;
+  int32_t pairs, items;
+};
+
+// first token row of block j in the tensor's own layout (rs*(m/8) + m%8 further for token m)
+__device__ __forceinline__ int block_base_row(const Geom& g, int j) {
+  if (g.layout == 1) return j * 64;
+  const int px = j % g.Wp;
+  const int rest = j / g.Wp;
+  const int py = rest % g.Hp;
+  const int t = rest / g.Hp;
+  return (t * g.H + py * 8) * g.W + px * 8;
+}
+
+__device__ __forceinline__ int64_t item_cost_prefix(const Args& a, int64_t t) {
+  const int64_t bh = t / a.pairs;
+  const int64_t p = t - bh * a.pairs;
+  int64_t row = bh * a.g.S + 2 * p;
+  if (row > a.g.rows) row = a.g.rows;
+  return a.ptr[row];
+}
+
+// XCD-partitioned item range of this workgroup (balanced by cumulative entries)
+__device__ __forceinline__ void item_range(const Args& a, int xcd, int64_t& lo_t, int64_t& hi_t) {
+  const int64_t total = a.ptr[a.g.rows];
+  auto first_item_with_cost = [&](int64_t target) {
+    int64_t lo = 0, hi = a.items;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (item_cost_prefix(a, mid + 1) > target) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
+  hi_t = xcd == 7 ? a.items : first_item_with_cost(total * (xcd + 1) / 8);
+}
+
+// Union walk over the ascending lists of rows r0 and r0+1 (wave-uniform).  Each
+// list is read through a 64-entry window held one entry per lane.
+struct PairWalk {
+  int pa, ea, pb, eb, wa_base, wb_base, wa, wb;
+  __device__ __forceinline__ void init(const Args& a, int64_t r0, bool two, int lane) {
+    pa = a.ptr[r0];
+    ea = a.ptr[r0 + 1];
+    pb = two ? a.ptr[r0 + 1] : 0;
+    eb = two ? a.ptr[r0 + 2] : 0;
+    wa_base = pa;
+    wb_base = pb;
+    wa = wa_base + lane < ea ? a.idx[wa_base + lane] : 0x7fffffff;
+    wb = wb_base + lane < eb ? a.idx[wb_base + lane] : 0x7fffffff;
+  }
+  __device__ __forceinline__ int peek(const Args& a, int& p, int e, int& base, int& w, int lane) {
+    if (p >= e) return 0x7fffffff;
+    if (p - base >= 64) {
+      base = p;
+      w = base + lane < e ? a.idx[base + lane] : 0x7fffffff;
+    }
+    return __builtin_amdgcn_readlane(w, p - base);
+  }
+  __device__ __forceinline__ void next(const Args& a, int lane, int& j, bool& ka, bool& kb) {
+    const int ja = peek(a, pa, ea, wa_base, wa, lane);
+    const int jb = peek(a, pb, eb, wb_base, wb, lane);
+    j = min(ja, jb);
+    ka = ja == j;
+    kb = jb == j;
+    pa += ka;
+    pb += kb;
+  }
+};
+
+// Stores a pair of 64 x 128 bf16 blocks from the transposed accumulators of the
+// four waves (wave w: block w >> 1, columns 32 (w & 1) .. +31), through LDS.
+__device__ __forceinline__ void store_pair(uint8_t* stage, const f32x16 (&acc)[4], float mul, bool valid, int wave,
+                                           int lane, int tid, const Geom& g, int i0, bool two, uint16_t* out_head) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const int blk = wave >> 1, col = 32 * (wave & 1) + l32;   // col = token of the block
+  __syncthreads();
+  if (valid) {
+    uint8_t* ob = stage + blk * 16384;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int unit = 8 * u + 2 * rq + h;
+        uint2 w;
+        w.x = pack_bf16x2(acc[u][4 * rq + 0] * mul, acc[u][4 * rq + 1] * mul);
+        w.y = pack_bf16x2(acc[u][4 * rq + 2] * mul, acc[u][4 * rq + 3] * mul);
+        *(uint2*)(ob + col * 256 + ((unit ^ (col & 31)) << 3)) = w;
+      }
+    }
+  }
+  __syncthreads();
+  const int sb = tid >> 7;
+  if (sb == 0 || two) {
+    const int rs = g.layout == 1 ? 8 : g.W;
+    const int t7 = tid & 127;
+    const int lchunk = t7 & 15;
+    const int base = block_base_row(g, i0 + sb);
+    const uint8_t* ob = stage + sb * 16384;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (t7 >> 4) + 8 * u;
+      const uint2 lo = *(const uint2*)(ob + row * 256 + (((2 * lchunk) ^ (row & 31)) << 3));
+      const uint2 hi = *(const uint2*)(ob + row * 256 + (((2 * lchunk + 1) ^ (row & 31)) << 3));
+      const int tok = base + (row >> 3) * rs + (row & 7);
+      *(uint4*)(out_head + (size_t)tok * kD + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass (bf16).  Stage: natural K | natural V | transposed K, 48 KB; two stages.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256, 1) dq_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[3 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[3 * kTile];
+  __shared__ int s_item;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int qb = wave >> 1, wq = wave & 1;
+  const Geom g = a.g;
+  const int rs = g.layout == 1 ? 8 : g.W;
+  const float c_log2 = a.c_log2;
+
+  int noff[4], toff[4];              // per-lane byte offsets of the 16-byte chunks this thread loads
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = (4 * wave + u) * 64 + lane;
+    const int m = c >> 4;
+    const int lc = (lane & 15) ^ (m & 15);
+    noff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
+    const int d = c >> 3;
+    const int lv = (lane & 7) ^ ((d >> 1) & 7);
+    toff[u] = d * 128 + lv * 16;
+  }
+  const int xcd = blockIdx.x & 7;
+  int64_t lo_t, hi_t;
+  item_range(a, xcd, lo_t, hi_t);
+
+  for (;;) {
+    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    __syncthreads();
+    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= hi_t) break;
+    const int64_t bh = item / a.pairs;
+    const int i0 = 2 * (int)(item - bh * a.pairs);
+    const int64_t r0 = bh * g.S + i0;
+    const bool two = i0 + 1 < g.S;
+    const bool has_q = qb == 0 || two;
+    PairWalk wk;
+    wk.init(a, r0, two, lane);
+
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.kt + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
+    auto issue = [&](int j, uint8_t* st) {
+      const int jc = min(max(j, 0), g.S - 1);
+      const int ns = block_base_row(g, jc) * kD * 2;
+      const int ts = jc * kD * 64 * 2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int slot = (4 * wave + u) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + slot), 16, noff[u], ns, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kTile + slot), 16, noff[u], ns, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (lds_void*)(st + 2 * kTile + slot), 16, toff[u], ts, 0, 0);
+      }
+    };
+
+    bf16x8 qreg[8], doreg[8];
+    float lse2 = 0.f, dlt = 0.f;
+    if (has_q) {
+      const int qtok = block_base_row(g, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
+      const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
+      const uint16_t* drow = a.dout + ((size_t)bh * g.L + qtok) * kD + 8 * h;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        qreg[s] = *(const bf16x8*)(qrow + 16 * s);
+        doreg[s] = *(const bf16x8*)(drow + 16 * s);
+      }
+      const float2 ld = a.ld[(size_t)bh * g.L + qtok];
+      lse2 = ld.x;
+      dlt = ld.y;
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[u][e] = 0.f;
+
+    int j;
+    bool ka, kb;
+    wk.next(a, lane, j, ka, kb);
+    if (j != 0x7fffffff) issue(j, stage0);
+    auto step = [&](uint8_t* st, uint8_t* other) {
+      int jn;
+      bool kan, kbn;
+      wk.next(a, lane, jn, kan, kbn);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (jn != 0x7fffffff) issue(jn, other);
+      const bool mine = qb == 0 ? ka : kb;
+      if (mine) {
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sacc[t][e] = 0.f;
+            pacc[t][e] = 0.f;
+          }
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const bf16x8 ak = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+            const bf16x8 av = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
+            pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc[t], 0, 0, 0);
+          }
+        }
+        // dZ = hi + lo, two bf16 terms: the dZ of one query sum to zero, so dQ is a
+        // small difference of large terms when K has a large common part, and a
+        // single bf16 rounding of dZ (2^-9) would show in it at the percent level.
+        bf16x8 dsh[4], dsl[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -lse2));
+            const float ds = p * (pacc[t][e] - dlt);
+            const __bf16 hi = (__bf16)ds;
+            dsh[2 * t + (e >> 3)][e & 7] = hi;
+            dsl[2 * t + (e >> 3)][e & 7] = (__bf16)(ds - (float)hi);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bf16x8 at = *(const bf16x8*)(st + 2 * kTile + tr_lds(32 * u + l32, 2 * s + h));
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsh[s], acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsl[s], acc[u], 0, 0, 0);
+          }
+        }
+      }
+      j = jn;
+      ka = kan;
+      kb = kbn;
+    };
+    while (j != 0x7fffffff) {
+      step(stage0, stage1);
+      if (j == 0x7fffffff) break;
+      step(stage1, stage0);
+    }
+    store_pair(stage0, acc, a.inv_sqrt_d, has_q, wave, lane, tid, g, i0, two, a.dq + (size_t)bh * g.L * kD);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV pass (bf16), key-major over the transposed mask.  Stage: natural Q |
+// natural dO | transposed Q | transposed dO | (lse2, Delta) of the 64 queries:
+// 64.5 KB; two stages.
+// ---------------------------------------------------------------------------
+constexpr int kLdOff = 4 * kTile;
+constexpr int kStageB = 4 * kTile + 512;
+
+__global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageB];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageB];
+  __shared__ int s_item;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int kbk = wave >> 1, wkk = wave & 1;     // key block of the pair, which 32 keys of it
+  const Geom g = a.g;
+  const int rs = g.layout == 1 ? 8 : g.W;
+  const float c_log2 = a.c_log2;
+
+  int noff[4], toff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = (4 * wave + u) * 64 + lane;
+    const int m = c >> 4;
+    const int lc = (lane & 15) ^ (m & 15);
+    noff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
+    const int d = c >> 3;
+    const int lv = (lane & 7) ^ ((d >> 1) & 7);
+    toff[u] = d * 128 + lv * 16;
+  }
+  // (lse2, Delta) of the 64 queries: 32 chunks of 16 bytes = 2 tokens each, wave 0
+  const int ldm = 2 * (lane & 31);
+  const int ldoff = (((ldm >> 3) * rs + (ldm & 7))) * 8;
+  const int xcd = blockIdx.x & 7;
+  int64_t lo_t, hi_t;
+  item_range(a, xcd, lo_t, hi_t);
+
+  for (;;) {
+    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    __syncthreads();
+    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= hi_t) break;
+    const int64_t bh = item / a.pairs;
+    const int j0 = 2 * (int)(item - bh * a.pairs);
+    const int64_t r0 = bh * g.S + j0;
+    const bool two = j0 + 1 < g.S;
+    const bool has_k = kbk == 0 || two;
+    PairWalk wk;
+    wk.init(a, r0, two, lane);
+
+    const size_t hoff = (size_t)bh * g.L * kD;
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hoff), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t drs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hoff), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qtrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.qt + hoff), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t dtrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.dot + hoff), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t lrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + (size_t)bh * g.L), (short)0, g.L * 8, 0x00020000);
+    auto issue = [&](int i, uint8_t* st) {
+      const int ic = min(max(i, 0), g.S - 1);
+      const int base = block_base_row(g, ic);
+      const int ns = base * kD * 2;
+      const int ts = ic * kD * 64 * 2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int slot = (4 * wave + u) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + slot), 16, noff[u], ns, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + kTile + slot), 16, noff[u], ns, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qtrs, (lds_void*)(st + 2 * kTile + slot), 16, toff[u], ts, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dtrs, (lds_void*)(st + 3 * kTile + slot), 16, toff[u], ts, 0, 0);
+      }
+      if (wave == 0 && lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(st + kLdOff), 16, ldoff, base * 8, 0, 0);
+    };
+
+    bf16x8 kreg[8], vreg[8];
+    if (has_k) {
+      const int ktok = block_base_row(g, j0 + kbk) + ((32 * wkk + l32) >> 3) * rs + (l32 & 7);
+      const uint16_t* krow = a.k + ((size_t)bh * g.L + ktok) * kD + 8 * h;
+      const uint16_t* vrow = a.v + ((size_t)bh * g.L + ktok) * kD + 8 * h;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        kreg[s] = *(const bf16x8*)(krow + 16 * s);
+        vreg[s] = *(const bf16x8*)(vrow + 16 * s);
+      }
+    }
+    f32x16 dka[4], dva[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dka[u][e] = 0.f;
+        dva[u][e] = 0.f;
+      }
+
+    int i;
+    bool ka, kb;
+    wk.next(a, lane, i, ka, kb);
+    if (i != 0x7fffffff) issue(i, stage0);
+    auto step = [&](uint8_t* st, uint8_t* other) {
+      int in_;
+      bool kan, kbn;
+      wk.next(a, lane, in_, kan, kbn);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (in_ != 0x7fffffff) issue(in_, other);
+      const bool mine = kbk == 0 ? ka : kb;
+      if (mine) {
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sacc[t][e] = 0.f;
+            pacc[t][e] = 0.f;
+          }
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const bf16x8 aq = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc[t], 0, 0, 0);
+            const bf16x8 ad = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
+            pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[s], pacc[t], 0, 0, 0);
+          }
+        }
+        // accumulator register e of tile t holds query 32t + 8(e/4) + 4h + e%4
+        bf16x8 pb[4], db[4];
+        const float2* ldt = (const float2*)(st + kLdOff);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float2 ld = ldt[32 * t + 8 * (e >> 2) + 4 * h + (e & 3)];
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -ld.x));
+            pb[2 * t + (e >> 3)][e & 7] = (__bf16)p;
+            db[2 * t + (e >> 3)][e & 7] = (__bf16)(p * (pacc[t][e] - ld.y));
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bf16x8 adt = *(const bf16x8*)(st + 3 * kTile + tr_lds(32 * u + l32, 2 * s + h));
+            dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt, pb[s], dva[u], 0, 0, 0);
+            const bf16x8 aqt = *(const bf16x8*)(st + 2 * kTile + tr_lds(32 * u + l32, 2 * s + h));
+            dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, db[s], dka[u], 0, 0, 0);
+          }
+        }
+      }
+      i = in_;
+      ka = kan;
+      kb = kbn;
+    };
+    while (i != 0x7fffffff) {
+      step(stage0, stage1);
+      if (i == 0x7fffffff) break;
+      step(stage1, stage0);
+    }
+    store_pair(stage0, dva, 1.f, has_k, wave, lane, tid, g, j0, two, a.dv + hoff);
+    store_pair(stage0, dka, a.inv_sqrt_d, has_k, wave, lane, tid, g, j0, two, a.dk + hoff);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 tensors: plain kernels, float64 arithmetic, one workgroup per row of
+// the (transposed) mask; head_dim 64 or 128.
+// ---------------------------------------------------------------------------
+// The query/key rows a thread works on live in LDS (not registers): at D = 128
+// they would not fit; dZ is kept in float64 at D = 64 and float32 at D = 128 so
+// that the four 64 x D tiles plus dZ stay within the 160 KB of LDS.
+template <int D>
+using ZT = typename std::conditional<D == 64, double, float>::type;
+
+template <int D>
+__global__ void __launch_bounds__(256) dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                     const float* __restrict__ v, const float* __restrict__ dout,
+                                                     const float2* __restrict__ ld, float* __restrict__ dq,
+                                                     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+                                                     Geom g, double scale) {
+  constexpr int DS = D / 4;
+  __shared__ float Qs[64][D + 1];
+  __shared__ float Os[64][D + 1];       // dO rows of the query block
+  __shared__ float Ks[64][D + 1];
+  __shared__ float Vs[64][D + 1];
+  __shared__ ZT<D> Zs[64][65];
+  const int64_t r = blockIdx.x;
+  const int64_t bh = r / g.S;
+  const int i = (int)(r - bh * g.S);
+  const int tid = threadIdx.x, qi = tid >> 2, sl = tid & 3;
+  const size_t hoff = (size_t)bh * g.L * D;
+  const int qtok = block_token_row(g, i, qi);
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int row = e / D, d = e % D;
+    const size_t off = hoff + (size_t)block_token_row(g, i, row) * D + d;
+    Qs[row][d] = q[off];
+    Os[row][d] = dout[off];
+  }
+  const float2 l = ld[(size_t)bh * g.L + qtok];
+  const double lse = (double)l.x * 0.69314718055994530942, dlt = l.y;
+  double acc[DS];
+#pragma unroll
+  for (int d = 0; d < DS; ++d) acc[d] = 0.0;
+  for (int it = ptr[r]; it < ptr[r + 1]; ++it) {
+    const int j = min(max(idx[it], 0), g.S - 1);
+    __syncthreads();
+    for (int e = tid; e < 64 * D; e += 256) {
+      const int row = e / D, d = e % D;
+      const size_t off = hoff + (size_t)block_token_row(g, j, row) * D + d;
+      Ks[row][d] = k[off];
+      Vs[row][d] = v[off];
+    }
+    __syncthreads();
+    for (int c = 0; c < 16; ++c) {
+      const int kk = sl + 4 * c;
+      double s = 0.0, dp = 0.0;
+      for (int d = 0; d < D; ++d) {
+        s = __fma_rn((double)Qs[qi][d], (double)Ks[kk][d], s);
+        dp = __fma_rn((double)Os[qi][d], (double)Vs[kk][d], dp);
+      }
+      const double p = exp(s * scale - lse);
+      Zs[qi][kk] = (ZT<D>)(p * (dp - dlt));
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 64; ++kk) {
+      const double z = Zs[qi][kk];
+#pragma unroll 8
+      for (int d = 0; d < DS; ++d) acc[d] = __fma_rn(z, (double)Ks[kk][sl * DS + d], acc[d]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DS; ++d) dq[hoff + (size_t)qtok * D + sl * DS + d] = (float)(acc[d] * scale);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                       const float* __restrict__ v, const float* __restrict__ dout,
+                                                       const float2* __restrict__ ld, float* __restrict__ dk,
+                                                       float* __restrict__ dv, const int32_t* __restrict__ ptr,
+                                                       const int32_t* __restrict__ idx, Geom g, double scale) {
+  constexpr int DS = D / 4;
+  __shared__ float Ks[64][D + 1];
+  __shared__ float Vs[64][D + 1];
+  __shared__ float Qs[64][D + 1];
+  __shared__ float Os[64][D + 1];       // dO rows of the query block
+  __shared__ double Ls[64][2];
+  const int64_t r = blockIdx.x;              // transposed row: key block j of head bh
+  const int64_t bh = r / g.S;
+  const int j = (int)(r - bh * g.S);
+  const int tid = threadIdx.x, ki = tid >> 2, sl = tid & 3;
+  const size_t hoff = (size_t)bh * g.L * D;
+  const int ktok = block_token_row(g, j, ki);
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int row = e / D, d = e % D;
+    const size_t off = hoff + (size_t)block_token_row(g, j, row) * D + d;
+    Ks[row][d] = k[off];
+    Vs[row][d] = v[off];
+  }
+  double dka[DS], dva[DS];
+#pragma unroll
+  for (int d = 0; d < DS; ++d) {
+    dka[d] = 0.0;
+    dva[d] = 0.0;
+  }
+  for (int it = ptr[r]; it < ptr[r + 1]; ++it) {
+    const int i = min(max(idx[it], 0), g.S - 1);
+    __syncthreads();
+    for (int e = tid; e < 64 * D; e += 256) {
+      const int row = e / D, d = e % D;
+      const size_t off = hoff + (size_t)block_token_row(g, i, row) * D + d;
+      Qs[row][d] = q[off];
+      Os[row][d] = dout[off];
+    }
+    if (tid < 64) {
+      const float2 l = ld[(size_t)bh * g.L + block_token_row(g, i, tid)];
+      Ls[tid][0] = (double)l.x * 0.69314718055994530942;
+      Ls[tid][1] = l.y;
+    }
+    __syncthreads();
+    // thread (key ki, slice sl): P and dZ of its key against every query (the four
+    // slices of a key recompute them; this path is for accuracy, not speed)
+    for (int qq = 0; qq < 64; ++qq) {
+      double s = 0.0, dp = 0.0;
+      for (int d = 0; d < D; ++d) {
+        s = __fma_rn((double)Qs[qq][d], (double)Ks[ki][d], s);
+        dp = __fma_rn((double)Os[qq][d], (double)Vs[ki][d], dp);
+      }
+      const double p = exp(s * scale - Ls[qq][0]);
+      const double z = p * (dp - Ls[qq][1]);
+#pragma unroll 8
+      for (int d = 0; d < DS; ++d) {
+        dva[d] = __fma_rn(p, (double)Os[qq][sl * DS + d], dva[d]);
+        dka[d] = __fma_rn(z, (double)Qs[qq][sl * DS + d], dka[d]);
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DS; ++d) {
+    dk[hoff + (size_t)ktok * D + sl * DS + d] = (float)(dka[d] * scale);
+    dv[hoff + (size_t)ktok * D + sl * DS + d] = (float)dva[d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// helpers: per-token (lse * log2 e, dO.o), the transposed mask
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float to_f(T x);
+template <>
+__device__ __forceinline__ float to_f<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <>
+__device__ __forceinline__ float to_f<float>(float x) { return x; }
+
+// 16 lanes per token row, each summing D/16 products in float32
+template <typename T>
+__global__ void __launch_bounds__(256) delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                    const float* __restrict__ lse, float2* __restrict__ ld,
+                                                    int64_t ntok, int D) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < ntok)
+    for (int d = sub; d < D; d += 16) s = fmaf(to_f<T>(o[row * D + d]), to_f<T>(dout[row * D + d]), s);
+  s += __shfl_xor(s, 1, 16);
+  s += __shfl_xor(s, 2, 16);
+  s += __shfl_xor(s, 4, 16);
+  s += __shfl_xor(s, 8, 16);
+  if (row < ntok && sub == 0) ld[row] = make_float2(lse[row] * 1.44269504088896341f, s);
+}
+
+__global__ void __launch_bounds__(256) zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) p[x] = 0u;
+}
+
+// bit (j, i) of the transposed bitmap for every kept tile (i, j); one wavefront per CSR row
+__global__ void __launch_bounds__(256) transpose_bits_kernel(const int32_t* __restrict__ row_ptr,
+                                                             const int32_t* __restrict__ col_idx,
+                                                             uint32_t* __restrict__ tbits, Geom g, int words) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= g.rows) return;
+  const int64_t bh = r / g.S;
+  const int i = (int)(r - bh * g.S);
+  for (int e = row_ptr[r] + lane; e < row_ptr[r + 1]; e += 64) {
+    const int j = min(max(col_idx[e], 0), g.S - 1);
+    atomicOr(&tbits[(bh * g.S + j) * words + (i >> 5)], 1u << (i & 31));
+  }
+}
+
+__global__ void __launch_bounds__(256) popcount_rows_kernel(const uint32_t* __restrict__ bits,
+                                                            int32_t* __restrict__ counts, int64_t rows, int words) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  int c = 0;
+  for (int x = lane; x < words; x += 64) c += __popc(bits[r * words + x]);
+  for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
+  if (lane == 0) counts[r] = c;
+}
+
+}  // namespace bwd
+
+hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, const float* lse, float2* ld,
+                                const int32_t* row_ptr, const int32_t* col_idx, uint32_t* tbits, int words,
+                                int32_t* tcounts, hipStream_t s) {
+  const int64_t ntok = (int64_t)g.B * g.nh * g.L;
+  const unsigned dgrid = (unsigned)((ntok * 16 + 255) / 256);
+  if (g.dtype == BSA_BF16)
+    bwd::delta_kernel<uint16_t><<<dgrid, 256, 0, s>>>((const uint16_t*)o, (const uint16_t*)dout, lse, ld, ntok, g.D);
+  else
+    bwd::delta_kernel<float><<<dgrid, 256, 0, s>>>((const float*)o, (const float*)dout, lse, ld, ntok, g.D);
+  const int64_t nbits = g.rows * words;
+  bwd::zero_u32_kernel<<<(unsigned)std::min<int64_t>((nbits + 255) / 256, 65536), 256, 0, s>>>(tbits, nbits);
+  const unsigned rgrid = (unsigned)((g.rows + 3) / 4);
+  bwd::transpose_bits_kernel<<<rgrid, 256, 0, s>>>(row_ptr, col_idx, tbits, g, words);
+  bwd::popcount_rows_kernel<<<rgrid, 256, 0, s>>>(tbits, tcounts, g.rows, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
+                           const void* kt, const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
+                           const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s) {
+  const double scale = 1.0 / sqrt((double)g.D);
+  if (g.dtype == BSA_F32) {
+    const unsigned grid = (unsigned)g.rows;
+    if (g.D == 64) {
+      bwd::dq_f32_kernel<64><<<grid, 256, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
+                                                   (const float*)dout, ld, (float*)dq, row_ptr, col_idx, g, scale);
+      bwd::dkdv_f32_kernel<64><<<grid, 256, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
+                                                     (const float*)dout, ld, (float*)dk, (float*)dv, tcolptr, trowidx,
+                                                     g, scale);
+    } else {
+      bwd::dq_f32_kernel<128><<<grid, 256, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
+                                                    (const float*)dout, ld, (float*)dq, row_ptr, col_idx, g, scale);
+      bwd::dkdv_f32_kernel<128><<<grid, 256, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
+                                                      (const float*)dout, ld, (float*)dk, (float*)dv, tcolptr,
+                                                      trowidx, g, scale);
+    }
+    return hipGetLastError();
+  }
+  bwd::Args a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.dout = (const uint16_t*)dout;
+  a.kt = (const uint16_t*)kt;
+  a.qt = (const uint16_t*)qt;
+  a.dot = (const uint16_t*)dot;
+  a.ld = ld;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.g = g;
+  a.c_log2 = (float)(1.4426950408889634 * scale);
+  a.inv_sqrt_d = (float)scale;
+  a.pairs = (g.S + 1) / 2;
+  a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
+  const int grid = ((num_cu + 7) / 8) * 8;        // one workgroup per CU (LDS-limited), a multiple of 8 XCDs
+  a.ptr = row_ptr;
+  a.idx = col_idx;
+  a.counters = counters;
+  bwd::dq_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  a.ptr = tcolptr;
+  a.idx = trowidx;
+  a.counters = counters + 8;
+  bwd::dkdv_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -46,6 +46,17 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
                             int num_cu, hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s);
+// Backward: per-token (lse*log2e, dO.o) into ld, and the transposed mask's bitmap
+// and per-key-block counts (scan and compact them to get the transposed CSR).
+hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, const float* lse, float2* ld,
+                                const int32_t* row_ptr, const int32_t* col_idx, uint32_t* tbits, int words,
+                                int32_t* tcounts, hipStream_t s);
+// Backward: dQ over the CSR, dK/dV over the transposed CSR (kt, qt, dot: prepared
+// transposes of K, Q, dO for bf16; counters: 16 ints, zeroed).
+hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
+                           const void* kt, const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
+                           const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s);
 // Zero a small device counter (a fill kernel, safe under stream capture).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 

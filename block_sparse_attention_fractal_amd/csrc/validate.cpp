@@ -92,4 +92,26 @@ FwdWs fwd_ws_layout(const Geom& g) {
   return w;
 }
 
+BwdWs bwd_ws_layout(const Geom& g) {
+  BwdWs w{};
+  w.words = (g.S + 31) / 32;
+  const int64_t tok = (int64_t)g.B * g.nh * g.L;
+  int64_t off = 0;
+  w.delta = off; off = align256(off + tok * 8);     // float2 per token
+  w.counter = off; off = align256(off + 64);
+  w.tcounts = off; off = align256(off + g.rows * 4);
+  w.tchunks = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
+  w.tbitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
+  w.tcolptr = off; off = align256(off + (g.rows + 1) * 4);
+  w.trowidx = off; off = align256(off + g.rows * (int64_t)g.S * 4);
+  w.kt = w.qt = w.dot = off;
+  if (g.dtype == BSA_BF16) {
+    w.kt = off; off = align256(off + tok * g.D * 2);
+    w.qt = off; off = align256(off + tok * g.D * 2);
+    w.dot = off; off = align256(off + tok * g.D * 2);
+  }
+  w.total = off;
+  return w;
+}
+
 }  // namespace bsa

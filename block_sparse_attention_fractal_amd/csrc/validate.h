@@ -19,6 +19,11 @@ struct MaskWs {       // byte offsets into the mask workspace
 struct FwdWs {
   int64_t counter, vt, total;
 };
+struct BwdWs {        // transposed mask, per-token dO.o, work counters, prepared transposes (bf16)
+  int64_t delta, counter, tcounts, tchunks, tbitmap, tcolptr, trowidx, kt, qt, dot, total;
+  int32_t words;
+};
+BwdWs bwd_ws_layout(const Geom& g);
 MaskWs mask_ws_layout(const Geom& g);
 FwdWs fwd_ws_layout(const Geom& g);
 

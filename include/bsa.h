@@ -220,11 +220,33 @@ int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t str
 int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
                void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
 
+/* Backward of the block-sparse attention (the gradient of sum(O * dO) with
+ * respect to Q, K and V, for training with the mask, NABLA page, Metodologia
+ * item 2 "Expansion"): with P = softmax over each query's kept keys of
+ * q.k / sqrt(D),
+ *   dV_k = sum_n P[n,k] dO_n,   dP[n,k] = dO_n . v_k,
+ *   dZ[n,k] = P[n,k] (dP[n,k] - dO_n . o_n),
+ *   dQ_n = sum_k dZ[n,k] k_k / sqrt(D),   dK_k = sum_n dZ[n,k] q_n / sqrt(D).
+ * q, k, v, o, dout, dq, dk, dv: [batch, heads, L, head_dim] in p->layout order
+ * (o and lse as returned by bsa_forward for the same mask; lse float32
+ * [batch, heads, L], required).  mask: the forward's CSR; per-entry shifts are
+ * not supported here (BSA_ERR_UNSUPPORTED when mask->shift is not NULL).  Every
+ * output element is written (key blocks no query keeps get zero dK, dV); the
+ * result is deterministic (no atomics on the gradients: dQ is summed per query
+ * block, dK and dV per key block over the transposed mask, which the call
+ * builds in its workspace).  ws: at least bwd_ws bytes (bsa_query_backward_ws),
+ * 256-byte aligned. */
+int bsa_query_backward_ws(const bsa_problem* p, int64_t* bwd_ws);
+int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                 int64_t ws_bytes, hipStream_t stream);
+
 /* Status code -> static string. */
 const char* bsa_status_str(int status);
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* bsa_last_error(void);
-/* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts. */
+/* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
+ * token-order tables and the backward pass. */
 int bsa_version(void);
 
 #ifdef __cplusplus
