@@ -114,6 +114,42 @@ def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
     }
 
 
+def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
+    """Event-timed bsa_backward calls (one call = row-term prep, transposed mask,
+    operand transposes, the dQ kernel and the dK/dV kernel) on the bench's mask, with a
+    seeded N(0,1) dout.  Executed FLOPs count the 7 tile products of 64 x 64 x D
+    (dQ: S, dP, dQ; dK/dV: S, dP, dV, dK) per kept tile; the dQ kernel's second
+    (low-part) dZ product is extra work on top."""
+    import torch
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    vt = bsa.prepare_v(v, g)
+    o, lse = bsa.attend(q, k, vt, mask, g, workspace=fwd_ws, out=o, return_lse=True)
+    del vt
+    gen = torch.Generator(device=q.device)
+    gen.manual_seed(1234)
+    dout = torch.randn(q.shape, generator=gen, device=q.device, dtype=torch.float32).to(q.dtype)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    prob = bsa.make_problem(q, g)
+    ws = torch.empty(max(bsa.backward_workspace_bytes(prob), 256), dtype=torch.uint8, device=q.device)
+    for _ in range(max(1, warmup)):
+        bsa.backward(q, k, v, mask, g, o, lse, dout, workspace=ws, out=grads)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        bsa.backward(q, k, v, mask, g, o, lse, dout, workspace=ws, out=grads)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    D = q.shape[-1]
+    flops = 7.0 * 2 * g.block * g.block * D * mask.nnz()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_call": round(ms, 4), "executed_tflop": round(flops / 1e12, 3),
+            "executed_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "dout": "seeded N(0,1), bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,12 +159,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also print per-stage details on stderr")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (dq, dk, dv) on the same mask after the forward steps")
     ap.add_argument("--sip-seed", type=int, default=None,
                     help="build the mask by SIP sampling with this Philox seed instead of the CDF cut")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path shards by (batch, head) "
-                                   "without communication, and no multi-GPU run is part of this build",
+                                   "without communication, so a multi-GPU figure is N independent copies of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -246,6 +284,8 @@ def main():
         "executed_tflop": round(exec_flops / 1e12, 3),
         "input_gen_s": round(t_gen, 1),
     }
+    if args.backward:
+        line["backward"] = time_backward(bsa, q, k, v, mask, g, fwd_ws, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         rp = mask.row_ptr.cpu().numpy().astype(np.int64)
         ci = mask.col_idx[:nnz].cpu().numpy()

@@ -96,6 +96,13 @@ def query_sizes(prob: _lib.Problem) -> dict:
     return {"rows": rows.value, "max_nnz": max_nnz.value, "mask_ws": mws.value, "fwd_ws": fws.value}
 
 
+def backward_workspace_bytes(prob: _lib.Problem) -> int:
+    """Bytes of device workspace bsa_backward needs for this problem."""
+    nbytes = ctypes.c_int64()
+    check(lib().bsa_query_backward_ws(ctypes.byref(prob), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes or ws.data_ptr() % 256:
@@ -267,16 +274,19 @@ def attention(q, k, v, grid: VideoGrid, thr: float, window=None, layout: str = "
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
              o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, layout: str = "original",
-             workspace: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of sum(o * dout) for forward(q, k, v, mask) with its o and lse."""
+             workspace: Optional[torch.Tensor] = None, out=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for forward(q, k, v, mask) with its o and lse.
+    `out` = (dq, dk, dv) tensors shaped like q to write into (else new ones)."""
     _check_qkv(q, k, v, o, dout)
     if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
         raise ValueError("lse must be float32 [batch, heads, L] as forward(return_lse=True) gives it")
     prob = make_problem(q, grid, layout)
-    nbytes = ctypes.c_int64()
-    check(lib().bsa_query_backward_ws(ctypes.byref(prob), ctypes.byref(nbytes)))
-    ws = _workspace(nbytes.value, q.device, workspace)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(backward_workspace_bytes(prob), q.device, workspace)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _check_qkv(q, dq, dk, dv)
     csr = mask.as_struct()
     check(lib().bsa_backward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
                              o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
