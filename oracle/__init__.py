@@ -25,6 +25,11 @@ unbiasedness.  `orders.py` adds the tile-major (TRA page) and 3D Hilbert
 (DFSAttn page) token orders, pinned in tests/test_oracle_orders_pins.py by
 bijection, equality with the fractal order for one-frame tiles, cube-shaped
 blocks and the unit-step walk of the Hilbert curve over a full 2^b cube.
+`groups.py` adds the fine-grained selection of 4-token key groups gathered into
+full tiles (AB-Attention page, third resource), pinned in
+tests/test_oracle_groups_pins.py by its exact reduction to the block path when
+a group is a whole block, by block CSRs expanded to groups, by torch float64
+attention with a token-level mask, and by the linearity of group means.
 No function is "parity unpinned".
 """
 from .nabla import (
