@@ -19,7 +19,12 @@ BSA_ORDER_FRACTAL, BSA_ORDER_TILE_MAJOR, BSA_ORDER_HILBERT = 0, 1, 2
 # every symbol declared in include/bsa.h
 EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
             "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_attend",
-            "bsa_query_backward_ws", "bsa_backward", "bsa_status_str", "bsa_last_error", "bsa_version"]
+            "bsa_query_backward_ws", "bsa_backward", "bsa_query_group_sizes", "bsa_build_group_mask",
+            "bsa_forward_groups", "bsa_prepare_v_groups", "bsa_attend_groups", "bsa_status_str", "bsa_last_error",
+            "bsa_version"]
+
+
+KEY_GROUP = 4   # BSA_KEY_GROUP
 
 
 class Problem(ctypes.Structure):
@@ -71,6 +76,11 @@ def lib():
     l.bsa_attend.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_query_backward_ws.argtypes = [P(Problem), P(i64)]
     l.bsa_backward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, vp, i64, vp]
+    l.bsa_query_group_sizes.argtypes = [P(Problem), ctypes.c_int, P(i64), P(i64), P(i64)]
+    l.bsa_build_group_mask.argtypes = [P(Problem), ctypes.c_int, P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
+    l.bsa_forward_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
+    l.bsa_prepare_v_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp]
+    l.bsa_attend_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_status_str.argtypes = [ctypes.c_int]
     l.bsa_status_str.restype = ctypes.c_char_p
     l.bsa_last_error.argtypes = []

@@ -292,3 +292,91 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask,
                              o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                              dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+# ---- 4-token key groups (gathered into 64-key tiles by the kernel) ----------
+KEY_GROUP = _lib.KEY_GROUP
+
+
+def query_group_sizes(prob: _lib.Problem) -> dict:
+    max_nnz, mws, fws = (ctypes.c_int64() for _ in range(3))
+    check(lib().bsa_query_group_sizes(ctypes.byref(prob), KEY_GROUP, ctypes.byref(max_nnz), ctypes.byref(mws),
+                                      ctypes.byref(fws)))
+    return {"max_nnz": max_nnz.value, "mask_ws": mws.value, "fwd_ws": fws.value}
+
+
+def build_group_mask(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, thr: float,
+                     window: Optional[Tuple[int, int, int]] = None, layout: str = "original",
+                     workspace: Optional[torch.Tensor] = None) -> BlockMask:
+    """Key-group mask: the reduced map of 64-token query blocks against 4-token key
+    groups, CDF cut at 1-thr (-> union with the groups of +-window tiles) -> CSR of
+    group ids (mask.S = L/4 columns per row)."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    rows = query_sizes(prob)["rows"]
+    sz = query_group_sizes(prob)
+    dev = q.device
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(sz["max_nnz"], dtype=torch.int32, device=dev)
+    nnz = torch.empty(1, dtype=torch.int32, device=dev)
+    mask = BlockMask(row_ptr, col_idx, nnz, rows, grid.L // KEY_GROUP)
+    ws = _workspace(sz["mask_ws"], dev, workspace)
+    wt, wh, ww = window if window is not None else (-1, -1, -1)
+    mp = _lib.MaskParams(float(thr), wt, wh, ww, _lib.BSA_MASK_CDF, 0)
+    csr = mask.as_struct()
+    check(lib().bsa_build_group_mask(ctypes.byref(prob), KEY_GROUP, ctypes.byref(mp), q.data_ptr(), k.data_ptr(),
+                                     ctypes.byref(csr), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return mask
+
+
+def prepare_v_groups(v: torch.Tensor, grid: VideoGrid, layout: str = "original") -> torch.Tensor:
+    """bf16 only: V as [batch, heads, L/4, D, 4] (each 4-token group channel-major), flat."""
+    _check_qkv(v)
+    prob = make_problem(v, grid, layout)
+    vg = torch.empty(v.numel(), dtype=v.dtype, device=v.device)
+    check(lib().bsa_prepare_v_groups(ctypes.byref(prob), KEY_GROUP, v.data_ptr(), vg.data_ptr(), _stream(v.device)))
+    return vg
+
+
+def _check_group_mask(mask: BlockMask, prob: _lib.Problem, grid: VideoGrid):
+    rows = query_sizes(prob)["rows"]
+    if mask.rows != rows or mask.S != grid.L // KEY_GROUP:
+        raise ValueError(f"group mask has {mask.rows} rows of {mask.S} columns, the problem needs "
+                         f"{rows} rows of {grid.L // KEY_GROUP}")
+    if mask.shift is not None:
+        raise ValueError("group masks carry no logit shifts")
+
+
+def attend_groups(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+                  layout: str = "original", return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None):
+    """The gathered-group attention kernel alone: `vp` = prepare_v_groups(v) for bf16, v for float32."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    _check_group_mask(mask, prob, grid)
+    if vp.numel() != q.numel() or vp.dtype != q.dtype or not vp.is_contiguous():
+        raise ValueError("vp must be a contiguous tensor with q's dtype and size")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(256, q.device, workspace)
+    csr = mask.as_struct()
+    check(lib().bsa_attend_groups(ctypes.byref(prob), KEY_GROUP, q.data_ptr(), k.data_ptr(), vp.data_ptr(),
+                                  ctypes.byref(csr), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                  ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def forward_groups(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+                   layout: str = "original", return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Attention of every query block over the tokens of its kept 4-token key groups."""
+    _check_qkv(q, k, v)
+    prob = make_problem(q, grid, layout)
+    _check_group_mask(mask, prob, grid)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(query_group_sizes(prob)["fwd_ws"], q.device, workspace)
+    csr = mask.as_struct()
+    check(lib().bsa_forward_groups(ctypes.byref(prob), KEY_GROUP, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   ctypes.byref(csr), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                   ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return (o, lse) if return_lse else o

@@ -20,8 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "bwd.hip",
-           "validate.cpp", "order.cpp"]
+SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "group_mask.hip", "attn_bf16.hip", "attn_f32.hip",
+           "attn_groups.hip", "bwd.hip", "validate.cpp", "order.cpp"]
 
 
 def hipcc() -> str:
@@ -40,7 +40,8 @@ def _flags():
 # per-file extras: the attention and mask kernels never see NaNs in their max/min
 # reductions (finite inputs), which lets the compiler drop the NaN-quieting
 # v_max x,x before every fmax
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"], "mask.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"], "mask.hip": ["-fno-honor-nans"], "group_mask.hip": ["-fno-honor-nans"],
+         "attn_groups.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

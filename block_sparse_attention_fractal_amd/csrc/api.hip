@@ -1,5 +1,6 @@
 // libbsa entry points: host-side validation, workspace carving and launches.
 // Declarations and contracts: include/bsa.h.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -56,7 +57,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 200; }
+int bsa_version(void) { return 300; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -330,6 +331,157 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
     vp = vt;
   }
   return enqueue_attend(g, q, k, vp, mask, o, lse, base, stream);
+}
+
+// ---- 4-token key groups --------------------------------------------------
+static int group_geom(const bsa_problem* p, int group, Geom* g) {
+  int st = geom_or_fail(p, g);
+  if (st != BSA_OK) return st;
+  std::string msg;
+  st = check_group(*g, group, &msg);
+  if (st != BSA_OK) return fail(st, msg);
+  return BSA_OK;
+}
+
+int bsa_query_group_sizes(const bsa_problem* p, int group, int64_t* max_nnz, int64_t* mask_ws, int64_t* fwd_ws) {
+  Geom g;
+  int st = group_geom(p, group, &g);
+  if (st != BSA_OK) return st;
+  if (max_nnz) *max_nnz = g.rows * (g.L / BSA_KEY_GROUP);
+  if (mask_ws) *mask_ws = grp_mask_ws_layout(g).total;
+  if (fwd_ws) *fwd_ws = grp_fwd_ws_layout(g).total;
+  return BSA_OK;
+}
+
+int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params* mp, const void* q, const void* k,
+                         const bsa_csr* out, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = group_geom(p, group, &g);
+  if (st != BSA_OK) return st;
+  std::string msg;
+  st = check_mask_params(g, mp, &msg);
+  if (st != BSA_OK) return fail(st, msg);
+  if (mp->mode != BSA_MASK_CDF) return fail(BSA_ERR_UNSUPPORTED, "bsa_build_group_mask: only BSA_MASK_CDF");
+  const int64_t SG = g.L / BSA_KEY_GROUP;
+  if (SG > group_select_max_groups())
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_build_group_mask: L/4 = " + std::to_string(SG) + " groups per head exceeds " +
+                                         std::to_string(group_select_max_groups()));
+  if (!q || !k || !out || !out->row_ptr || !out->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_build_group_mask: null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out->row_ptr, 4) || !aligned(out->col_idx, 4))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_build_group_mask: misaligned pointer");
+  if (out->capacity < g.rows * SG)
+    return fail(BSA_ERR_CAPACITY, "bsa_build_group_mask: col_idx capacity " + std::to_string(out->capacity) +
+                                      " < batch*heads*S*(L/4) = " + std::to_string(g.rows * SG));
+  const GrpMaskWs w = grp_mask_ws_layout(g);
+  if (!ws || ws_bytes < w.total)
+    return fail(BSA_ERR_WORKSPACE, "bsa_build_group_mask: workspace needs " + std::to_string(w.total) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, "bsa_build_group_mask: workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  double* qp = reinterpret_cast<double*>(base + w.qp);
+  double* kg = reinterpret_cast<double*>(base + w.kg);
+  double* z = reinterpret_cast<double*>(base + w.z);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
+  const bool win = mp->win_t >= 0;
+  // candidates: groups within lambda of the row's max logit (as in the block cut)
+  const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)SG) - std::log(mp->thr) : 0.0;
+  const int wt = win ? mp->win_t : -1, wh = win ? mp->win_h : -1, ww = win ? mp->win_w : -1;
+  // query-block means from the block pooling kernel (its key output lands in kg
+  // and is overwritten by the group means right after)
+  hipError_t e = launch_pool(g, q, k, qp, kg, stream);
+  if (e == hipSuccess) e = launch_pool_groups(g, k, kg, stream);
+  const int64_t bh = (int64_t)g.B * g.nh;
+  for (int64_t h0 = 0; h0 < bh && e == hipSuccess; h0 += w.chunk_heads) {
+    const int64_t nh = std::min<int64_t>(w.chunk_heads, bh - h0);
+    e = launch_logits(g, qp, kg, z, (int)SG, h0, nh, stream);
+    if (e == hipSuccess)
+      e = launch_group_select(g, z, h0 * g.S, nh * g.S, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
+  if (e == hipSuccess) {
+    Geom gg = g;
+    gg.S = (int32_t)SG;   // compaction walks L/4 columns per row (rows unchanged)
+    e = launch_compact(gg, bitmap, w.words, out->row_ptr, out->col_idx, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "bsa_build_group_mask launch");
+  return BSA_OK;
+}
+
+static int check_group_attend(const bsa_problem* p, int group, Geom* g, const void* q, const void* k, const void* v,
+                              const bsa_csr* mask, const void* o, const float* lse, void* ws, int64_t ws_bytes,
+                              bool whole, const char* who) {
+  int st = group_geom(p, group, g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !o || !mask || !mask->row_ptr || !mask->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": null pointer");
+  if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, std::string(who) + ": group masks carry no logit shifts");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": misaligned pointer");
+  const GrpFwdWs w = grp_fwd_ws_layout(*g);
+  const int64_t need = whole ? w.total : w.vg;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(need) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace must be 256-byte aligned");
+  return BSA_OK;
+}
+
+static int enqueue_attend_groups(const Geom& g, const void* q, const void* k, const void* vp, const bsa_csr* mask,
+                                 void* o, float* lse, char* ws, hipStream_t stream) {
+  const GrpFwdWs w = grp_fwd_ws_layout(g);
+  hipError_t e;
+  if (g.dtype == BSA_BF16) {
+    int ncu = 0;
+    const int st = current_cu_count(&ncu);
+    if (st != BSA_OK) return st;
+    int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
+    e = launch_zero_i32(counter, 8, stream);
+    if (e == hipSuccess)
+      e = launch_attn_groups_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter, ncu, stream);
+  } else {
+    e = launch_attn_groups_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
+                               mask->col_idx, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "group attention launch");
+  return BSA_OK;
+}
+
+int bsa_prepare_v_groups(const bsa_problem* p, int group, const void* v, void* vg, hipStream_t stream) {
+  Geom g;
+  int st = group_geom(p, group, &g);
+  if (st != BSA_OK) return st;
+  if (g.dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_prepare_v_groups: only bf16 uses a prepared V");
+  if (!v || !vg) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v_groups: null pointer");
+  if (!aligned(v, 16) || !aligned(vg, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v_groups: misaligned pointer");
+  if (v == vg) return fail(BSA_ERR_INVALID_ARG, "bsa_prepare_v_groups: v and vg must not alias");
+  hipError_t e = launch_prep_vg(g, v, vg, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare_v_groups launch");
+  return BSA_OK;
+}
+
+int bsa_attend_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* vp,
+                      const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = check_group_attend(p, group, &g, q, k, vp, mask, o, lse, ws, ws_bytes, false, "bsa_attend_groups");
+  if (st != BSA_OK) return st;
+  return enqueue_attend_groups(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream);
+}
+
+int bsa_forward_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* v,
+                       const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = check_group_attend(p, group, &g, q, k, v, mask, o, lse, ws, ws_bytes, true, "bsa_forward_groups");
+  if (st != BSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  const void* vp = v;
+  if (g.dtype == BSA_BF16) {
+    void* vg = base + grp_fwd_ws_layout(g).vg;
+    hipError_t e = launch_prep_vg(g, v, vg, stream);
+    if (e != hipSuccess) return hip_fail(e, "prepare_v_groups launch");
+    vp = vg;
+  }
+  return enqueue_attend_groups(g, q, k, vp, mask, o, lse, base, stream);
 }
 
 }  // extern "C"

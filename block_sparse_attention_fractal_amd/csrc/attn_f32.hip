@@ -14,7 +14,10 @@
 
 namespace bsa {
 
-template <int D>
+// kGroups: col_idx lists 4-token key groups (AB-Attention page, "Los tres recursos
+// de AB-Attention", third resource); every 16 entries form one 64-key tile and the
+// padding keys of a row's last tile are masked.
+template <int D, bool kGroups>
 __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                        const float* __restrict__ v, float* __restrict__ o,
                                                        float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
@@ -39,15 +42,25 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__
   for (int d = 0; d < DS; ++d) oacc[d] = 0.0;
   double m = -INFINITY, l = 0.0;
   const int beg = row_ptr[r], end = row_ptr[r + 1];
-  for (int it = beg; it < end; ++it) {
-    const int j = min(max(col_idx[it], 0), g.S - 1);
-    const double sh = shift ? (double)shift[it] : 0.0;   // the entry's logit shift, if any
+  const int gpb = g.N / 4;   // groups per block
+  for (int it = beg; it < end; it += kGroups ? 16 : 1) {
+    const int j = kGroups ? 0 : min(max(col_idx[it], 0), g.S - 1);
+    const double sh = !kGroups && shift ? (double)shift[it] : 0.0;   // the entry's logit shift, if any
     __syncthreads();
     for (int e = tid; e < 64 * D; e += 256) {
       const int row = e / D, d = e % D;
-      const size_t off = (size_t)block_token_row(g, j, row) * D + d;
-      Ks[row][d] = kh[off];
-      Vs[row][d] = vh[off];
+      int tok;
+      bool valid = true;
+      if (kGroups) {
+        valid = it + (row >> 2) < end;
+        const int gid = valid ? min(max(col_idx[it + (row >> 2)], 0), g.L / 4 - 1) : 0;
+        tok = block_token_row(g, gid / gpb, (gid % gpb) * 4 + (row & 3));
+      } else {
+        tok = block_token_row(g, j, row);
+      }
+      const size_t off = (size_t)tok * D + d;
+      Ks[row][d] = valid ? kh[off] : 0.f;
+      Vs[row][d] = valid ? vh[off] : 0.f;
     }
     __syncthreads();
     double s[16];
@@ -58,7 +71,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__
       double acc = 0.0;
 #pragma unroll 4
       for (int d = 0; d < D; ++d) acc = __fma_rn((double)Qs[qi][d], (double)Ks[kk][d], acc);
-      s[c] = acc * scale + sh;
+      s[c] = kGroups && it + (kk >> 2) >= end ? -INFINITY : acc * scale + sh;
       mt = fmax(mt, s[c]);
     }
     mt = fmax(mt, __shfl_xor(mt, 1));
@@ -95,9 +108,20 @@ hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const 
                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s) {
   const double scale = 1.0 / sqrt((double)g.D);
   if (g.D == 64)
-    attn_f32_kernel<64><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
+    attn_f32_kernel<64, false><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
   else
-    attn_f32_kernel<128><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
+    attn_f32_kernel<128, false><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, shift, g, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_groups_f32(const Geom& g, const float* q, const float* k, const float* v, float* o,
+                                  float* lse, const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s) {
+  const double scale = 1.0 / sqrt((double)g.D);
+  if (g.D == 64)
+    attn_f32_kernel<64, true><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, nullptr, g, scale);
+  else
+    attn_f32_kernel<128, true><<<(unsigned)g.rows, 256, 0, s>>>(q, k, v, o, lse, row_ptr, col_idx, nullptr, g,
+                                                                scale);
   return hipGetLastError();
 }
 

@@ -1,0 +1,370 @@
+// Attention over gathered 4-token key groups, bf16 inputs, head_dim 128, gfx950 MFMA.
+//
+// The mask lists, for every query block of 64 tokens, the kept key GROUPS of 4
+// consecutive fractal-order tokens (AB-Attention page, news.hamidun.com/es/news/14960,
+// "Los tres recursos de AB-Attention", third resource: small key/value blocks
+// gathered by index into full matrix-core tiles, without reordering tokens).
+// Every 16 kept groups of a row (ascending) form one 64-key tile; the last tile of
+// a row is padded and its padding keys take no part in the softmax.
+//
+// Work decomposition
+//   * a work item is ONE query block (tiles of different rows rarely coincide,
+//     so there is nothing to share between neighbouring rows); 256-thread
+//     workgroups, wave w owns queries 32*(w&1).. and the 32 keys of slots
+//     8*(w>>1).. of every tile; the two waves of a query range merge their
+//     online-softmax states at the end;
+//   * persistent grid, two workgroups per CU, XCD-partitioned item ranges
+//     balanced by cumulative kept groups (as in the block kernel);
+//   * a K tile slot is 4 key rows (1 KB) loaded with ONE direct-to-LDS 16-byte
+//     buffer load per wave (lane -> row lane/16, chunk lane%16, swizzled
+//     chunk c ^ (row & 15)); a V slot is the group's 128 x 4 transposed block
+//     of the prepared V (1 KB, contiguous), also one load;
+//   * S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16; the V^T
+//     operand of a lane is two 8-byte LDS reads (4 keys of one channel from each
+//     of two groups), in exactly the key order P leaves the S^T accumulator.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace bsa {
+namespace grp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kD = 128;
+constexpr int kStage = 32768;     // 16 K slots (16 KB) + 16 V slots (16 KB)
+constexpr int kVOff = 16384;
+constexpr float kLazy = 8.0f;
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* vg;     // [B*nh, L/4, D, 4]
+  uint16_t* o;
+  float* lse;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;  // group ids
+  int32_t* counters;
+  Geom g;
+  float c_log2;
+  uint32_t magic_wp, magic_hp;
+  int32_t groups;          // L / 4 per head
+};
+
+__device__ __forceinline__ int k_lds(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic) {
+  return (uint32_t)(((uint64_t)n * magic) >> 32);
+}
+
+// First row (tensor layout) of block j: fractal order -> 64 j; original order ->
+// the patch's top-left token (block ids and patch counts < 2^16: multiply-high).
+__device__ __forceinline__ int block_base_row(const Args& a, int j) {
+  const Geom& g = a.g;
+  if (g.layout == 1) return j * 64;
+  const int rest = (int)div_magic((uint32_t)j, a.magic_wp);
+  const int px = j - rest * g.Wp;
+  const int t = (int)div_magic((uint32_t)rest, a.magic_hp);
+  const int py = rest - t * g.Hp;
+  return (t * g.H + py * 8) * g.W + px * 8;
+}
+// First row of group gid: tokens 4(gid % 16) .. +3 of block gid / 16, which sit
+// in one patch row (P = 8), so the group's 4 rows are consecutive in memory.
+__device__ __forceinline__ int group_base_row(const Args& a, int gid) {
+  if (a.g.layout == 1) return gid * 4;
+  return block_base_row(a, gid >> 4) + ((gid & 15) >> 1) * a.g.W + (gid & 1) * 4;
+}
+
+__global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ int s_item;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wq = wave & 1;       // which 32 queries
+  const int kh = wave >> 1;      // which 8 slots (32 keys) of every tile
+  const Geom g = a.g;
+  const float c_log2 = a.c_log2;
+  const int rs = g.layout == 1 ? 8 : g.W;
+
+  // per-lane parts of this wave's four slot loads (slots 4*wave + u)
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int slot = 4 * wave + u;
+    const int row = 4 * slot + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    koff[u] = (lane >> 4) * kD * 2 + lc * 16;
+  }
+
+  const int xcd = blockIdx.x & 7;
+  const int64_t items = g.rows;
+  const int64_t total = a.row_ptr[items];
+  int64_t lo_t, hi_t;
+  {
+    auto first_item_with_cost = [&](int64_t target) {
+      int64_t lo = 0, hi = items;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (a.row_ptr[mid + 1] > target) hi = mid; else lo = mid + 1;
+      }
+      return lo;
+    };
+    lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
+    hi_t = xcd == 7 ? items : first_item_with_cost(total * (xcd + 1) / 8);
+  }
+
+  for (;;) {
+    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    __syncthreads();
+    const int64_t r = __builtin_amdgcn_readfirstlane(s_item);
+    if (r >= hi_t) break;
+    const int64_t bh = r / g.S;
+    const int i = (int)(r - bh * g.S);
+    const int p0 = a.row_ptr[r], e0 = a.row_ptr[r + 1];
+    const int ng = e0 - p0;
+    const int ntiles = (ng + 15) >> 4;
+
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.k + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.vg + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
+
+    // 64 group ids (4 tiles) per window, one per lane; entries past the row's end
+    // repeat its last group (their keys are masked)
+    int win_c = -1, win = 0;
+    auto issue = [&](int t, auto stage_c) {
+      constexpr int stage = decltype(stage_c)::value;
+      if ((t >> 2) != win_c) {
+        win_c = t >> 2;
+        win = a.col_idx[min(p0 + 64 * win_c + lane, e0 - 1)];
+      }
+      uint8_t* st = smem + stage * kStage;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int slot = 4 * wave + u;
+        const int gid = min(max(__builtin_amdgcn_readlane(win, 16 * (t & 3) + slot), 0), a.groups - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + slot * 1024), 16, koff[u],
+                                                 group_base_row(a, gid) * kD * 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kVOff + slot * 1024), 16, lane * 16,
+                                                 gid * 1024, 0, 0);
+      }
+    };
+
+    bf16x8 qreg[8];
+    {
+      const int qtok = block_base_row(a, i) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
+      const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qreg[s] = *(const bf16x8*)(qrow + 16 * s);
+    }
+    f32x16 oacc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+    auto step = [&](int t, auto stage_c) {
+      constexpr int stage = decltype(stage_c)::value;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, stage ^ 1>{});
+      const int nvalid = min(16, ng - 16 * t);
+      if (8 * kh < nvalid) {
+        const uint8_t* st = smem + stage * kStage;
+        f32x16 sacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 ak = *(const bf16x8*)(st + k_lds(32 * kh + l32, 2 * s + h));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc, 0, 0, 0);
+        }
+        // register e holds key 8(e/4) + 4h + e%4 of this wave's 32, i.e. slot 8kh + 2(e/4) + h
+        if (nvalid < 16) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (8 * kh + 2 * (e >> 2) + h >= nvalid) sacc[e] = -INFINITY;
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+        mx = pair_max(mx) * c_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          m_ref = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
+        }
+        bf16x8 pbv[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -m_ref));
+          l_run += p;
+          pbv[e >> 3][e & 7] = (__bf16)p;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int sa = kVOff + (8 * kh + 4 * s + h) * 1024;   // keys 16s + 4h + 0..3
+          const int sb = sa + 2 * 1024;                          // keys 16s + 8 + 4h + 0..3
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int d = 32 * u + l32;
+            const uint2 lo = *(const uint2*)(st + sa + d * 8);
+            const uint2 hi = *(const uint2*)(st + sb + d * 8);
+            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            const bf16x8 av = __builtin_bit_cast(bf16x8, w);
+            oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+          }
+        }
+      }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    // merge the two key halves of each query range, then normalise and store
+    __syncthreads();
+    float* xo = (float*)smem + wq * (64 * 64);               // partner accumulators, [reg][lane]
+    float2* xm = (float2*)(smem + 32768) + wq * 64;          // partner (m_ref, l_run)
+    if (kh == 1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xo[(16 * u + e) * 64 + lane] = oacc[u][e];
+      xm[lane] = make_float2(m_ref, l_run);
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float2 pm = xm[lane];
+      const float m_tot = fmaxf(m_ref, pm.x);
+      const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_tot);
+      const float a1 = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - m_tot);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[u][e] = a0 * oacc[u][e] + a1 * xo[(16 * u + e) * 64 + lane];
+      l_run = pair_sum(a0 * l_run + a1 * pm.y);
+      m_ref = m_tot;
+    }
+    __syncthreads();
+    const int qrow = 32 * wq + l32;
+    if (kh == 0) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;     // an empty row yields zeros
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int unit = 8 * u + 2 * rq + h;
+          uint2 w;
+          w.x = pack_bf16x2(oacc[u][4 * rq + 0] * inv, oacc[u][4 * rq + 1] * inv);
+          w.y = pack_bf16x2(oacc[u][4 * rq + 2] * inv, oacc[u][4 * rq + 3] * inv);
+          *(uint2*)(smem + qrow * 256 + ((unit ^ (qrow & 31)) << 3)) = w;
+        }
+      }
+      if (a.lse && h == 0) {
+        const int tok = block_base_row(a, i) + (qrow >> 3) * rs + (qrow & 7);
+        a.lse[(size_t)bh * g.L + tok] = (m_ref + log2f(l_run)) * 0.69314718055994531f;
+      }
+    }
+    __syncthreads();
+    {
+      const int lchunk = tid & 15;
+      const int base = block_base_row(a, i);
+      uint16_t* oh = a.o + (size_t)bh * g.L * kD;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = (tid >> 4) + 16 * u;
+        const uint2 lo = *(const uint2*)(smem + row * 256 + (((2 * lchunk) ^ (row & 31)) << 3));
+        const uint2 hi = *(const uint2*)(smem + row * 256 + (((2 * lchunk + 1) ^ (row & 31)) << 3));
+        const int tok = base + (row >> 3) * rs + (row & 7);
+        *(uint4*)(oh + (size_t)tok * kD + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+  }
+}
+
+// V -> [B*nh, L/4, D, 4]: each 4-token group transposed to channel-major (4 keys
+// of one channel are 8 contiguous bytes).  One thread per (group, 8 channels).
+__global__ void __launch_bounds__(256) prep_vg_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vg,
+                                                      Geom g) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (bh, group, chunk of 8 channels)
+  const int chunks = g.D / 8;
+  const int64_t ng = (int64_t)g.B * g.nh * (g.L / 4);
+  if (idx >= ng * chunks) return;
+  const int c = (int)(idx % chunks);
+  const int64_t gg = idx / chunks;
+  const int64_t bh = gg / (g.L / 4);
+  const int gid = (int)(gg - bh * (g.L / 4));
+  const int blk = gid / (g.N / 4), m0 = (gid % (g.N / 4)) * 4;
+  const int row0 = block_token_row(g, blk, m0);        // the group's 4 rows are consecutive
+  const uint16_t* src = v + ((size_t)bh * g.L + row0) * g.D + 8 * c;
+  uint4 rows[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) rows[t] = *(const uint4*)(src + (size_t)t * g.D);
+  // channel d of token t is 16-bit half (d & 1) of word d / 2 of rows[t]
+  auto half = [&](int t, int d) -> uint32_t {
+    const uint32_t w = ((const uint32_t*)&rows[t])[d >> 1];
+    return (d & 1) ? (w >> 16) : (w & 0xffffu);
+  };
+  uint4* dst = (uint4*)(vg + (gg * g.D + 8 * c) * 4);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {      // channels 2x and 2x+1: keys 0-3 of each
+    const int d0 = 2 * x, d1 = 2 * x + 1;
+    dst[x] = make_uint4(half(0, d0) | (half(1, d0) << 16), half(2, d0) | (half(3, d0) << 16),
+                        half(0, d1) | (half(1, d1) << 16), half(2, d1) | (half(3, d1) << 16));
+  }
+}
+
+}  // namespace grp
+
+hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s) {
+  const int64_t n = (int64_t)g.B * g.nh * (g.L / 4) * (g.D / 8);
+  grp::prep_vg_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vg, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, const void* vg, void* o, float* lse,
+                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
+                                   hipStream_t s) {
+  grp::Args a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.vg = (const uint16_t*)vg;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.counters = counters;
+  a.g = g;
+  a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
+  a.magic_wp = (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
+  a.groups = g.L / 4;
+  const int grid = ((num_cu * 2 + 7) / 8) * 8;
+  grp::attn_groups_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

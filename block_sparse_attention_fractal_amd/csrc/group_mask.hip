@@ -1,0 +1,412 @@
+// Key-group mask (AB-Attention page, news.hamidun.com/es/news/14960, "Los tres
+// recursos de AB-Attention", third resource: 4-token key/value blocks), selected
+// with the NABLA reduced map and CDF cut taken at group granularity (NABLA page,
+// gist.science/es/paper/2507.13546, Metodologia item 2, "Atencion Reducida" and
+// "Umbralizacion CDF"; item 3 for the window union).
+//
+//   * pool_groups_kernel: float64 means of 4 consecutive fractal-order keys;
+//   * the logits reuse the float64 block-logit GEMM with L/4 key columns, run
+//     over a chunk of heads at a time so the workspace stays bounded;
+//   * group_select_kernel: the CDF cut of one row per 256-thread workgroup.
+//     A row has L/4 entries (31 680 at 33 x 48 x 80 tokens), too many to hold
+//     in registers as the block select does, so the row is read twice from
+//     the logits (max, then the float32 offsets z - max into LDS, 4 B per
+//     entry) and every radix pass runs over LDS.  The numerics are those of the
+//     block select: the ORDER is decided on the float64 logits, the masses are
+//     float32 exponentials in fixed point (2^-30 of the row max) summed exactly,
+//     the 24-bit monotone key is radix-selected 8 bits per pass until the
+//     crossing bin holds <= 256 entries, which are then ranked exactly on their
+//     float64 logits (ties by index); more than 256 entries with one 24-bit key
+//     fall back to passes over the exact 64-bit order keys, then index order.
+#include <float.h>
+
+#include "kernels.h"
+#include "mask_util.h"
+
+namespace bsa {
+namespace gmask {
+
+constexpr int kMaxSG = 32768;     // groups per head the LDS row buffer holds
+
+// float64 means of every 4 consecutive fractal-order rows of k -> kg [B*nh, L/4, D].
+// Thread = (group, 4 channels); the group's 4 rows are consecutive in memory.
+template <typename T>
+__global__ void __launch_bounds__(256) pool_groups_kernel(const T* __restrict__ k, double* __restrict__ kg, Geom g) {
+  const int per = g.D / 4;                          // threads per group
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t SG = g.L / 4;
+  const int64_t ngroups = (int64_t)g.B * g.nh * SG;
+  if (idx >= ngroups * per) return;
+  const int c = (int)(idx % per);
+  const int64_t gg = idx / per;
+  const int64_t bh = gg / SG;
+  const int gid = (int)(gg - bh * SG);
+  const int blk = gid / (g.N / 4), m0 = (gid % (g.N / 4)) * 4;
+  const T* src = k + ((size_t)bh * g.L + block_token_row(g, blk, m0)) * g.D + 4 * c;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float x;
+      if constexpr (sizeof(T) == 2) {
+        x = __uint_as_float((uint32_t)((const uint16_t*)src)[(size_t)t * g.D + d] << 16);
+      } else {
+        x = ((const float*)src)[(size_t)t * g.D + d];
+      }
+      acc[d] += (double)x;                          // sums of 4 bf16/f32 values are exact in float64
+    }
+  }
+  double* dst = kg + (size_t)gg * g.D + 4 * c;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dst[d] = acc[d] * 0.25;
+}
+
+struct SelectSmem {
+  float dv[kMaxSG];                   // (float)(z - max) of candidates, -inf otherwise
+  uint32_t bm[kMaxSG / 32];           // kept bits of the row
+  uint32_t hc[256];                   // radix bins: counts
+  unsigned long long hm[256];         //             masses
+  uint32_t cj[256], cw[256];          // crossing entries: index, mass
+  unsigned long long ck[256];         //                   exact order key
+  unsigned long long red_u[4];
+  double red_d[4];
+  float red_f[4];
+  unsigned long long scan[4];
+  int found_bin;
+  uint32_t found_cnt, ncross;
+  unsigned long long found_above;
+};
+
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int d) {
+  const uint32_t lo = __shfl_up((uint32_t)v, d, 64), hi = __shfl_up((uint32_t)(v >> 32), d, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int d) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, d, 64), hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ double shfl_xor_f64(double v, int d) {
+  return __longlong_as_double((long long)shfl_xor_u64((unsigned long long)__double_as_longlong(v), d));
+}
+
+__global__ void __launch_bounds__(256) group_select_kernel(const double* __restrict__ z, int64_t row0, int SG,
+                                                           Geom g, double thr, double lambda, int win_t, int win_h,
+                                                           int win_w, uint32_t* __restrict__ bitmap,
+                                                           int32_t* __restrict__ counts, int words) {
+  __shared__ SelectSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t r = row0 + blockIdx.x;
+  const int i = (int)(r % g.S);
+  const double* zr = z + (int64_t)blockIdx.x * SG;
+  const int gpb = g.N / 4;
+  for (int x = tid; x < words; x += 256) sm.bm[x] = 0u;
+
+  // workgroup reductions (fixed tree order, deterministic)
+  auto sum_u64 = [&](unsigned long long v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v += shfl_xor_u64(v, d);
+    if (lane == 0) sm.red_u[wv] = v;
+    __syncthreads();
+    const unsigned long long t = sm.red_u[0] + sm.red_u[1] + sm.red_u[2] + sm.red_u[3];
+    __syncthreads();
+    return t;
+  };
+  auto max_u64 = [&](unsigned long long v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) { const unsigned long long o = shfl_xor_u64(v, d); v = o > v ? o : v; }
+    if (lane == 0) sm.red_u[wv] = v;
+    __syncthreads();
+    unsigned long long t = sm.red_u[0];
+    for (int x = 1; x < 4; ++x) t = sm.red_u[x] > t ? sm.red_u[x] : t;
+    __syncthreads();
+    return t;
+  };
+  auto min_u64 = [&](unsigned long long v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) { const unsigned long long o = shfl_xor_u64(v, d); v = o < v ? o : v; }
+    if (lane == 0) sm.red_u[wv] = v;
+    __syncthreads();
+    unsigned long long t = sm.red_u[0];
+    for (int x = 1; x < 4; ++x) t = sm.red_u[x] < t ? sm.red_u[x] : t;
+    __syncthreads();
+    return t;
+  };
+  auto max_f64 = [&](double v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v = fmax(v, shfl_xor_f64(v, d));
+    if (lane == 0) sm.red_d[wv] = v;
+    __syncthreads();
+    const double t = fmax(fmax(sm.red_d[0], sm.red_d[1]), fmax(sm.red_d[2], sm.red_d[3]));
+    __syncthreads();
+    return t;
+  };
+  auto min_f32 = [&](float v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v = fminf(v, __shfl_xor(v, d, 64));
+    if (lane == 0) sm.red_f[wv] = v;
+    __syncthreads();
+    const float t = fminf(fminf(sm.red_f[0], sm.red_f[1]), fminf(sm.red_f[2], sm.red_f[3]));
+    __syncthreads();
+    return t;
+  };
+  // inclusive prefix sum of one value per thread, thread order
+  auto incl_scan_u64 = [&](unsigned long long v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const unsigned long long o = shfl_up_u64(v, d);
+      if (lane >= d) v += o;
+    }
+    if (lane == 63) sm.scan[wv] = v;
+    __syncthreads();
+    unsigned long long base = 0;
+    for (int x = 0; x < wv; ++x) base += sm.scan[x];
+    __syncthreads();
+    return base + v;
+  };
+  auto set_bit = [&](int j) { atomicOr(&sm.bm[j >> 5], 1u << (j & 31)); };
+
+  if (thr == 0.0) {
+    for (int x = tid; x < words; x += 256) {
+      const int left = SG - 32 * x;
+      sm.bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    }
+  } else {
+    // pass 1 over the logits: row max; pass 2: candidates, masses, offsets into LDS
+    double m = -DBL_MAX;
+    for (int j = tid; j < SG; j += 256) m = fmax(m, zr[j]);
+    m = max_f64(m);
+    unsigned long long wsum = 0;
+    float dmin = 0.f;
+    for (int j = tid; j < SG; j += 256) {
+      const double d = zr[j] - m;
+      const float df = (float)d;
+      const float e = d >= -lambda ? __builtin_amdgcn_exp2f(df * 1.44269504088896341f) : 0.f;
+      const uint32_t w = (uint32_t)(e * 1073741824.0f);    // e <= 1: at most 2^30, exact
+      sm.dv[j] = w != 0u ? df : -INFINITY;
+      wsum += w;
+      if (w != 0u) dmin = fminf(dmin, df);
+    }
+    const unsigned long long total = sum_u64(wsum);     // (its barriers also publish dv)
+    dmin = min_f32(dmin);
+    const float tscale = dmin < 0.f ? 16777215.0f / (-dmin) : 0.f;
+    const double target = (1.0 - thr) * (double)total;   // keep while exclusive prefix < target
+    // mass and 24-bit key of entry j, recomputed from its offset exactly as above
+    auto mass_key = [&](int j, uint32_t& w, uint32_t& t) {
+      const float df = sm.dv[j];
+      if (df == -INFINITY) {
+        w = 0u;
+        t = 0u;
+        return;
+      }
+      const float e = __builtin_amdgcn_exp2f(df * 1.44269504088896341f);
+      w = (uint32_t)(e * 1073741824.0f);
+      t = (uint32_t)fminf((df - dmin) * tscale, 16777215.0f);
+    };
+    // one radix pass: (count, mass) histogram of bin(j) >= 0, then the bin in
+    // which the cumulative mass from the top (bin 255 first) reaches the target
+    auto crossing = [&](auto bin, unsigned long long above_in, int& b_out, unsigned long long& above_out,
+                        uint32_t& cnt_out) {
+      sm.hc[tid] = 0u;
+      sm.hm[tid] = 0ull;
+      if (tid == 0) sm.found_bin = -1;
+      __syncthreads();
+      for (int j = tid; j < SG; j += 256) {
+        uint32_t w;
+        const int b = bin(j, w);
+        if (b >= 0) {
+          atomicAdd(&sm.hc[b], 1u);
+          atomicAdd(&sm.hm[b], (unsigned long long)w);
+        }
+      }
+      __syncthreads();
+      const int b = 255 - tid;                           // thread order = bins from the top
+      const unsigned long long mb = sm.hm[b];
+      const unsigned long long incl = incl_scan_u64(mb);
+      const unsigned long long excl = incl - mb;
+      if (sm.hc[b] != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + incl)) {
+        sm.found_bin = b;
+        sm.found_above = above_in + excl;
+        sm.found_cnt = sm.hc[b];
+      }
+      __syncthreads();
+      b_out = sm.found_bin;
+      above_out = sm.found_above;
+      cnt_out = sm.found_cnt;
+      __syncthreads();                                   // bins and results are reused next pass
+      return b_out >= 0;
+    };
+
+    uint32_t tpre = 0;
+    int tsh = 24;
+    unsigned long long above = 0;
+    uint32_t cnt = 0;
+    bool reach = true;
+    while (tsh > 0) {
+      const int sh = tsh - 8;
+      const uint32_t pf = tpre;
+      const int tshc = tsh;
+      int b;
+      unsigned long long ab;
+      uint32_t cb;
+      if (!crossing(
+              [&](int j, uint32_t& w) {
+                uint32_t t;
+                mass_key(j, w, t);
+                return w != 0u && (t >> tshc) == pf ? (int)((t >> sh) & 255u) : -1;
+              },
+              above, b, ab, cb)) {
+        reach = false;                                   // only possible on the first pass
+        break;
+      }
+      tpre = (pf << 8) | (uint32_t)b;
+      tsh = sh;
+      above = ab;
+      cnt = cb;
+      if (cnt <= 256u) break;
+    }
+    auto in_bin = [&](int j, uint32_t& w) {
+      uint32_t t;
+      mass_key(j, w, t);
+      return w != 0u && (t >> tsh) == tpre;
+    };
+    if (!reach) {                                        // every candidate is kept
+      for (int j = tid; j < SG; j += 256)
+        if (sm.dv[j] != -INFINITY) set_bit(j);
+    } else {
+      for (int j = tid; j < SG; j += 256) {
+        uint32_t w, t;
+        mass_key(j, w, t);
+        if (w != 0u && (t >> tsh) > tpre) set_bit(j);
+      }
+      if (cnt <= 256u) {
+        // the crossing bin's entries, ranked exactly on their float64 logits
+        if (tid == 0) sm.ncross = 0u;
+        __syncthreads();
+        for (int j = tid; j < SG; j += 256) {
+          uint32_t w;
+          if (in_bin(j, w)) {
+            const uint32_t x = atomicAdd(&sm.ncross, 1u);
+            sm.cj[x] = (uint32_t)j;
+            sm.cw[x] = w;
+            sm.ck[x] = order_key(zr[j]);
+          }
+        }
+        __syncthreads();
+        const uint32_t n = sm.ncross;
+        if ((uint32_t)tid < n) {
+          const uint32_t my_j = sm.cj[tid];
+          const unsigned long long my_k = sm.ck[tid];
+          unsigned long long before = 0;
+          for (uint32_t y = 0; y < n; ++y) {
+            const unsigned long long ky = sm.ck[y];
+            if (ky > my_k || (ky == my_k && sm.cj[y] < my_j)) before += sm.cw[y];
+          }
+          if ((double)(above + before) < target) set_bit((int)my_j);
+        }
+      } else {
+        // more than 256 entries share one 24-bit key: exact 64-bit keys, then ties
+        unsigned long long kmax = 0, kmin = ~0ull;
+        for (int j = tid; j < SG; j += 256) {
+          uint32_t w;
+          if (in_bin(j, w)) {
+            const unsigned long long key = order_key(zr[j]);
+            kmax = key > kmax ? key : kmax;
+            kmin = key < kmin ? key : kmin;
+          }
+        }
+        kmax = max_u64(kmax);
+        kmin = min_u64(kmin);
+        const unsigned long long diff = kmax ^ kmin;
+        int shift = diff == 0 ? 0 : ((63 - __clzll(diff)) & ~7);
+        unsigned long long prefix = shift >= 56 ? 0ull : (kmax & (~0ull << (shift + 8)));
+        for (;;) {
+          const unsigned long long hi_mask = shift >= 56 ? 0ull : (~0ull << (shift + 8));
+          const int sh = shift;
+          const unsigned long long pf = prefix;
+          int b;
+          unsigned long long ab;
+          uint32_t cb;
+          // the crossing entry lies in this bin and shares the decided prefix,
+          // so a bin is always found
+          crossing(
+              [&](int j, uint32_t& w) {
+                if (!in_bin(j, w)) return -1;
+                const unsigned long long key = order_key(zr[j]);
+                return (key & hi_mask) == pf ? (int)((key >> sh) & 255u) : -1;
+              },
+              above, b, ab, cb);
+          prefix |= (unsigned long long)b << shift;
+          above = ab;
+          cnt = cb;
+          if (cnt <= 1u || shift == 0) break;
+          shift -= 8;
+        }
+        const unsigned long long hi_key = shift == 0 ? prefix : (prefix | ((1ull << shift) - 1));
+        uint32_t wt = 0;
+        for (int j = tid; j < SG; j += 256) {
+          uint32_t w;
+          if (in_bin(j, w)) {
+            const unsigned long long key = order_key(zr[j]);
+            if (key > hi_key || (cnt <= 1u && key >= prefix)) set_bit(j);
+            if (cnt > 1u && key == prefix) wt = w;
+          }
+        }
+        if (cnt > 1u) {
+          // exact ties at the cut: lowest indices first while the mass stays below
+          // the target; all tied entries have the same logit, hence the same mass
+          wt = (uint32_t)max_u64(wt);
+          unsigned long long acc = above;
+          for (int base = 0; base < SG; base += 256) {
+            const int j = base + tid;
+            bool tie = false;
+            if (j < SG) {
+              uint32_t w;
+              tie = in_bin(j, w) && order_key(zr[j]) == prefix;
+            }
+            const unsigned long long incl = incl_scan_u64(tie ? 1ull : 0ull);
+            if (tie && (double)(acc + (incl - 1) * wt) < target) set_bit(j);
+            acc += sum_u64(tie ? 1ull : 0ull) * wt;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (win_t >= 0)
+    for (int j = tid; j < SG; j += 256)
+      if (in_window(g, i, j / gpb, win_t, win_h, win_w)) set_bit(j);
+  __syncthreads();
+  unsigned long long pc = 0;
+  for (int x = tid; x < words; x += 256) {
+    const uint32_t v = sm.bm[x];
+    bitmap[r * words + x] = v;
+    pc += __popc(v);
+  }
+  pc = sum_u64(pc);
+  if (tid == 0) counts[r] = (int32_t)pc;
+}
+
+}  // namespace gmask
+
+hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStream_t s) {
+  const int64_t n = (int64_t)g.B * g.nh * (g.L / 4) * (g.D / 4);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (g.dtype == 1)
+    gmask::pool_groups_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)k, kg, g);
+  else
+    gmask::pool_groups_kernel<float><<<grid, 256, 0, s>>>((const float*)k, kg, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, double thr,
+                               double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+                               int words, hipStream_t s) {
+  gmask::group_select_kernel<<<(unsigned)nrows, 256, 0, s>>>(z, row0, g.L / 4, g, thr, lambda, win_t, win_h, win_w,
+                                                             bitmap, counts, words);
+  return hipGetLastError();
+}
+
+int group_select_max_groups() { return gmask::kMaxSG; }
+
+}  // namespace bsa

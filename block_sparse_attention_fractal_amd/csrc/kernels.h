@@ -57,6 +57,26 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
                            const void* kt, const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s);
+// Logits of query-block means against Sk key columns (blocks or 4-token groups)
+// for heads h0 .. h0+nheads-1; z holds those heads' rows only.
+hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
+                         int64_t nheads, hipStream_t s);
+// 4-token key groups: float64 group means of k -> kg [B*nh, L/4, D].
+hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStream_t s);
+// CDF cut + window union over the L/4 group logits of rows row0 .. row0+nrows-1
+// (z: those rows, L/4 entries each) -> bitmap rows and kept counts.
+hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, double thr,
+                               double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+                               int words, hipStream_t s);
+int group_select_max_groups();
+// V -> [B*nh, L/4, D, 4] bf16 (each group channel-major) for the gathered attention.
+hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s);
+// Attention over a CSR of 4-token key groups (bf16 needs the prepared vg; f32 reads v).
+hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, const void* vg, void* o, float* lse,
+                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
+                                   hipStream_t s);
+hipError_t launch_attn_groups_f32(const Geom& g, const float* q, const float* k, const float* v, float* o,
+                                  float* lse, const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s);
 // Zero a small device counter (a fill kernel, safe under stream capture).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 

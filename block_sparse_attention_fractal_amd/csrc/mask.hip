@@ -13,6 +13,7 @@
 #include <float.h>
 
 #include "kernels.h"
+#include "mask_util.h"
 
 namespace bsa {
 
@@ -23,17 +24,20 @@ namespace bsa {
 // (c = 0..3), so its LDS operand reads are 16-byte loads at a 16-byte lane
 // stride (no bank conflicts).
 // ---------------------------------------------------------------------------
+// The same kernel serves the key-group map: Sk key columns per head (S for
+// blocks, L/4 for 4-token groups) and heads h0 .. h0 + gridDim.z - 1, with z
+// holding only those heads' rows.
 template <int D>
 __global__ void __launch_bounds__(256) block_logits_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
-                                                           double* __restrict__ z, Geom g, double inv_sqrt_d) {
+                                                           double* __restrict__ z, int Sq, int Sk, int64_t h0,
+                                                           double inv_sqrt_d) {
   constexpr int TM = 128, KC = 16;
   __shared__ __attribute__((aligned(16))) double As[KC][TM];
   __shared__ __attribute__((aligned(16))) double Bs[KC][TM];
-  const int S = g.S;
-  const int64_t bh = blockIdx.z;
+  const int64_t bh = h0 + blockIdx.z;
   const int i0 = blockIdx.y * TM, j0 = blockIdx.x * TM;
-  const double* qh = qp + (size_t)bh * S * D;
-  const double* kh = kp + (size_t)bh * S * D;
+  const double* qh = qp + (size_t)bh * Sq * D;
+  const double* kh = kp + (size_t)bh * Sk * D;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   double acc[8][8];
@@ -48,8 +52,8 @@ __global__ void __launch_bounds__(256) block_logits_kernel(const double* __restr
       const int gi = i0 + lr, gj = j0 + lr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        As[lk + e][lr] = gi < S ? qh[(size_t)gi * D + k0 + lk + e] : 0.0;
-        Bs[lk + e][lr] = gj < S ? kh[(size_t)gj * D + k0 + lk + e] : 0.0;
+        As[lk + e][lr] = gi < Sq ? qh[(size_t)gi * D + k0 + lk + e] : 0.0;
+        Bs[lk + e][lr] = gj < Sk ? kh[(size_t)gj * D + k0 + lk + e] : 0.0;
       }
     }
     __syncthreads();
@@ -70,28 +74,32 @@ __global__ void __launch_bounds__(256) block_logits_kernel(const double* __restr
     }
     __syncthreads();
   }
-  double* zh = z + (size_t)bh * S * S;
+  double* zh = z + (size_t)blockIdx.z * Sq * Sk;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     const int gi = i0 + 32 * (x >> 1) + 2 * ty + (x & 1);
-    if (gi >= S) continue;
+    if (gi >= Sq) continue;
 #pragma unroll
     for (int y = 0; y < 8; ++y) {
       const int gj = j0 + 32 * (y >> 1) + 2 * tx + (y & 1);
-      if (gj < S) zh[(size_t)gi * S + gj] = acc[x][y] * inv_sqrt_d;
+      if (gj < Sk) zh[(size_t)gi * Sk + gj] = acc[x][y] * inv_sqrt_d;
     }
   }
 }
 
-hipError_t launch_block_logits(const Geom& g, const double* qp, const double* kp, double* z, hipStream_t s) {
-  const int t = (g.S + 127) / 128;
-  dim3 grid(t, t, (unsigned)(g.B * g.nh));
+hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
+                         int64_t nheads, hipStream_t s) {
+  dim3 grid((Sk + 127) / 128, (g.S + 127) / 128, (unsigned)nheads);
   const double inv = 1.0 / sqrt((double)g.D);
   if (g.D == 64)
-    block_logits_kernel<64><<<grid, 256, 0, s>>>(qp, kp, z, g, inv);
+    block_logits_kernel<64><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv);
   else
-    block_logits_kernel<128><<<grid, 256, 0, s>>>(qp, kp, z, g, inv);
+    block_logits_kernel<128><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv);
   return hipGetLastError();
+}
+
+hipError_t launch_block_logits(const Geom& g, const double* qp, const double* kp, double* z, hipStream_t s) {
+  return launch_logits(g, qp, kp, z, g.S, 0, (int64_t)g.B * g.nh, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,13 +207,6 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 // ---------------------------------------------------------------------------
 constexpr int kMaxS = 4096;
 
-// order-preserving map of a double to uint64 (larger value -> larger key);
-// -0.0 and +0.0 are equal values and must share one key
-__device__ __forceinline__ uint64_t order_key(double z) {
-  const uint64_t b = z == 0.0 ? 0ull : (uint64_t)__double_as_longlong(z);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
 // Wavefront-wide reduction with DPP moves inside each row of 16 lanes and lane
 // swaps across rows and halves; every lane ends with the result.
 __device__ __forceinline__ uint32_t dpp_step(uint32_t v, int step) {
@@ -261,16 +262,6 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
   return ((uint64_t)hi << 32) | lo;
-}
-
-// Sliding-tile window (NABLA page, Metodologia item 3): block ids are tiles
-// (t, y, x) of Hp x Wp patches per frame; ids i and j are within the window when
-// every coordinate differs by at most the given extent.
-__device__ __forceinline__ bool in_window(const Geom& g, int i, int j, int win_t, int win_h, int win_w) {
-  const int HW = g.Hp * g.Wp;
-  const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
-  const int tj = j / HW, yj = (j / g.Wp) % g.Hp, xj = j % g.Wp;
-  return abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w;
 }
 
 template <int NS>

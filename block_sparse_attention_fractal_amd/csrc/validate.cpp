@@ -2,6 +2,7 @@
 // every rejection here happens before anything touches a GPU.
 #include "validate.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 
@@ -110,6 +111,45 @@ BwdWs bwd_ws_layout(const Geom& g) {
     w.qt = off; off = align256(off + tok * g.D * 2);
     w.dot = off; off = align256(off + tok * g.D * 2);
   }
+  w.total = off;
+  return w;
+}
+
+int check_group(const Geom& g, int group, std::string* msg) {
+  if (group != BSA_KEY_GROUP)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "key group size %lld: only %lld is implemented", group, BSA_KEY_GROUP);
+  const long long SG = g.L / BSA_KEY_GROUP;
+  if (g.rows * SG >= (1LL << 31))
+    return fail(msg, BSA_ERR_UNSUPPORTED,
+                "batch*heads*S*(L/4) = %lld does not fit int32 CSR offsets (split the call by heads)", g.rows * SG);
+  return BSA_OK;
+}
+
+GrpMaskWs grp_mask_ws_layout(const Geom& g) {
+  GrpMaskWs w{};
+  const int64_t SG = g.L / BSA_KEY_GROUP;
+  const int64_t bh = (int64_t)g.B * g.nh;
+  const int64_t per_head = (int64_t)g.S * SG * 8;          // one head's group logits
+  const int64_t budget = int64_t(1) << 31;                 // logits of at most ~2 GiB at a time
+  w.chunk_heads = std::max<int64_t>(1, std::min<int64_t>(bh, budget / per_head));
+  w.words = (int32_t)((SG + 31) / 32);
+  int64_t off = 0;
+  w.qp = off; off = align256(off + g.rows * g.D * 8);
+  w.kg = off; off = align256(off + bh * SG * g.D * 8);
+  w.z = off; off = align256(off + w.chunk_heads * per_head);
+  w.counts = off; off = align256(off + g.rows * 4);
+  w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
+  w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
+  w.total = off;
+  return w;
+}
+
+GrpFwdWs grp_fwd_ws_layout(const Geom& g) {
+  GrpFwdWs w{};
+  int64_t off = 0;
+  w.counter = off; off = align256(off + 64);
+  w.vg = off;
+  if (g.dtype == BSA_BF16) off = align256(off + (int64_t)g.B * g.nh * g.L * g.D * 2);
   w.total = off;
   return w;
 }

@@ -23,6 +23,18 @@ struct BwdWs {        // transposed mask, per-token dO.o, work counters, prepare
   int64_t delta, counter, tcounts, tchunks, tbitmap, tcolptr, trowidx, kt, qt, dot, total;
   int32_t words;
 };
+struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits, bits
+  int64_t qp, kg, z, counts, bitmap, chunk_sums, total;
+  int64_t chunk_heads;  // heads whose group logits are computed together
+  int32_t words;        // 32-bit words per bitmap row (L/4 bits)
+};
+struct GrpFwdWs {
+  int64_t counter, vg, total;
+};
+// Checks the key-group size and the limits of the group path.
+int check_group(const Geom& g, int group, std::string* msg);
+GrpMaskWs grp_mask_ws_layout(const Geom& g);
+GrpFwdWs grp_fwd_ws_layout(const Geom& g);
 BwdWs bwd_ws_layout(const Geom& g);
 MaskWs mask_ws_layout(const Geom& g);
 FwdWs fwd_ws_layout(const Geom& g);

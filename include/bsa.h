@@ -241,12 +241,61 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                  int64_t ws_bytes, hipStream_t stream);
 
+/* ---- 4-token key groups ---------------------------------------------
+ * Fine-grained key selection gathered into full tiles (AB-Attention page,
+ * news.hamidun.com/es/news/14960, "Los tres recursos de AB-Attention", third
+ * resource): keys and values are selected in groups of BSA_KEY_GROUP = 4
+ * consecutive fractal-order tokens, and the attention kernel gathers every 16
+ * kept groups of a row into one 64-key tile by index (no token is reordered or
+ * copied).  Query blocks stay N = 64 tokens, so CSR rows are the same rows
+ * r = (b*heads + h)*S + i as above, but col_idx holds GROUP ids g in [0, L/4)
+ * (group g = fractal tokens [4g, 4g+4)), ascending.
+ * Selection (reading of the page in the NABLA setting): the reduced map taken
+ * at group granularity, A[i, g] = softmax_g(Qp_i . Kg_g / sqrt(D)) with Qp the
+ * 64-token query-block means and Kg the 4-token key-group means, cut per row
+ * exactly as bsa_build_mask cuts the block map (CDF at 1 - thr, same ordering,
+ * tie and thr == 0 rules); a window keeps every group of each window block.
+ * Limits (else BSA_ERR_UNSUPPORTED): group == BSA_KEY_GROUP;
+ * batch*heads*S*(L/4) < 2^31 (int32 CSR offsets: larger problems are split by
+ * heads, every (batch, head) being independent); L/4 <= 32768 for the mask
+ * (one row of the group map is cut inside one workgroup's LDS); mode
+ * BSA_MASK_CDF only. */
+#define BSA_KEY_GROUP 4
+
+/* max_nnz: col_idx capacity bsa_build_group_mask needs (rows * L/4); mask_ws:
+ * its workspace bytes; fwd_ws: bsa_forward_groups' workspace bytes (a prepared
+ * V for bf16 plus work counters). */
+int bsa_query_group_sizes(const bsa_problem* p, int group, int64_t* max_nnz, int64_t* mask_ws, int64_t* fwd_ws);
+
+/* Group mask: pooling of Q into blocks and K into groups (float64), the group
+ * map in float64 (computed a chunk of heads at a time inside ws), the CDF cut
+ * and window union per row, CSR compaction.  q, k in p->layout order; out as for
+ * bsa_build_mask with capacity >= max_nnz (out->shift unused).  ws: at least
+ * mask_ws bytes, 256-byte aligned, clobbered. */
+int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params* mp, const void* q, const void* k,
+                         const bsa_csr* out, void* ws, int64_t ws_bytes, hipStream_t stream);
+
+/* Attention over the kept groups: query token n of block i attends, with scale
+ * 1/sqrt(head_dim), to the tokens of the groups in CSR row i and to nothing else
+ * (o, lse as in bsa_forward; an empty row gives o = 0 and lse = -inf).  mask:
+ * group CSR (ids in [0, L/4), ascending; mask->shift must be NULL).  ws: at least
+ * fwd_ws bytes (bsa_query_group_sizes), 256-byte aligned.
+ * bsa_prepare_v_groups (bf16 only) writes V as [batch, heads, L/4, head_dim, 4]:
+ * each group's 4 tokens stored channel-major (vg: the size of V, 16-byte
+ * aligned); bsa_attend_groups then runs the attention on it (f32: pass V itself)
+ * with ws of at least 256 bytes. */
+int bsa_forward_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* v,
+                       const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
+int bsa_prepare_v_groups(const bsa_problem* p, int group, const void* v, void* vg, hipStream_t stream);
+int bsa_attend_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* vp,
+                      const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
+
 /* Status code -> static string. */
 const char* bsa_status_str(int status);
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* bsa_last_error(void);
 /* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
- * token-order tables and the backward pass. */
+ * token-order tables and the backward pass; 300 adds the 4-token key-group path. */
 int bsa_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 200
+    assert lib.bsa_version() == 300
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -147,3 +147,60 @@ def test_permute_and_pool_reject_before_launch(lib):
     assert lib.bsa_permute(ctypes.byref(p), FAKE, FAKE + 8, 0, None) == 1      # misaligned
     assert lib.bsa_pool(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == 1
     assert lib.bsa_block_map(ctypes.byref(P(H=31)), FAKE, FAKE, FAKE, None) == 2
+
+
+def group_sizes(lib, p, group=4):
+    vals = [ctypes.c_int64() for _ in range(3)]
+    st = lib.bsa_query_group_sizes(ctypes.byref(p), group, *[ctypes.byref(v) for v in vals])
+    return st, [v.value for v in vals]
+
+
+@pytest.mark.parametrize("B,nh,T,H,W", [(1, 8, 8, 32, 32), (1, 40, 21, 32, 48), (1, 24, 33, 48, 80)])
+def test_query_group_sizes(lib, B, nh, T, H, W):
+    D = 128
+    st, (max_nnz, mws, fws) = group_sizes(lib, P(B, nh, T, H, W, D))
+    assert st == 0, lib.bsa_last_error().decode()
+    L = T * H * W
+    S, SG = L // 64, L // 4
+    rows = B * nh * S
+    assert max_nnz == rows * SG
+    # workspace: query-block means, group means, a chunk of heads of group logits
+    # (as many heads as fit 2 GiB, at least one), counts, bitmap, scan chunk sums
+    a = lambda x: (x + 255) // 256 * 256
+    per_head = S * SG * 8
+    chunk = max(1, min(B * nh, (1 << 31) // per_head))
+    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(rows * 4)
+                   + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
+    assert fws == 256 + a(B * nh * L * D * 2)
+
+
+def test_group_path_rejects_before_launch(lib):
+    p = P()
+    st, (max_nnz, mws, fws) = group_sizes(lib, p)
+    assert st == 0
+    assert group_sizes(lib, p, group=8)[0] == 4                       # only 4-token groups
+    assert group_sizes(lib, P(B=2, nh=24, T=33, H=48, W=80))[0] == 4  # int32 CSR offsets: split by heads
+    mp = _lib.MaskParams(0.1, -1, -1, -1, 0, 0)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
+    g = lib.bsa_build_group_mask
+    small = _lib.CSR(FAKE, FAKE, max_nnz - 1, None, None)
+    assert g(ctypes.byref(p), 4, ctypes.byref(mp), FAKE, FAKE, ctypes.byref(small), FAKE, mws, None) == 5
+    assert g(ctypes.byref(p), 4, ctypes.byref(mp), FAKE, FAKE, ctypes.byref(csr), FAKE, mws - 1, None) == 6
+    sip = _lib.MaskParams(0.1, -1, -1, -1, 1, 0)
+    assert g(ctypes.byref(p), 4, ctypes.byref(sip), FAKE, FAKE, ctypes.byref(csr), FAKE, mws, None) == 4
+    bad_thr = _lib.MaskParams(1.5, -1, -1, -1, 0, 0)
+    assert g(ctypes.byref(p), 4, ctypes.byref(bad_thr), FAKE, FAKE, ctypes.byref(csr), FAKE, mws, None) == 1
+    wide = P(T=40, H=64, W=64, nh=1)                                   # L/4 = 40960 groups per head
+    st, (mn, mw, _) = group_sizes(lib, wide)
+    assert st == 0
+    wcsr = _lib.CSR(FAKE, FAKE, mn, None, None)
+    assert g(ctypes.byref(wide), 4, ctypes.byref(mp), FAKE, FAKE, ctypes.byref(wcsr), FAKE, mw, None) == 4
+    f = lib.bsa_forward_groups
+    assert f(ctypes.byref(p), 4, FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws - 1, None) == 6
+    assert f(ctypes.byref(p), 4, FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 1
+    shifted = _lib.CSR(FAKE, FAKE, max_nnz, None, FAKE)
+    assert f(ctypes.byref(p), 4, FAKE, FAKE, FAKE, ctypes.byref(shifted), FAKE, None, FAKE, fws, None) == 4
+    assert lib.bsa_attend_groups(ctypes.byref(p), 3, FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, 256,
+                                 None) == 4
+    f32 = P(dtype=0, D=64)
+    assert lib.bsa_prepare_v_groups(ctypes.byref(f32), 4, FAKE, FAKE + 256, None) == 4
