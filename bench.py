@@ -114,6 +114,59 @@ def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
     }
 
 
+def time_groups(bsa, cfg, q, k, v, g, steps, warmup, stream):
+    """Event-timed key-group path: build_group_mask, prepare_v_groups and
+    attend_groups on the same inputs.  A problem whose group CSR would need more
+    than int32 offsets (batch*heads*S*L/4 >= 2^31) runs one call per batch item,
+    all within the timed region.  Executed FLOPs: 4*64*64*D per gathered 64-key
+    tile (ceil(groups/16) tiles per row)."""
+    import torch
+    D = q.shape[-1]
+    parts = [slice(None)] if cfg.batch * cfg.heads * cfg.S * (cfg.L // 4) < 2 ** 31 else \
+        [slice(b, b + 1) for b in range(cfg.batch)]
+    qs, ks, vs = ([x[p] for p in parts] for x in (q, k, v))
+    prob = bsa.make_problem(qs[0], g)
+    gs = bsa.query_group_sizes(prob)
+    mws = torch.empty(gs["mask_ws"], dtype=torch.uint8, device=q.device)
+    fws = torch.empty(256, dtype=torch.uint8, device=q.device)
+    vg = torch.empty(qs[0].numel(), dtype=q.dtype, device=q.device)
+    outs = [torch.empty_like(x) for x in qs]
+    masks = [None] * len(parts)
+
+    def one(ev=None):
+        t = [0.0, 0.0, 0.0]
+        for x in range(len(parts)):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            masks[x] = bsa.build_group_mask(qs[x], ks[x], g, cfg.thr, cfg.window, workspace=mws)
+            e[1].record(stream)
+            bsa.prepare_v_groups(vs[x], g, out=vg)
+            e[2].record(stream)
+            bsa.attend_groups(qs[x], ks[x], vg, masks[x], g, workspace=fws, out=outs[x])
+            e[3].record(stream)
+            if ev is not None:
+                ev.append(e)
+
+    for _ in range(max(1, warmup)):
+        one()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        one(evs)
+    torch.cuda.synchronize()
+    per = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(3)]
+    ms = [float(np.sum(x)) / steps for x in per]
+    nnz = sum(m.nnz() for m in masks)
+    tiles = sum(int(((m.row_ptr[1:] - m.row_ptr[:-1] + 15) // 16).sum()) for m in masks)
+    flops = 4.0 * 64 * 64 * D * tiles
+    tf = flops / (ms[2] * 1e-3) / 1e12
+    total_groups = cfg.rows * (cfg.L // 4)
+    return {"calls_per_step": len(parts), "ms_mask": round(ms[0], 4), "ms_prepare_v": round(ms[1], 4),
+            "ms_attend": round(ms[2], 4), "ms_total": round(sum(ms), 4), "nnz_groups": nnz,
+            "density": round(nnz / total_groups, 5), "tiles": tiles, "executed_tflop": round(flops / 1e12, 3),
+            "attend_tflops": round(tf, 2), "attend_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
     """Event-timed bsa_backward calls (one call = row-term prep, transposed mask,
     operand transposes, the dQ kernel and the dK/dV kernel) on the bench's mask, with a
@@ -161,6 +214,8 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also print per-stage details on stderr")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (dq, dk, dv) on the same mask after the forward steps")
+    ap.add_argument("--groups", action="store_true",
+                    help="also time the 4-token key-group path (group mask, V preparation, gathered attention)")
     ap.add_argument("--sip-seed", type=int, default=None,
                     help="build the mask by SIP sampling with this Philox seed instead of the CDF cut")
     args = ap.parse_args()
@@ -284,6 +339,8 @@ def main():
         "executed_tflop": round(exec_flops / 1e12, 3),
         "input_gen_s": round(t_gen, 1),
     }
+    if args.groups:
+        line["groups"] = time_groups(bsa, cfg, q, k, v, g, args.steps, args.warmup, stream)
     if args.backward:
         line["backward"] = time_backward(bsa, q, k, v, mask, g, fwd_ws, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:

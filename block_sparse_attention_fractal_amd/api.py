@@ -329,11 +329,15 @@ def build_group_mask(q: torch.Tensor, k: torch.Tensor, grid: VideoGrid, thr: flo
     return mask
 
 
-def prepare_v_groups(v: torch.Tensor, grid: VideoGrid, layout: str = "original") -> torch.Tensor:
-    """bf16 only: V as [batch, heads, L/4, D, 4] (each 4-token group channel-major), flat."""
+def prepare_v_groups(v: torch.Tensor, grid: VideoGrid, layout: str = "original",
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 only: V as [batch, heads, L/4, D, 4] (each 4-token group channel-major), flat
+    (written into `out` when given: a contiguous tensor of V's dtype and size)."""
     _check_qkv(v)
     prob = make_problem(v, grid, layout)
-    vg = torch.empty(v.numel(), dtype=v.dtype, device=v.device)
+    if out is not None and (out.numel() != v.numel() or out.dtype != v.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor with v's dtype and size")
+    vg = torch.empty(v.numel(), dtype=v.dtype, device=v.device) if out is None else out
     check(lib().bsa_prepare_v_groups(ctypes.byref(prob), KEY_GROUP, v.data_ptr(), vg.data_ptr(), _stream(v.device)))
     return vg
 

@@ -7,11 +7,13 @@
 //   * pool_groups_kernel: float64 means of 4 consecutive fractal-order keys;
 //   * the logits reuse the float64 block-logit GEMM with L/4 key columns, run
 //     over a chunk of heads at a time so the workspace stays bounded;
-//   * group_select_kernel: the CDF cut of one row per 256-thread workgroup.
+//   * group_select_kernel: the CDF cut of one row per 1024-thread workgroup.
 //     A row has L/4 entries (31 680 at 33 x 48 x 80 tokens), too many to hold
 //     in registers as the block select does, so the row is read twice from
 //     the logits (max, then the float32 offsets z - max into LDS, 4 B per
-//     entry) and every radix pass runs over LDS.  The numerics are those of the
+//     entry) and every radix pass runs over LDS (the float32 exponential of an
+//     entry is only recomputed where its mass enters a histogram or the exact
+//     ranking; the keys are a subtraction and a scale).  The numerics are those of the
 //     block select: the ORDER is decided on the float64 logits, the masses are
 //     float32 exponentials in fixed point (2^-30 of the row max) summed exactly,
 //     the 24-bit monotone key is radix-selected 8 bits per pass until the
@@ -27,6 +29,8 @@ namespace bsa {
 namespace gmask {
 
 constexpr int kMaxSG = 32768;     // groups per head the LDS row buffer holds
+constexpr int kNT = 1024;         // threads per row: the LDS row buffer allows one workgroup
+constexpr int kNW = kNT / 64;     // per CU, so the row gets 16 waves to hide its loads
 
 // float64 means of every 4 consecutive fractal-order rows of k -> kg [B*nh, L/4, D].
 // Thread = (group, 4 channels); the group's 4 rows are consecutive in memory.
@@ -69,10 +73,10 @@ struct SelectSmem {
   unsigned long long hm[256];         //             masses
   uint32_t cj[256], cw[256];          // crossing entries: index, mass
   unsigned long long ck[256];         //                   exact order key
-  unsigned long long red_u[4];
-  double red_d[4];
-  float red_f[4];
-  unsigned long long scan[4];
+  unsigned long long red_u[kNW];
+  double red_d[kNW];
+  float red_f[kNW];
+  unsigned long long scan[kNW];
   int found_bin;
   uint32_t found_cnt, ncross;
   unsigned long long found_above;
@@ -90,7 +94,7 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int d) {
   return __longlong_as_double((long long)shfl_xor_u64((unsigned long long)__double_as_longlong(v), d));
 }
 
-__global__ void __launch_bounds__(256) group_select_kernel(const double* __restrict__ z, int64_t row0, int SG,
+__global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restrict__ z, int64_t row0, int SG,
                                                            Geom g, double thr, double lambda, int win_t, int win_h,
                                                            int win_w, uint32_t* __restrict__ bitmap,
                                                            int32_t* __restrict__ counts, int words) {
@@ -100,7 +104,7 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
   const int i = (int)(r % g.S);
   const double* zr = z + (int64_t)blockIdx.x * SG;
   const int gpb = g.N / 4;
-  for (int x = tid; x < words; x += 256) sm.bm[x] = 0u;
+  for (int x = tid; x < words; x += kNT) sm.bm[x] = 0u;
 
   // workgroup reductions (fixed tree order, deterministic)
   auto sum_u64 = [&](unsigned long long v) {
@@ -108,7 +112,8 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
     for (int d = 32; d > 0; d >>= 1) v += shfl_xor_u64(v, d);
     if (lane == 0) sm.red_u[wv] = v;
     __syncthreads();
-    const unsigned long long t = sm.red_u[0] + sm.red_u[1] + sm.red_u[2] + sm.red_u[3];
+    unsigned long long t = 0;
+    for (int x = 0; x < kNW; ++x) t += sm.red_u[x];
     __syncthreads();
     return t;
   };
@@ -118,7 +123,7 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
     if (lane == 0) sm.red_u[wv] = v;
     __syncthreads();
     unsigned long long t = sm.red_u[0];
-    for (int x = 1; x < 4; ++x) t = sm.red_u[x] > t ? sm.red_u[x] : t;
+    for (int x = 1; x < kNW; ++x) t = sm.red_u[x] > t ? sm.red_u[x] : t;
     __syncthreads();
     return t;
   };
@@ -128,7 +133,7 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
     if (lane == 0) sm.red_u[wv] = v;
     __syncthreads();
     unsigned long long t = sm.red_u[0];
-    for (int x = 1; x < 4; ++x) t = sm.red_u[x] < t ? sm.red_u[x] : t;
+    for (int x = 1; x < kNW; ++x) t = sm.red_u[x] < t ? sm.red_u[x] : t;
     __syncthreads();
     return t;
   };
@@ -137,7 +142,8 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
     for (int d = 32; d > 0; d >>= 1) v = fmax(v, shfl_xor_f64(v, d));
     if (lane == 0) sm.red_d[wv] = v;
     __syncthreads();
-    const double t = fmax(fmax(sm.red_d[0], sm.red_d[1]), fmax(sm.red_d[2], sm.red_d[3]));
+    double t = sm.red_d[0];
+    for (int x = 1; x < kNW; ++x) t = fmax(t, sm.red_d[x]);
     __syncthreads();
     return t;
   };
@@ -146,7 +152,8 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
     for (int d = 32; d > 0; d >>= 1) v = fminf(v, __shfl_xor(v, d, 64));
     if (lane == 0) sm.red_f[wv] = v;
     __syncthreads();
-    const float t = fminf(fminf(sm.red_f[0], sm.red_f[1]), fminf(sm.red_f[2], sm.red_f[3]));
+    float t = sm.red_f[0];
+    for (int x = 1; x < kNW; ++x) t = fminf(t, sm.red_f[x]);
     __syncthreads();
     return t;
   };
@@ -167,64 +174,76 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
   auto set_bit = [&](int j) { atomicOr(&sm.bm[j >> 5], 1u << (j & 31)); };
 
   if (thr == 0.0) {
-    for (int x = tid; x < words; x += 256) {
+    for (int x = tid; x < words; x += kNT) {
       const int left = SG - 32 * x;
       sm.bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
     }
   } else {
-    // pass 1 over the logits: row max; pass 2: candidates, masses, offsets into LDS
+    // pass 1 over the logits: row max; pass 2: candidates, masses, offsets into
+    // LDS (four independent loads in flight per thread in both passes)
     double m = -DBL_MAX;
-    for (int j = tid; j < SG; j += 256) m = fmax(m, zr[j]);
+    for (int j0 = tid; j0 < SG; j0 += 4 * kNT) {
+      double v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = zr[min(j0 + u * kNT, SG - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = fmax(m, v[u]);
+    }
     m = max_f64(m);
     unsigned long long wsum = 0;
     float dmin = 0.f;
-    for (int j = tid; j < SG; j += 256) {
-      const double d = zr[j] - m;
-      const float df = (float)d;
-      const float e = d >= -lambda ? __builtin_amdgcn_exp2f(df * 1.44269504088896341f) : 0.f;
-      const uint32_t w = (uint32_t)(e * 1073741824.0f);    // e <= 1: at most 2^30, exact
-      sm.dv[j] = w != 0u ? df : -INFINITY;
-      wsum += w;
-      if (w != 0u) dmin = fminf(dmin, df);
+    for (int j0 = tid; j0 < SG; j0 += 4 * kNT) {
+      double v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = zr[min(j0 + u * kNT, SG - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kNT;
+        if (j >= SG) continue;
+        const double d = v[u] - m;
+        const float df = (float)d;
+        const float e = d >= -lambda ? __builtin_amdgcn_exp2f(df * 1.44269504088896341f) : 0.f;
+        const uint32_t w = (uint32_t)(e * 1073741824.0f);   // e <= 1: at most 2^30, exact
+        sm.dv[j] = w != 0u ? df : -INFINITY;
+        wsum += w;
+        if (w != 0u) dmin = fminf(dmin, df);
+      }
     }
     const unsigned long long total = sum_u64(wsum);     // (its barriers also publish dv)
     dmin = min_f32(dmin);
     const float tscale = dmin < 0.f ? 16777215.0f / (-dmin) : 0.f;
     const double target = (1.0 - thr) * (double)total;   // keep while exclusive prefix < target
-    // mass and 24-bit key of entry j, recomputed from its offset exactly as above
-    auto mass_key = [&](int j, uint32_t& w, uint32_t& t) {
-      const float df = sm.dv[j];
-      if (df == -INFINITY) {
-        w = 0u;
-        t = 0u;
-        return;
-      }
-      const float e = __builtin_amdgcn_exp2f(df * 1.44269504088896341f);
-      w = (uint32_t)(e * 1073741824.0f);
-      t = (uint32_t)fminf((df - dmin) * tscale, 16777215.0f);
+    // 24-bit key of a candidate offset, and its mass, recomputed exactly as above
+    auto key_of = [&](float df) { return (uint32_t)fminf((df - dmin) * tscale, 16777215.0f); };
+    auto mass_of = [&](float df) {
+      return (uint32_t)(__builtin_amdgcn_exp2f(df * 1.44269504088896341f) * 1073741824.0f);
     };
     // one radix pass: (count, mass) histogram of bin(j) >= 0, then the bin in
     // which the cumulative mass from the top (bin 255 first) reaches the target
     auto crossing = [&](auto bin, unsigned long long above_in, int& b_out, unsigned long long& above_out,
                         uint32_t& cnt_out) {
-      sm.hc[tid] = 0u;
-      sm.hm[tid] = 0ull;
+      if (tid < 256) {
+        sm.hc[tid] = 0u;
+        sm.hm[tid] = 0ull;
+      }
       if (tid == 0) sm.found_bin = -1;
       __syncthreads();
-      for (int j = tid; j < SG; j += 256) {
-        uint32_t w;
-        const int b = bin(j, w);
+      for (int j = tid; j < SG; j += kNT) {
+        const float df = sm.dv[j];
+        if (df == -INFINITY) continue;
+        const int b = bin(j, df);
         if (b >= 0) {
           atomicAdd(&sm.hc[b], 1u);
-          atomicAdd(&sm.hm[b], (unsigned long long)w);
+          atomicAdd(&sm.hm[b], (unsigned long long)mass_of(df));
         }
       }
       __syncthreads();
-      const int b = 255 - tid;                           // thread order = bins from the top
-      const unsigned long long mb = sm.hm[b];
+      const int b = 255 - min(tid, 255);                 // threads 0..255: bins from the top
+      const unsigned long long mb = tid < 256 ? sm.hm[b] : 0ull;
       const unsigned long long incl = incl_scan_u64(mb);
       const unsigned long long excl = incl - mb;
-      if (sm.hc[b] != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + incl)) {
+      if (tid < 256 && sm.hc[b] != 0u && (double)(above_in + excl) < target &&
+          target <= (double)(above_in + incl)) {
         sm.found_bin = b;
         sm.found_above = above_in + excl;
         sm.found_cnt = sm.hc[b];
@@ -250,10 +269,9 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
       unsigned long long ab;
       uint32_t cb;
       if (!crossing(
-              [&](int j, uint32_t& w) {
-                uint32_t t;
-                mass_key(j, w, t);
-                return w != 0u && (t >> tshc) == pf ? (int)((t >> sh) & 255u) : -1;
+              [&](int, float df) {
+                const uint32_t t = key_of(df);
+                return (t >> tshc) == pf ? (int)((t >> sh) & 255u) : -1;
               },
               above, b, ab, cb)) {
         reach = false;                                   // only possible on the first pass
@@ -265,30 +283,25 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
       cnt = cb;
       if (cnt <= 256u) break;
     }
-    auto in_bin = [&](int j, uint32_t& w) {
-      uint32_t t;
-      mass_key(j, w, t);
-      return w != 0u && (t >> tsh) == tpre;
-    };
+    auto in_bin = [&](float df) { return df != -INFINITY && (key_of(df) >> tsh) == tpre; };
     if (!reach) {                                        // every candidate is kept
-      for (int j = tid; j < SG; j += 256)
+      for (int j = tid; j < SG; j += kNT)
         if (sm.dv[j] != -INFINITY) set_bit(j);
     } else {
-      for (int j = tid; j < SG; j += 256) {
-        uint32_t w, t;
-        mass_key(j, w, t);
-        if (w != 0u && (t >> tsh) > tpre) set_bit(j);
+      for (int j = tid; j < SG; j += kNT) {
+        const float df = sm.dv[j];
+        if (df != -INFINITY && (key_of(df) >> tsh) > tpre) set_bit(j);
       }
       if (cnt <= 256u) {
         // the crossing bin's entries, ranked exactly on their float64 logits
         if (tid == 0) sm.ncross = 0u;
         __syncthreads();
-        for (int j = tid; j < SG; j += 256) {
-          uint32_t w;
-          if (in_bin(j, w)) {
+        for (int j = tid; j < SG; j += kNT) {
+          const float df = sm.dv[j];
+          if (in_bin(df)) {
             const uint32_t x = atomicAdd(&sm.ncross, 1u);
             sm.cj[x] = (uint32_t)j;
-            sm.cw[x] = w;
+            sm.cw[x] = mass_of(df);
             sm.ck[x] = order_key(zr[j]);
           }
         }
@@ -307,9 +320,8 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
       } else {
         // more than 256 entries share one 24-bit key: exact 64-bit keys, then ties
         unsigned long long kmax = 0, kmin = ~0ull;
-        for (int j = tid; j < SG; j += 256) {
-          uint32_t w;
-          if (in_bin(j, w)) {
+        for (int j = tid; j < SG; j += kNT) {
+          if (in_bin(sm.dv[j])) {
             const unsigned long long key = order_key(zr[j]);
             kmax = key > kmax ? key : kmax;
             kmin = key < kmin ? key : kmin;
@@ -330,8 +342,8 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
           // the crossing entry lies in this bin and shares the decided prefix,
           // so a bin is always found
           crossing(
-              [&](int j, uint32_t& w) {
-                if (!in_bin(j, w)) return -1;
+              [&](int j, float df) {
+                if (!in_bin(df)) return -1;
                 const unsigned long long key = order_key(zr[j]);
                 return (key & hi_mask) == pf ? (int)((key >> sh) & 255u) : -1;
               },
@@ -344,12 +356,12 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
         }
         const unsigned long long hi_key = shift == 0 ? prefix : (prefix | ((1ull << shift) - 1));
         uint32_t wt = 0;
-        for (int j = tid; j < SG; j += 256) {
-          uint32_t w;
-          if (in_bin(j, w)) {
+        for (int j = tid; j < SG; j += kNT) {
+          const float df = sm.dv[j];
+          if (in_bin(df)) {
             const unsigned long long key = order_key(zr[j]);
             if (key > hi_key || (cnt <= 1u && key >= prefix)) set_bit(j);
-            if (cnt > 1u && key == prefix) wt = w;
+            if (cnt > 1u && key == prefix) wt = mass_of(df);
           }
         }
         if (cnt > 1u) {
@@ -357,13 +369,9 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
           // the target; all tied entries have the same logit, hence the same mass
           wt = (uint32_t)max_u64(wt);
           unsigned long long acc = above;
-          for (int base = 0; base < SG; base += 256) {
+          for (int base = 0; base < SG; base += kNT) {
             const int j = base + tid;
-            bool tie = false;
-            if (j < SG) {
-              uint32_t w;
-              tie = in_bin(j, w) && order_key(zr[j]) == prefix;
-            }
+            const bool tie = j < SG && in_bin(sm.dv[j]) && order_key(zr[j]) == prefix;
             const unsigned long long incl = incl_scan_u64(tie ? 1ull : 0ull);
             if (tie && (double)(acc + (incl - 1) * wt) < target) set_bit(j);
             acc += sum_u64(tie ? 1ull : 0ull) * wt;
@@ -374,11 +382,11 @@ __global__ void __launch_bounds__(256) group_select_kernel(const double* __restr
   }
   __syncthreads();
   if (win_t >= 0)
-    for (int j = tid; j < SG; j += 256)
+    for (int j = tid; j < SG; j += kNT)
       if (in_window(g, i, j / gpb, win_t, win_h, win_w)) set_bit(j);
   __syncthreads();
   unsigned long long pc = 0;
-  for (int x = tid; x < words; x += 256) {
+  for (int x = tid; x < words; x += kNT) {
     const uint32_t v = sm.bm[x];
     bitmap[r * words + x] = v;
     pc += __popc(v);
@@ -402,7 +410,7 @@ hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStrea
 hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, double thr,
                                double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
                                int words, hipStream_t s) {
-  gmask::group_select_kernel<<<(unsigned)nrows, 256, 0, s>>>(z, row0, g.L / 4, g, thr, lambda, win_t, win_h, win_w,
+  gmask::group_select_kernel<<<(unsigned)nrows, gmask::kNT, 0, s>>>(z, row0, g.L / 4, g, thr, lambda, win_t, win_h, win_w,
                                                              bitmap, counts, words);
   return hipGetLastError();
 }

@@ -809,8 +809,10 @@ hipError_t launch_scan(const Geom& g, const int32_t* counts, int32_t* row_ptr, i
 }
 
 // ---------------------------------------------------------------------------
-// Bitmap -> ascending column list; one wavefront per row.  Each lane tests one
-// block id per step and a ballot turns the bits into coalesced output slots.
+// Bitmap -> ascending column list; one wavefront per row, 64 bitmap words
+// (2048 columns) per step: popcounts and an exclusive scan across the lanes give
+// each word's output offset; a sparse step lets each lane write its own word's
+// column ids, a dense one walks the columns in order, 64 per ballot.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) compact_kernel(const uint32_t* __restrict__ bitmap, int words,
                                                       const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
@@ -820,13 +822,39 @@ __global__ void __launch_bounds__(256) compact_kernel(const uint32_t* __restrict
   if (r >= rows) return;
   const uint32_t* bm = bitmap + r * words;
   int32_t base = row_ptr[r];
-  for (int j0 = 0; j0 < S; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t wv = bm[min(j >> 5, words - 1)];
-    const bool on = j < S && ((wv >> (j & 31)) & 1u);
-    const uint64_t mask = __ballot(on);
-    if (on) col_idx[base + __popcll(mask & ((1ull << lane) - 1))] = j;
-    base += __popcll(mask);
+  for (int x0 = 0; x0 < words; x0 += 64) {
+    const int x = x0 + lane;
+    uint32_t wbits = x < words ? bm[x] : 0u;
+    if (32 * x + 32 > S) wbits &= x * 32 >= S ? 0u : ((1u << (S - 32 * x)) - 1u);   // columns >= S
+    const int pc = __popc(wbits);
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (total > 256) {
+      // dense step: columns in order, 64 per ballot, so the stores are coalesced
+      const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int32_t b2 = base;
+      for (int c = 0; c < 32; ++c) {
+        const uint32_t wv = (uint32_t)__shfl((int)wbits, 2 * c + (lane >> 5), 64);   // word of column 64c + lane
+        const bool on = (wv >> (lane & 31)) & 1u;
+        const uint64_t msk = __ballot(on);
+        if (on) col_idx[b2 + __popcll(msk & lt)] = 32 * x0 + 64 * c + lane;
+        b2 += __popcll(msk);
+      }
+    } else {
+      // sparse step: each lane writes its own word's columns
+      int32_t* out = col_idx + base + (incl - pc);
+      while (wbits) {
+        const int b = __ffs(wbits) - 1;
+        *out++ = 32 * x + b;
+        wbits &= wbits - 1u;
+      }
+    }
+    base += total;
   }
 }
 
