@@ -284,13 +284,12 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
     e = launch_scan(g, tcounts, tcolptr, reinterpret_cast<int32_t*>(base + w.tchunks), nullptr, stream);
   if (e == hipSuccess) e = launch_compact(g, tbits, w.words, tcolptr, trowidx, stream);
   if (e == hipSuccess && g.dtype == BSA_BF16) {
-    e = launch_prep_vt(g, k, base + w.kt, stream);
-    if (e == hipSuccess) e = launch_prep_vt(g, q, base + w.qt, stream);
+    e = launch_prep_vt(g, q, base + w.qt, stream);
     if (e == hipSuccess) e = launch_prep_vt(g, dout, base + w.dot, stream);
   }
   if (e == hipSuccess) e = launch_zero_i32(counters, 16, stream);
   if (e == hipSuccess)
-    e = launch_backward(g, q, k, v, dout, base + w.kt, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
+    e = launch_backward(g, q, k, v, dout, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
                         mask->col_idx, tcolptr, trowidx, counters, ncu, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return BSA_OK;

@@ -34,6 +34,9 @@ namespace bwd {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kD = 128;
 constexpr int kTile = 16384;          // one 64 x 128 bf16 tile (natural or transposed)
@@ -53,8 +56,7 @@ struct Args {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const uint16_t* kt;      // prepared transposes [B*nh, S, D, 64]
-  const uint16_t* qt;
+  const uint16_t* qt;      // prepared transposes [B*nh, S, D, 64]
   const uint16_t* dot;
   const float2* ld;        // per token: (lse * log2 e, Delta)
   uint16_t* dq;
@@ -176,11 +178,14 @@ __device__ __forceinline__ void store_pair(uint8_t* stage, const f32x16 (&acc)[4
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass (bf16).  Stage: natural K | natural V | transposed K, 48 KB; two stages.
+// dQ pass (bf16).  Stage: natural K | natural V, 32 KB; two stages; two
+// workgroups per CU (249 VGPRs).  The K^T operand of the dQ product comes from
+// the natural K tile through gfx950's transposing LDS reads.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 1) dq_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[3 * kTile];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[3 * kTile];
+__global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem_dq[4 * kTile];
+  uint8_t* const stage0 = smem_dq;
+  uint8_t* const stage1 = smem_dq + 2 * kTile;
   __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -189,17 +194,28 @@ __global__ void __launch_bounds__(256, 1) dq_bf16_kernel(Args a) {
   const int rs = g.layout == 1 ? 8 : g.W;
   const float c_log2 = a.c_log2;
 
-  int noff[4], toff[4];              // per-lane byte offsets of the 16-byte chunks this thread loads
+  int noff[4];                       // per-lane byte offsets of the 16-byte chunks this thread loads
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int c = (4 * wave + u) * 64 + lane;
     const int m = c >> 4;
     const int lc = (lane & 15) ^ (m & 15);
     noff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
-    const int d = c >> 3;
-    const int lv = (lane & 7) ^ ((d >> 1) & 7);
-    toff[u] = d * 128 + lv * 16;
   }
+  // byte offset in the natural K tile of this lane's transposing read for k-step s,
+  // channel tile u, read r2 (keys 16s + 4h + 0..3, or + 8): row 16s + 8r2 + 4h + j/4,
+  // 16-byte chunk 4u + c0 swizzled by the row's low 4 bits.  Those bits are
+  // 8r2 + 4h + j/4, so the swizzled chunk is 4(u ^ (2r2 + h)) + (c0 ^ j/4): four
+  // per-lane bases (one per u ^ h) plus immediates cover all 32 reads of a tile.
+  int trp[4];
+  {
+    const int trj = lane & 15, trg = lane >> 4, hh = trg >> 1;
+    const int c0 = 2 * (trg & 1) + ((trj & 3) >> 1);
+    const int b0 = (4 * hh + (trj >> 2)) * 256 + 16 * (c0 ^ (trj >> 2)) + 8 * (trj & 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) trp[x] = b0 + 64 * (x ^ hh);
+  }
+  auto tr_off = [&](int u, int s, int r2) { return trp[u ^ (2 * r2)] + 2048 * r2 + 4096 * s; };
   const int xcd = blockIdx.x & 7;
   int64_t lo_t, hi_t;
   item_range(a, xcd, lo_t, hi_t);
@@ -221,18 +237,14 @@ __global__ void __launch_bounds__(256, 1) dq_bf16_kernel(Args a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t trs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.kt + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
     auto issue = [&](int j, uint8_t* st) {
       const int jc = min(max(j, 0), g.S - 1);
       const int ns = block_base_row(g, jc) * kD * 2;
-      const int ts = jc * kD * 64 * 2;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int slot = (4 * wave + u) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + slot), 16, noff[u], ns, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kTile + slot), 16, noff[u], ns, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (lds_void*)(st + 2 * kTile + slot), 16, toff[u], ts, 0, 0);
       }
     };
 
@@ -270,44 +282,50 @@ __global__ void __launch_bounds__(256, 1) dq_bf16_kernel(Args a) {
       if (jn != 0x7fffffff) issue(jn, other);
       const bool mine = qb == 0 ? ka : kb;
       if (mine) {
-        f32x16 sacc[2], pacc[2];
+        // one 32-key half of the tile at a time keeps only one S / dP pair live
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+          f32x16 sacc, pacc;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            sacc[t][e] = 0.f;
-            pacc[t][e] = 0.f;
+            sacc[e] = 0.f;
+            pacc[e] = 0.f;
           }
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
             const bf16x8 ak = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
-            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc, 0, 0, 0);
             const bf16x8 av = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
-            pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc[t], 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc, 0, 0, 0);
           }
-        }
-        // dZ = hi + lo, two bf16 terms: the dZ of one query sum to zero, so dQ is a
-        // small difference of large terms when K has a large common part, and a
-        // single bf16 rounding of dZ (2^-9) would show in it at the percent level.
-        bf16x8 dsh[4], dsl[4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
+          // dZ = hi + lo, two bf16 terms: the dZ of one query sum to zero, so dQ is a
+          // small difference of large terms when K has a large common part, and a
+          // single bf16 rounding of dZ (2^-9) would show in it at the percent level.
+          bf16x8 dsh[2], dsl[2];
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, -lse2));
-            const float ds = p * (pacc[t][e] - dlt);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -lse2));
+            const float ds = p * (pacc[e] - dlt);
             const __bf16 hi = (__bf16)ds;
-            dsh[2 * t + (e >> 3)][e & 7] = hi;
-            dsl[2 * t + (e >> 3)][e & 7] = (__bf16)(ds - (float)hi);
+            dsh[e >> 3][e & 7] = hi;
+            dsl[e >> 3][e & 7] = (__bf16)(ds - (float)hi);
           }
-        }
+          // K^T operand straight from the natural K tile with transposing LDS reads:
+          // in each 16-lane group, source lane j reads keys-row kbase + j/4 at channels
+          // dbase + 4(j%4) .. +3 and lane i receives keys kbase .. kbase+3 of channel
+          // dbase + i; two reads give the 8 keys of a lane's operand
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * t + s2;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bf16x8 at = *(const bf16x8*)(st + 2 * kTile + tr_lds(32 * u + l32, 2 * s + h));
-            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsh[s], acc[u], 0, 0, 0);
-            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsl[s], acc[u], 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+              const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 0)));
+              const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 1)));
+              const bf16x8 at =
+                  __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsh[s2], acc[u], 0, 0, 0);
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsl[s2], acc[u], 0, 0, 0);
+            }
           }
         }
       }
@@ -705,7 +723,7 @@ hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, 
 }
 
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* kt, const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s) {
   const double scale = 1.0 / sqrt((double)g.D);
@@ -731,7 +749,6 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout;
-  a.kt = (const uint16_t*)kt;
   a.qt = (const uint16_t*)qt;
   a.dot = (const uint16_t*)dot;
   a.ld = ld;
@@ -747,7 +764,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.ptr = row_ptr;
   a.idx = col_idx;
   a.counters = counters;
-  bwd::dq_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  bwd::dq_bf16_kernel<<<((num_cu * 2 + 7) / 8) * 8, 256, 0, s>>>(a);   // two workgroups per CU
   a.ptr = tcolptr;
   a.idx = trowidx;
   a.counters = counters + 8;

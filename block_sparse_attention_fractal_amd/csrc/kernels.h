@@ -51,10 +51,10 @@ hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const 
 hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, const float* lse, float2* ld,
                                 const int32_t* row_ptr, const int32_t* col_idx, uint32_t* tbits, int words,
                                 int32_t* tcounts, hipStream_t s);
-// Backward: dQ over the CSR, dK/dV over the transposed CSR (kt, qt, dot: prepared
+// Backward: dQ over the CSR, dK/dV over the transposed CSR (qt, dot: prepared
 // transposes of K, Q, dO for bf16; counters: 16 ints, zeroed).
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* kt, const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s);
 // Logits of query-block means against Sk key columns (blocks or 4-token groups)

@@ -20,7 +20,7 @@ struct FwdWs {
   int64_t counter, vt, total;
 };
 struct BwdWs {        // transposed mask, per-token dO.o, work counters, prepared transposes (bf16)
-  int64_t delta, counter, tcounts, tchunks, tbitmap, tcolptr, trowidx, kt, qt, dot, total;
+  int64_t delta, counter, tcounts, tchunks, tbitmap, tcolptr, trowidx, qt, dot, total;
   int32_t words;
 };
 struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits, bits
