@@ -120,3 +120,57 @@ def test_backward_odd_blocks_and_unused_keys(dtype, D):
 def test_backward_dense_mask_bf16():
     cfg = small_cfg(nh=2, T=2, H=16, W=32, thr=0.0, seed=31)
     run_case(cfg, make_inputs(cfg), thr=0.0)
+
+
+def test_backward_fullsize_sampled():
+    """The Wan2.1-scale workload (40 heads, 21 x 32 x 48 tokens) at full size, as the
+    benchmark's backward leg runs it: dQ on sampled query blocks (the oracle needs
+    only that row's keys) and dK, dV on sampled key blocks (the oracle sums exactly
+    the rows whose CSR keeps the block), on three heads."""
+    cfg = get_config(2)
+    inputs = make_inputs(cfg)
+    g = grid_of(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    for n in ("q_bits", "k_bits", "v_bits"):
+        inputs.pop(n)
+    mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window)
+    o, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+    do_np = dout_for(cfg)
+    dq, dk, dv = bsa.backward(q, k, v, mask, g, o, lse, to_dev(do_np, cfg.dtype))
+    torch.cuda.synchronize()
+    S = cfg.S
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    o_h = to_host_f64(o)
+    grads = [to_host_f64(x) for x in (dq, dk, dv)]
+    rng = np.random.default_rng(8)
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for h in (0, 17, 39):
+        r0 = h * S
+        lo, hi = int(rp[r0]), int(rp[r0 + S])
+        ci = mask.col_idx[lo:hi].cpu().numpy()
+        prp = rp[r0:r0 + S + 1] - lo
+        qf, kf, vf, dof = (x[0:1, h:h + 1][:, :, src] for x in (inputs["q"], inputs["k"], inputs["v"], do_np))
+        of = o_h[0:1, h:h + 1][:, :, src]
+        qrows = sorted(rng.choice(S, 8, replace=False).tolist())
+        rdq, _, _ = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci, dof, 64, rows=qrows, O=of)
+        for i in qrows:
+            tok = src[i * 64:(i + 1) * 64]
+            got["dq"].append(grads[0][0, h, tok])
+            ref["dq"].append(rdq[0, 0, i * 64:(i + 1) * 64])
+        rows_of = np.repeat(np.arange(S), np.diff(prp))
+        for j in rng.choice(S, 4, replace=False):
+            krows = sorted(set(rows_of[ci == j].tolist()))
+            if not krows:
+                continue
+            _, rdk, rdv = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci, dof, 64, rows=krows, O=of)
+            tok = src[j * 64:(j + 1) * 64]
+            got["dk"].append(grads[1][0, h, tok])
+            ref["dk"].append(rdk[0, 0, j * 64:(j + 1) * 64])
+            got["dv"].append(grads[2][0, h, tok])
+            ref["dv"].append(rdv[0, 0, j * 64:(j + 1) * 64])
+    res = [grad_errors(np.stack(got[n]), np.stack(ref[n]), cfg.dtype, n) for n in ("dq", "dk", "dv")]
+    msg = "; ".join(m for _, m in res)
+    print(msg)
+    assert all(ok for ok, _ in res), msg

@@ -190,3 +190,30 @@ def test_fullsize_group_mask_and_sampled_attention(ci, heads, n_rows):
             assert np.abs(lse_h[0, h, tok] - LSE[0, 0, i * 64:(i + 1) * 64]).max() < 2e-3
     print(f"cfg{ci} (B=1): group density={rp[-1] / cfg.rows / SG:.4f} (rows {cfg.rows // cfg.batch}), "
           f"heads {heads}: mismatches={tot_mis} band={tot_band}")
+
+
+def test_group_mask_at_the_largest_row():
+    """One head with L/4 = 32768 groups (32 x 64 x 64 tokens, S = 2048): the group
+    select's LDS row buffer is exactly full."""
+    cfg = Config(96, "groups-max", "bf16", 1, 1, 32, 64, 64, 128, 8, 64, 0.2, None, 3.0, seed=19)
+    assert cfg.L // G == 32768
+    inputs = make_inputs(cfg)
+    g = grid_of(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    mask = bsa.build_group_mask(q, k, g, cfg.thr)
+    o, lse = bsa.forward_groups(q, k, v, mask, g, return_lse=True)
+    torch.cuda.synchronize()
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    ref = groups.head_group_mask(inputs["q"][0, 0][src], inputs["k"][0, 0][src], 64, G, cfg.thr)
+    n_mis, n_band = compare_masks(rp, ci, ref, cfg.thr, cfg.L // G)
+    del ref
+    rows = [0, 1, 777, 2047]
+    qf, kf, vf = (inputs[n][:, :, src] for n in "qkv")
+    O, LSE = groups.group_attention(qf, kf, vf, rp, ci, 64, G, rows=rows)
+    o_h = to_host_f64(o)
+    for i in rows:
+        tok = src[i * 64:(i + 1) * 64]
+        compare_outputs(o_h[0, 0, tok], O[0, 0, i * 64:(i + 1) * 64], "bf16", what=f"row {i}")
+    print(f"groups-max: kept {rp[-1]} of {2048 * 32768}, mismatches={n_mis} band={n_band}")

@@ -166,3 +166,57 @@ def test_sip_thr_zero_is_dense():
     o = bsa.forward(q, k, v, mask, g)
     O, _ = oracle.dense_attention(inputs["q"], inputs["k"], inputs["v"])
     compare_outputs(to_host_f64(o), O, "bf16")
+
+
+def test_sip_fullsize_heads_and_sampled_attention():
+    """The HunyuanVideo-scale hybrid workload in the benchmark's launch
+    configuration (B = 2, 24 heads, window, one call): the whole SIP mask is built
+    on the GPU, three heads (local, diffuse, second batch item) are compared with
+    the oracle's sampling on the GPU's CDF budgets, and sampled rows of the
+    shifted attention with the oracle."""
+    cfg = get_config(4)
+    inputs = make_inputs(cfg)
+    g = grid_of(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    for n in ("q_bits", "k_bits", "v_bits"):
+        inputs.pop(n)
+    seed = 77
+    cdf = bsa.build_mask(q, k, g, cfg.thr, None)
+    mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window, sip_seed=seed)
+    o, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+    torch.cuda.synchronize()
+    S = cfg.S
+    budget = np.diff(cdf.row_ptr.cpu().numpy())
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    wmask = oracle.sta_window(cfg.T, cfg.H // cfg.patch, cfg.W // cfg.patch, cfg.window)
+    o_h = to_host_f64(o)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(4)
+    for b, h in ((0, 0), (0, 20), (1, 5)):
+        bh = b * cfg.heads + h
+        r0 = bh * S
+        lo, hi = int(rp[r0]), int(rp[r0 + S])
+        ci = mask.col_idx[lo:hi].cpu().numpy()
+        sh = mask.shift[lo:hi].cpu().numpy().astype(np.float64)
+        prp = rp[r0:r0 + S + 1] - lo
+        got = csr_to_keep(prp, ci, S)
+        A = oracle.head_mask(inputs["q"][b, h][src], inputs["k"][b, h][src], 64, cfg.thr)["A"]
+        u = sip.uniforms(np.arange(r0, r0 + S), S, seed)
+        keep_ref, shift_ref = sip.build_sip_mask(A, budget[r0:r0 + S], u, cfg.thr, wmask)
+        pi = np.stack([sip.inclusion_probabilities(A[i], int(budget[r0 + i])) for i in range(S)])
+        band = (np.abs(u - pi) <= U_BAND) & ~wmask
+        diff = got != keep_ref
+        assert not (diff & ~band).any(), f"head {(b, h)}: {int((diff & ~band).sum())} blocks differ outside the band"
+        rows = np.repeat(np.arange(S), np.diff(prp))
+        both = keep_ref[rows, ci]
+        assert np.abs(sh[both] - shift_ref[rows[both], ci[both]]).max(initial=0.0) <= 1e-5 * max(1.0, shift_ref.max())
+        # sampled rows of the shifted attention
+        qf, kf, vf = (inputs[n][b:b + 1, h:h + 1][:, :, src] for n in "qkv")
+        sample = sorted(set(rng.choice(S, 6, replace=False).tolist()) | {0, S - 1})
+        O, LSE = sip.shifted_block_sparse_attention(qf, kf, vf, prp, ci, sh, 64, rows=sample)
+        for i in sample:
+            tok = src[i * 64:(i + 1) * 64]
+            compare_outputs(o_h[b, h, tok], O[0, 0, i * 64:(i + 1) * 64], "bf16", what=f"head {(b, h)} row {i}")
+            assert np.abs(lse_h[b, h, tok] - LSE[0, 0, i * 64:(i + 1) * 64]).max() < 2e-3
+        print(f"head {(b, h)}: kept {int(got.sum())}, differing in band {int(diff.sum())}")
