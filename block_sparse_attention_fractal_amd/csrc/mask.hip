@@ -18,73 +18,94 @@
 namespace bsa {
 
 // ---------------------------------------------------------------------------
-// Block logits: z[bh][i][j] = (qp_i . kp_j) / sqrt(D), float64 GEMM per head.
-// 128 x 128 output tile per 256-thread workgroup, 8 x 8 per thread, k chunks
-// of 16 staged in LDS k-major.  Each thread owns rows/cols 32c + 2t + {0,1}
-// (c = 0..3), so its LDS operand reads are 16-byte loads at a 16-byte lane
-// stride (no bank conflicts).
-// ---------------------------------------------------------------------------
+// Block logits: z[bh][i][j] = (qp_i . kp_j) / sqrt(D), float64 GEMM per head on
+// the float64 matrix cores (v_mfma_f64_16x16x4f64: A[i][k] in lane 16k + i,
+// B[k][j] in lane 16k + j, C[i][j] in lane 16(i % 4) + j, register i / 4).
+// 128 x 128 output tile per 256-thread workgroup, each wave a 64 x 64 quarter
+// (4 x 4 MFMA tiles); k chunks of 16 staged in LDS k-major (so the 16 lanes of a
+// fragment read 128 contiguous bytes), double-buffered: the next chunk is read
+// into registers while the current one is multiplied.
 // The same kernel serves the key-group map: Sk key columns per head (S for
 // blocks, L/4 for 4-token groups) and heads h0 .. h0 + gridDim.z - 1, with z
 // holding only those heads' rows.
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
-__global__ void __launch_bounds__(256) block_logits_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
+__global__ void __launch_bounds__(256, 2) block_logits_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
                                                            double* __restrict__ z, int Sq, int Sk, int64_t h0,
                                                            double inv_sqrt_d) {
   constexpr int TM = 128, KC = 16;
-  __shared__ __attribute__((aligned(16))) double As[KC][TM];
-  __shared__ __attribute__((aligned(16))) double Bs[KC][TM];
+  __shared__ __attribute__((aligned(16))) double As[2][KC][TM];
+  __shared__ __attribute__((aligned(16))) double Bs[2][KC][TM];
   const int64_t bh = h0 + blockIdx.z;
   const int i0 = blockIdx.y * TM, j0 = blockIdx.x * TM;
   const double* qh = qp + (size_t)bh * Sq * D;
   const double* kh = kp + (size_t)bh * Sk * D;
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  double acc[8][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;   // this wave's quarter of the tile
+  const int fi = lane & 15, fk = lane >> 4;                 // fragment row/col and k of this lane
+  f64x4 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
-  // loader: row lr = tid >> 1, k half lk = (tid & 1) * 8
+    for (int n = 0; n < 4; ++n) acc[m][n] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  // loader: row lr = tid >> 1, k half lk = (tid & 1) * 8; the next chunk is read
+  // into registers while the current one is multiplied out of the other buffer
   const int lr = tid >> 1, lk = (tid & 1) * 8;
-  for (int k0 = 0; k0 < D; k0 += KC) {
-    {
-      const int gi = i0 + lr, gj = j0 + lr;
+  const int gi = i0 + lr, gj = j0 + lr;
+  const double* qrow = qh + (size_t)min(gi, Sq - 1) * D + lk;
+  const double* krow = kh + (size_t)min(gj, Sk - 1) * D + lk;
+  double ra[8], rb[8];
+  auto fetch = [&](int k0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        As[lk + e][lr] = gi < Sq ? qh[(size_t)gi * D + k0 + lk + e] : 0.0;
-        Bs[lk + e][lr] = gj < Sk ? kh[(size_t)gj * D + k0 + lk + e] : 0.0;
-      }
+    for (int e = 0; e < 8; ++e) {
+      ra[e] = gi < Sq ? qrow[k0 + e] : 0.0;
+      rb[e] = gj < Sk ? krow[k0 + e] : 0.0;
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      double a[8], b[8];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double2 av = *(const double2*)&As[kk][32 * c + 2 * ty];
-        const double2 bv = *(const double2*)&Bs[kk][32 * c + 2 * tx];
-        a[2 * c] = av.x; a[2 * c + 1] = av.y;
-        b[2 * c] = bv.x; b[2 * c + 1] = bv.y;
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-#pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] = __fma_rn(a[x], b[y], acc[x][y]);
+    for (int e = 0; e < 8; ++e) {
+      As[buf][lk + e][lr] = ra[e];
+      Bs[buf][lk + e][lr] = rb[e];
     }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int c = 0; c < D / KC; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < D / KC) fetch((c + 1) * KC);
+#pragma unroll
+    for (int kk = 0; kk < KC; kk += 4) {
+      double a[4], b[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] = As[buf][kk + fk][wr + 16 * m + fi];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) b[n] = Bs[buf][kk + fk][wc + 16 * n + fi];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+    if (c + 1 < D / KC) stash(buf ^ 1);
     __syncthreads();
   }
   double* zh = z + (size_t)blockIdx.z * Sq * Sk;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int gi = i0 + 32 * (x >> 1) + 2 * ty + (x & 1);
-    if (gi >= Sq) continue;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int y = 0; y < 8; ++y) {
-      const int gj = j0 + 32 * (y >> 1) + 2 * tx + (y & 1);
-      if (gj < Sk) zh[(size_t)gi * Sk + gj] = acc[x][y] * inv_sqrt_d;
+    for (int r = 0; r < 4; ++r) {
+      const int gi = i0 + wr + 16 * m + 4 * r + fk;
+      if (gi >= Sq) continue;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int gj = j0 + wc + 16 * n + fi;
+        if (gj < Sk) zh[(size_t)gi * Sk + gj] = acc[m][n][r] * inv_sqrt_d;
+      }
     }
-  }
 }
 
 hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
