@@ -667,7 +667,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     double pmax = 0.0;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      p[k] = lane + 64 * k < S ? block_prob(zr[lane + 64 * k], m, sum) : 0.0;   // the compaction's formula
+      p[k] = lane + 64 * k < S ? block_prob(zr[lane + 64 * k], m, sum) : 0.0;
       pos += p[k] > 0.0;
       pmax = fmax(pmax, p[k]);
     }
@@ -714,8 +714,15 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     for (int k = 0; k < NS; ++k) {
       const int j = lane + 64 * k;
       if (j < S) {
-        const double u = (double)(philox4x64_w0((uint64_t)r, (uint64_t)j, seed) >> 11) * 0x1p-53;
-        if (u < (j == top ? 1.0 : incl_prob(p[k], c))) set_bit(j);
+        // u in [0, 1): pi >= 1 is always taken and pi == 0 never, so the draw is
+        // only made where it can decide
+        const double pi = j == top ? 1.0 : incl_prob(p[k], c);
+        if (pi >= 1.0) {
+          set_bit(j);
+        } else if (pi > 0.0) {
+          const double u = (double)(philox4x64_w0((uint64_t)r, (uint64_t)j, seed) >> 11) * 0x1p-53;
+          if (u < pi) set_bit(j);
+        }
       }
     }
   }
@@ -886,8 +893,8 @@ hipError_t launch_compact(const Geom& g, const uint32_t* bitmap, int words, cons
 }
 
 // The same compaction for a SIP mask, which also writes each entry's logit shift
-// log(1 / pi), pi recomputed from the row's (max, sum, c) exactly as sip_kernel
-// computed it; window blocks and thr == 0 rows carry shift 0.
+// log(1 / pi) from the row's (max, sum, c); window blocks, the top block and
+// thr == 0 rows carry shift 0.
 __global__ void __launch_bounds__(256) compact_sip_kernel(const uint32_t* __restrict__ bitmap, int words,
                                                           const int32_t* __restrict__ row_ptr,
                                                           int32_t* __restrict__ col_idx, float* __restrict__ shift,
@@ -902,6 +909,9 @@ __global__ void __launch_bounds__(256) compact_sip_kernel(const uint32_t* __rest
   const uint32_t* bm = bitmap + r * words;
   const double m = rowstat[4 * r], sum = rowstat[4 * r + 1], c = rowstat[4 * r + 2];
   const int top = (int)rowstat[4 * r + 3];
+  // -log(min(1, c * exp(z - m) / sum)) = max(0, log(sum) - log(c) - (z - m)): one log pair
+  // per row instead of an exp and a log per entry (c = inf gives 0: every block certain)
+  const double lsc = log(sum) - log(c);
   int32_t base = row_ptr[r];
   for (int j0 = 0; j0 < S; j0 += 64) {
     const int j = j0 + lane;
@@ -913,7 +923,7 @@ __global__ void __launch_bounds__(256) compact_sip_kernel(const uint32_t* __rest
       col_idx[slot] = j;
       float sh = 0.f;
       if (thr != 0.0 && j != top && !(win_t >= 0 && in_window(g, i, j, win_t, win_h, win_w)))
-        sh = (float)(-log(incl_prob(block_prob(z[r * S + j], m, sum), c)));
+        sh = (float)fmax(0.0, lsc - (z[r * S + j] - m));
       shift[slot] = sh;
     }
     base += __popcll(mask);
