@@ -127,7 +127,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];   // double-buffered K + V^T
   __shared__ int s_item;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its derived LDS offsets stay scalar
   const int h = lane >> 5, l32 = lane & 31;
   const int qb = wave >> 1;      // which block of the pair
   const int wq = wave & 1;       // which 32 queries of that block
@@ -293,12 +294,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
-        float m3[8];
+        // tile max as a tree of three-input maxima (16 instructions for 32 values)
+        float m10[11];
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          m3[x] = fmaxf(fmaxf(sacc[x >> 2][4 * (x & 3)], sacc[x >> 2][4 * (x & 3) + 1]),
-                        fmaxf(sacc[x >> 2][4 * (x & 3) + 2], sacc[x >> 2][4 * (x & 3) + 3]));
-        float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])), fmaxf(fmaxf(m3[4], m3[5]), fmaxf(m3[6], m3[7])));
+        for (int x = 0; x < 10; ++x) {
+          const int a0 = 3 * x, a1 = 3 * x + 1, a2 = 3 * x + 2;
+          m10[x] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
+        }
+        m10[10] = fmaxf(sacc[1][14], sacc[1][15]);
+        const float mA = fmaxf(fmaxf(m10[0], m10[1]), m10[2]), mB = fmaxf(fmaxf(m10[3], m10[4]), m10[5]);
+        const float mC = fmaxf(fmaxf(m10[6], m10[7]), m10[8]);
+        float mx = fmaxf(fmaxf(mA, mB), fmaxf(fmaxf(mC, m10[9]), m10[10]));
         mx = pair_max(mx) * c_log2 + shl;
         if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
           const float m_new = fmaxf(m_ref, mx);
