@@ -51,6 +51,7 @@ namespace bsa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
 struct AttnBf16Args {
@@ -148,6 +149,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     const int lv = (lane & 7) ^ ((d >> 1) & 7);
     voff[u] = d * 128 + lv * 16;
   }
+
+  // LDS addresses of this lane's MFMA operands in stage 0: the row term of the
+  // swizzle is the same for both key halves (K) and all four row blocks (V^T), so
+  // a K read is kaddr[s] plus an immediate and a V^T read vaddr[s] plus one
+  uint32_t kaddr[8], vaddr[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + k_lds(l32, 2 * s + h));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) vaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + v_lds(l32, 2 * s + h));
+  // opaque to the optimiser: otherwise it splits each address back into the array
+  // base (a relocated symbol, so never an immediate) plus the offset, and adds the
+  // two before every read
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kaddr[s]));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(vaddr[s]));
 
   // this workgroup's XCD and its item range (balanced by cumulative kept tiles)
   const int xcd = blockIdx.x & 7;
@@ -290,7 +307,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const bf16x8 ak = *(const bf16x8*)(st + k_lds(32 * t + l32, 2 * s + h));
+            const bf16x8 ak = *(lds_bf16x8*)(kaddr[s] + stage * kStage + t * 8192);
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
@@ -330,7 +347,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const bf16x8 av = *(const bf16x8*)(st + v_lds(32 * u + l32, 2 * s + h));
+            const bf16x8 av = *(lds_bf16x8*)(vaddr[s] + stage * kStage + u * 4096);
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
           }
         }
