@@ -74,6 +74,10 @@ struct AttnBf16Args {
 constexpr int kD = 128;
 constexpr int kStage = 32768;          // one K tile (16 KB) + one V^T tile (16 KB)
 constexpr int kVt = 16384;             // V^T offset inside a stage
+constexpr int kTile = 16384;           // one K or V^T tile
+constexpr int kVRing = 3 * kTile;      // K ring: 3 slots at 0; V^T ring: 2 slots from here
+constexpr int kLds = 5 * kTile;        // 80 KB: two workgroups fill a CU's 160 KB
+constexpr int kItemSlot = kLds - 4;    // the item index, only live between items (last word of V^T slot 1)
 constexpr float kLazy = 8.0f;          // log2 slack before the reference max is raised
 
 // K tile: 64 rows x 256 B, 16-byte chunk c of row k stored at chunk c ^ (k & 15).
@@ -125,8 +129,8 @@ __device__ __forceinline__ int64_t item_cost_prefix(const AttnBf16Args& a, int64
 
 template <bool kShift>   // whether the CSR carries per-entry logit shifts
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];   // double-buffered K + V^T
-  __shared__ int s_item;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // K ring (3 slots) + V^T ring (2 slots)
+  int& s_item = *(int*)(smem + kItemSlot);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its derived LDS offsets stay scalar
@@ -157,7 +161,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) kaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + k_lds(l32, 2 * s + h));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) vaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + v_lds(l32, 2 * s + h));
+  for (int s = 0; s < 4; ++s) vaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + kVRing - kVt + v_lds(l32, 2 * s + h));
   // opaque to the optimiser: otherwise it splits each address back into the array
   // base (a relocated symbol, so never an immediate) plus the offset, and adds the
   // two before every read
@@ -216,6 +220,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         wa_base = pa;
         wa = wa_base + lane < ea ? a.col_idx[wa_base + lane] : 0x7fffffff;
         sa = shift_at(wa_base + lane, ea);
+        // wait here, on the rare refill path, so that no path reaches the readlane
+        // below with a load pending (the compiler would otherwise wait for every
+        // outstanding load, tile loads included, before each readlane)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       }
       return __builtin_amdgcn_readlane(wa, pa - wa_base);
     };
@@ -225,6 +233,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         wb_base = pb;
         wb = wb_base + lane < eb ? a.col_idx[wb_base + lane] : 0x7fffffff;
         sb = shift_at(wb_base + lane, eb);
+        // wait here, on the rare refill path, so that no path reaches the readlane
+        // below with a load pending (the compiler would otherwise wait for every
+        // outstanding load, tile loads included, before each readlane)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       }
       return __builtin_amdgcn_readlane(wb, pb - wb_base);
     };
@@ -252,18 +264,31 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, g.L * kD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)vth, (short)0, g.S * kD * 64 * 2, 0x00020000);
-    auto issue = [&](int j, auto stage_c) {
-      constexpr int stage = decltype(stage_c)::value;
-      const int jc = min(max(j, 0), g.S - 1);     // malformed ids stay in bounds
+    // a tile id past the end of the walk is clamped: every step issues exactly
+    // four K and four V^T loads per thread, which keeps the vmcnt arithmetic exact
+    auto issue_k = [&](int j, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      const int jc = min(max(j, 0), g.S - 1);
       const int ks = block_base_row(a, jc) * kD * 2;
-      const int vs = jc * kD * 64 * 2;
-      uint8_t* st = smem + stage * kStage;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + (4 * wave + u) * 1024), 16, koff[u], ks, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kVt + (4 * wave + u) * 1024), 16, voff[u], vs,
-                                                 0, 0);
-      }
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * kTile + (4 * wave + u) * 1024), 16,
+                                                 koff[u], ks, 0, 0);
+    };
+    auto issue_v = [&](int j, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      const int jc = min(max(j, 0), g.S - 1);
+      const int vs = jc * kD * 64 * 2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + kVRing + slot * kTile + (4 * wave + u) * 1024),
+                                                 16, voff[u], vs, 0, 0);
+    };
+    // wait for this thread's older loads, then a plain barrier (the compiler's own
+    // barrier would first wait for every outstanding load, including the ones
+    // meant to stay in flight); lgkmcnt(0) keeps LDS writes ordered as well
+    auto wait_barrier4 = [&]() {
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
     bf16x8 qreg[8];
@@ -280,26 +305,32 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
     float m_ref = -INFINITY, l_run = 0.f;
 
-    int j;
-    bool ka, kb;
-    float shl;
+    // tiles j (current), j1, j2: K of a tile is loaded two steps ahead of its QK
+    // products, V^T one step ahead (issued first, so a step's wait can leave the
+    // newest K in flight)
+    int j, j1, j2;
+    bool ka, kb, ka1, kb1, ka2, kb2;
+    float shl, shl1, shl2;
     next_tile(j, ka, kb, shl);
-    if (j != 0x7fffffff) issue(j, std::integral_constant<int, 0>{});
-    // one tile: publish stage `stage`, prefetch the next tile into the other
-    // stage, then both contractions and the softmax update; the loop is unrolled
-    // twice so every LDS address is a per-lane constant plus an immediate
-    auto step = [&](auto stage_c) {
-      constexpr int stage = decltype(stage_c)::value;
-      int jn;
-      bool kan, kbn;
-      float shln;
-      next_tile(jn, kan, kbn, shln);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (jn != 0x7fffffff) issue(jn, std::integral_constant<int, stage ^ 1>{});
+    next_tile(j1, ka1, kb1, shl1);
+    issue_v(j, std::integral_constant<int, 0>{});
+    issue_k(j, std::integral_constant<int, 0>{});
+    issue_k(j1, std::integral_constant<int, 1>{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // one tile in K slot KS = j % 3 and V^T slot VS = j % 2: QK and the softmax
+    // update, then (after V^T is everywhere) PV; the loop is unrolled six times so
+    // every LDS address is a per-lane constant plus an immediate
+    auto step = [&](auto ks_c, auto vs_c) {
+      constexpr int KS = decltype(ks_c)::value;
+      constexpr int VS = decltype(vs_c)::value;
+      next_tile(j2, ka2, kb2, shl2);
+      wait_barrier4();                                        // K(j) and V(j) resident everywhere
+      issue_v(j1, std::integral_constant<int, VS ^ 1>{});     // into the slot V(j-1) used
+      issue_k(j2, std::integral_constant<int, (KS + 2) % 3>{});   // into the slot K(j-1) used
       const bool mine = qb == 0 ? ka : kb;
+      bf16x8 pbv[4];
       if (mine) {
-        const uint8_t* st = smem + stage * kStage;
         f32x16 sacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -307,7 +338,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const bf16x8 ak = *(lds_bf16x8*)(kaddr[s] + stage * kStage + t * 8192);
+            const bf16x8 ak = *(lds_bf16x8*)(kaddr[s] + KS * kTile + t * 8192);
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
@@ -333,7 +364,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
         }
-        bf16x8 pbv[4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -347,21 +377,31 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const bf16x8 av = *(lds_bf16x8*)(vaddr[s] + stage * kStage + u * 4096);
+            const bf16x8 av = *(lds_bf16x8*)(vaddr[s] + VS * kTile + u * 4096);
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
           }
         }
       }
-      j = jn;
-      ka = kan;
-      kb = kbn;
-      shl = shln;
+      j = j1; ka = ka1; kb = kb1; shl = shl1;
+      j1 = j2; ka1 = ka2; kb1 = kb2; shl1 = shl2;
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     while (j != 0x7fffffff) {
-      step(std::integral_constant<int, 0>{});
+      step(I0{}, I0{});
       if (j == 0x7fffffff) break;
-      step(std::integral_constant<int, 1>{});
+      step(I1{}, I1{});
+      if (j == 0x7fffffff) break;
+      step(I2{}, I0{});
+      if (j == 0x7fffffff) break;
+      step(I0{}, I1{});
+      if (j == 0x7fffffff) break;
+      step(I1{}, I0{});
+      if (j == 0x7fffffff) break;
+      step(I2{}, I1{});
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the clamped loads past the end have landed
 
     // epilogue: normalise, stage O through LDS (block qb at qb * 16 KB), store coalesced
     __syncthreads();
