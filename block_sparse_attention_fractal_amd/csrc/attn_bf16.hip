@@ -72,7 +72,6 @@ struct AttnBf16Args {
 };
 
 constexpr int kD = 128;
-constexpr int kStage = 32768;          // one K tile (16 KB) + one V^T tile (16 KB)
 constexpr int kVt = 16384;             // V^T offset inside a stage
 constexpr int kTile = 16384;           // one K or V^T tile
 constexpr int kVRing = 3 * kTile;      // K ring: 3 slots at 0; V^T ring: 2 slots from here
@@ -338,7 +337,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const bf16x8 ak = *(lds_bf16x8*)(kaddr[s] + KS * kTile + t * 8192);
+            const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * 8192);
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
@@ -377,7 +376,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const bf16x8 av = *(lds_bf16x8*)(vaddr[s] + VS * kTile + u * 4096);
+            const bf16x8 av = *(lds_bf16x8*)(uintptr_t)(vaddr[s] + VS * kTile + u * 4096);
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
           }
         }

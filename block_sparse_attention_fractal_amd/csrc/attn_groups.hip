@@ -19,9 +19,18 @@
 //     buffer load per wave (lane -> row lane/16, chunk lane%16, swizzled
 //     chunk c ^ (row & 15)); a V slot is the group's 128 x 4 transposed block
 //     of the prepared V (1 KB, contiguous), also one load;
-//   * S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16; the V^T
-//     operand of a lane is two 8-byte LDS reads (4 keys of one channel from each
-//     of two groups), in exactly the key order P leaves the S^T accumulator.
+//   * LDS holds a ring of three K tiles and a ring of two V tiles (80 KB): at
+//     step t the workgroup issues V of tile t+1 and then K of tile t+2, so one
+//     wait for all but the newest four loads and one barrier per tile make
+//     tile t resident while two more are in flight; the group ids of tile t+3
+//     are loaded at step t (older than that step's tile loads, so the same
+//     wait covers them);
+//   * S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16.  The V tile
+//     stores the group of tile entry e at slot e with bits 0 and 1 swapped, so
+//     the two 4-key halves of a lane's V^T operand (entries 8(w>>1) + 4s + h and
+//     that + 2) sit in neighbouring slots: two 8-byte LDS reads land directly in
+//     the operand registers, in exactly the key order P leaves the S^T
+//     accumulator.
 #include <math.h>
 
 #include "kernels.h"
@@ -32,10 +41,18 @@ namespace grp {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// volatile: each 8-byte V read stays a read of its own (the compiler would pair
+// neighbouring reads of one operand half and then copy the halves together)
+typedef __attribute__((address_space(3))) const volatile u32x2 lds_u2;
 
 constexpr int kD = 128;
-constexpr int kStage = 32768;     // 16 K slots (16 KB) + 16 V slots (16 KB)
-constexpr int kVOff = 16384;
+constexpr int kTile = 16384;      // 16 slots of 1 KB: one K or one V tile
+constexpr int kVRing = 3 * kTile;  // K ring: 3 tiles at 0; V ring: 2 tiles from here
+constexpr int kLds = 5 * kTile;    // 80 KB: two workgroups fill a CU's 160 KB
+constexpr int kItemSlot = kLds - 4;     // the item index, only live between items (last word of V slot 1)
 constexpr float kLazy = 8.0f;
 
 struct Args {
@@ -49,8 +66,9 @@ struct Args {
   int32_t* counters;
   Geom g;
   float c_log2;
-  uint32_t magic_wp, magic_hp;
-  int32_t groups;          // L / 4 per head
+  uint32_t magic_wp, magic_hp;   // fractal order: magic_wp = 0
+  int32_t pxmul, rs;             // row offset of patch column px (8 or 64) and of patch row m / 8 (W or 8)
+  int32_t groups;                // L / 4 per head
 };
 
 __device__ __forceinline__ int k_lds(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
@@ -84,16 +102,24 @@ __device__ __forceinline__ int block_base_row(const Args& a, int j) {
 }
 // First row of group gid: tokens 4(gid % 16) .. +3 of block gid / 16, which sit
 // in one patch row (P = 8), so the group's 4 rows are consecutive in memory.
+// Written without a branch on the layout: in fractal order the host passes
+// magic_wp = 0 (so the patch coordinates beyond px vanish), pxmul = 64, rs = 8.
 __device__ __forceinline__ int group_base_row(const Args& a, int gid) {
-  if (a.g.layout == 1) return gid * 4;
-  return block_base_row(a, gid >> 4) + ((gid & 15) >> 1) * a.g.W + (gid & 1) * 4;
+  const Geom& g = a.g;
+  const int j = gid >> 4;
+  const int rest = (int)div_magic((uint32_t)j, a.magic_wp);
+  const int px = j - rest * g.Wp;
+  const int t = (int)div_magic((uint32_t)rest, a.magic_hp);
+  const int py = rest - t * g.Hp;
+  return (t * g.H + py * 8) * g.W + px * a.pxmul + ((gid & 15) >> 1) * a.rs + (gid & 1) * 4;
 }
 
 __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  __shared__ int s_item;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // K ring (3 tiles) + V ring (2 tiles)
+  int& s_item = *(int*)(smem + kItemSlot);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int wq = wave & 1;       // which 32 queries
   const int kh = wave >> 1;      // which 8 slots (32 keys) of every tile
@@ -110,6 +136,16 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
     const int lc = (lane & 15) ^ (row & 15);
     koff[u] = (lane >> 4) * kD * 2 + lc * 16;
   }
+  // LDS addresses of this lane's operands in ring slot 0 (reads add an immediate);
+  // opaque to the optimiser, which would otherwise split each back into the
+  // array base plus an offset and add the two before every read
+  uint32_t kaddr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + k_lds(32 * kh + l32, 2 * s + h));
+  uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void*)(smem + kVRing + (8 * kh + 2 * h) * 1024 + l32 * 8);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kaddr[s]));
+  asm volatile("" : "+v"(vaddr));
 
   const int xcd = blockIdx.x & 7;
   const int64_t items = g.rows;
@@ -144,25 +180,37 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.vg + (size_t)bh * g.L * kD), (short)0, g.L * kD * 2, 0x00020000);
 
-    // 64 group ids (4 tiles) per window, one per lane; entries past the row's end
-    // repeat its last group (their keys are masked)
-    int win_c = -1, win = 0;
-    auto issue = [&](int t, auto stage_c) {
-      constexpr int stage = decltype(stage_c)::value;
-      if ((t >> 2) != win_c) {
-        win_c = t >> 2;
-        win = a.col_idx[min(p0 + 64 * win_c + lane, e0 - 1)];
-      }
-      uint8_t* st = smem + stage * kStage;
+    // The row's group ids through a buffer over its own entries: lane l holds entry
+    // 16t + l % 16 of tile t, and entries past the row's end read as group 0 (those
+    // keys are masked, and tiles past the end are loaded but never read)
+    const __amdgpu_buffer_rsrc_t grs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + p0), (short)0, ng * 4, 0x00020000);
+    const int goff = (lane & 15) * 4;
+    auto gids_of = [&](int t) { return __builtin_amdgcn_raw_buffer_load_b32(grs, goff, 64 * t, 0); };
+    // this wave's four group ids of a tile, as scalars
+    struct Ids { int v[4]; };
+    auto ids_of = [&](int gl) {
+      Ids r;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int slot = 4 * wave + u;
-        const int gid = min(max(__builtin_amdgcn_readlane(win, 16 * (t & 3) + slot), 0), a.groups - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + slot * 1024), 16, koff[u],
-                                                 group_base_row(a, gid) * kD * 2, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + kVOff + slot * 1024), 16, lane * 16,
-                                                 gid * 1024, 0, 0);
-      }
+      for (int u = 0; u < 4; ++u) r.v[u] = min(max(__builtin_amdgcn_readlane(gl, 4 * wave + u), 0), a.groups - 1);
+      return r;
+    };
+    auto issue_k = [&](const Ids& id, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * kTile + (4 * wave + u) * 1024), 16,
+                                                 koff[u], group_base_row(a, id.v[u]) * kD * 2, 0, 0);
+    };
+    auto issue_v = [&](const Ids& id, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + kVRing + slot * kTile + (4 * wave + u) * 1024),
+                                                 16, lane * 16, id.v[(u >> 1) | ((u & 1) << 1)] * 1024, 0, 0);
+    };
+    auto wait_barrier4 = [&]() {
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
     bf16x8 qreg[8];
@@ -179,69 +227,109 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
       for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
     float m_ref = -INFINITY, l_run = 0.f;
 
-    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-    auto step = [&](int t, auto stage_c) {
-      constexpr int stage = decltype(stage_c)::value;
+    if (ntiles > 0) {
+      // ids: tile t+1 as scalars (its V is issued at step t), tile t+2 in a VGPR
+      // (its K is issued at step t), tile t+3 loaded at step t
+      Ids s1 = ids_of(gids_of(1));
+      int g2 = gids_of(2);
+      {
+        const Ids s0 = ids_of(gids_of(0));
+        issue_v(s0, std::integral_constant<int, 0>{});
+        issue_k(s0, std::integral_constant<int, 0>{});
+      }
+      issue_k(s1, std::integral_constant<int, 1>{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, stage ^ 1>{});
-      const int nvalid = min(16, ng - 16 * t);
-      if (8 * kh < nvalid) {
-        const uint8_t* st = smem + stage * kStage;
-        f32x16 sacc;
+      int t = 0;
+      auto step = [&](auto ks_c, auto vs_c) {
+        constexpr int KS = decltype(ks_c)::value;
+        constexpr int VS = decltype(vs_c)::value;
+        wait_barrier4();                                   // K(t) and V(t) resident everywhere
+        const int g3 = gids_of(t + 3);                     // older than the tile loads below
+        const Ids s2 = ids_of(g2);
+        issue_v(s1, std::integral_constant<int, VS ^ 1>{});
+        issue_k(s2, std::integral_constant<int, (KS + 2) % 3>{});
+        const int nvalid = min(16, ng - 16 * t);
+        if (8 * kh < nvalid) {
+          // all eight K operand reads in flight before the first product
+          bf16x8 ak[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+          for (int s = 0; s < 8; ++s) ak[s] = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x16 sacc;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 ak = *(const bf16x8*)(st + k_lds(32 * kh + l32, 2 * s + h));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc, 0, 0, 0);
-        }
-        // register e holds key 8(e/4) + 4h + e%4 of this wave's 32, i.e. slot 8kh + 2(e/4) + h
-        if (nvalid < 16) {
+          for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (8 * kh + 2 * (e >> 2) + h >= nvalid) sacc[e] = -INFINITY;
-        }
-        float mx = sacc[0];
+          for (int s = 0; s < 8; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[s], qreg[s], sacc, 0, 0, 0);
+          // the V operands (keys 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3 of channel
+          // 32u + l32) are read while the softmax runs
+          u32x2 vlo[2][4], vhi[2][4];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-        mx = pair_max(mx) * c_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
-          const float m_new = fmaxf(m_ref, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-          m_ref = m_new;
-          l_run *= alpha;
+          for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 4; ++u) {
+              vlo[s][u] = *(lds_u2*)(uintptr_t)(vaddr + VS * kTile + s * 4096 + u * 256);
+              vhi[s][u] = *(lds_u2*)(uintptr_t)(vaddr + VS * kTile + s * 4096 + u * 256 + 1024);
+            }
+          // register e holds key 8(e/4) + 4h + e%4 of this wave's 32, i.e. slot 8kh + 2(e/4) + h
+          if (nvalid < 16) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
-        }
-        bf16x8 pbv[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -m_ref));
-          l_run += p;
-          pbv[e >> 3][e & 7] = (__bf16)p;
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int sa = kVOff + (8 * kh + 4 * s + h) * 1024;   // keys 16s + 4h + 0..3
-          const int sb = sa + 2 * 1024;                          // keys 16s + 8 + 4h + 0..3
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int d = 32 * u + l32;
-            const uint2 lo = *(const uint2*)(st + sa + d * 8);
-            const uint2 hi = *(const uint2*)(st + sb + d * 8);
-            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            const bf16x8 av = __builtin_bit_cast(bf16x8, w);
-            oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+            for (int e = 0; e < 16; ++e)
+              if (8 * kh + 2 * (e >> 2) + h >= nvalid) sacc[e] = -INFINITY;
           }
+          float m5[5];
+#pragma unroll
+          for (int x = 0; x < 5; ++x) m5[x] = fmaxf(fmaxf(sacc[3 * x], sacc[3 * x + 1]), sacc[3 * x + 2]);
+          float mx = fmaxf(fmaxf(fmaxf(m5[0], m5[1]), m5[2]), fmaxf(fmaxf(m5[3], m5[4]), sacc[15]));
+          mx = pair_max(mx) * c_log2;
+          if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
+          }
+          bf16x8 pbv[2];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -m_ref));
+            l_run += p;
+            pbv[e >> 3][e & 7] = (__bf16)p;
+          }
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bf16x8 av = __builtin_bit_cast(
+                  bf16x8, (u32x4){vlo[s][u].x, vlo[s][u].y, vhi[s][u].x, vhi[s][u].y});
+              oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+            }
         }
+        s1 = s2;
+        g2 = g3;
+        ++t;
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      for (;;) {
+        step(I0{}, I0{});
+        if (t >= ntiles) break;
+        step(I1{}, I1{});
+        if (t >= ntiles) break;
+        step(I2{}, I0{});
+        if (t >= ntiles) break;
+        step(I0{}, I1{});
+        if (t >= ntiles) break;
+        step(I1{}, I0{});
+        if (t >= ntiles) break;
+        step(I2{}, I1{});
+        if (t >= ntiles) break;
       }
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, std::integral_constant<int, 0>{});
-      if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the loads past the row's end have landed
     }
 
     // merge the two key halves of each query range, then normalise and store
@@ -359,8 +447,10 @@ hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, 
   a.counters = counters;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-  a.magic_wp = (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
   a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
+  a.pxmul = g.layout == 1 ? 64 : 8;
+  a.rs = g.layout == 1 ? 8 : g.W;
   a.groups = g.L / 4;
   const int grid = ((num_cu * 2 + 7) / 8) * 8;
   grp::attn_groups_bf16_kernel<<<grid, 256, 0, s>>>(a);
