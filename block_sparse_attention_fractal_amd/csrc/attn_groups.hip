@@ -195,12 +195,16 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
       for (int u = 0; u < 4; ++u) r.v[u] = min(max(__builtin_amdgcn_readlane(gl, 4 * wave + u), 0), a.groups - 1);
       return r;
     };
-    auto issue_k = [&](const Ids& id, auto slot_c) {
+    // byte offset of each lane's group in this head's K, computed by all lanes at
+    // once and read back per slot (cheaper than the same arithmetic on scalars
+    // for each of the wave's four slots)
+    auto kbytes_of = [&](int gl) { return group_base_row(a, min(max(gl, 0), a.groups - 1)) * kD * 2; };
+    auto issue_k = [&](int kb, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * kTile + (4 * wave + u) * 1024), 16,
-                                                 koff[u], group_base_row(a, id.v[u]) * kD * 2, 0, 0);
+                                                 koff[u], __builtin_amdgcn_readlane(kb, 4 * wave + u), 0, 0);
     };
     auto issue_v = [&](const Ids& id, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
@@ -229,15 +233,17 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
 
     if (ntiles > 0) {
       // ids: tile t+1 as scalars (its V is issued at step t), tile t+2 in a VGPR
-      // (its K is issued at step t), tile t+3 loaded at step t
-      Ids s1 = ids_of(gids_of(1));
+      // (its K offsets are computed and issued at step t), tile t+3 loaded at step t
+      const int g1v = gids_of(1);
+      Ids s1 = ids_of(g1v);
       int g2 = gids_of(2);
       {
-        const Ids s0 = ids_of(gids_of(0));
+        const int g0v = gids_of(0);
+        const Ids s0 = ids_of(g0v);
         issue_v(s0, std::integral_constant<int, 0>{});
-        issue_k(s0, std::integral_constant<int, 0>{});
+        issue_k(kbytes_of(g0v), std::integral_constant<int, 0>{});
       }
-      issue_k(s1, std::integral_constant<int, 1>{});
+      issue_k(kbytes_of(g1v), std::integral_constant<int, 1>{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       int t = 0;
@@ -248,7 +254,7 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
         const int g3 = gids_of(t + 3);                     // older than the tile loads below
         const Ids s2 = ids_of(g2);
         issue_v(s1, std::integral_constant<int, VS ^ 1>{});
-        issue_k(s2, std::integral_constant<int, (KS + 2) % 3>{});
+        issue_k(kbytes_of(g2), std::integral_constant<int, (KS + 2) % 3>{});
         const int nvalid = min(16, ng - 16 * t);
         if (8 * kh < nvalid) {
           // all eight K operand reads in flight before the first product
