@@ -67,6 +67,7 @@ struct AttnBf16Args {
   Geom g;
   float c_log2;        // log2(e) / sqrt(D)
   uint32_t magic_wp, magic_hp;   // floor(2^32/d)+1: exact n/d = (n*magic)>>32 for n, d < 2^16
+  int32_t pxmul;                 // rows per patch column step: 8 (original order) or 64 (fractal, magic_wp = 0)
   int32_t pairs;       // query-block pairs per head = ceil(S/2)
   int32_t items;       // B*heads*pairs
 };
@@ -109,12 +110,11 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic) {
 // Block ids and patch counts are < 2^16, so the divisions use multiply-high.
 __device__ __forceinline__ int block_base_row(const AttnBf16Args& a, int j) {
   const Geom& g = a.g;
-  if (g.layout == 1) return j * 64;
-  const int rest = (int)div_magic((uint32_t)j, a.magic_wp);
+  const int rest = (int)div_magic((uint32_t)j, a.magic_wp);   // 0 in fractal order (magic_wp = 0)
   const int px = j - rest * g.Wp;
   const int t = (int)div_magic((uint32_t)rest, a.magic_hp);
   const int py = rest - t * g.Hp;
-  return (t * g.H + py * 8) * g.W + px * 8;
+  return (t * g.H + py * 8) * g.W + px * a.pxmul;
 }
 
 // Cumulative kept tiles of the rows before item t (items ordered head-major).
@@ -241,12 +241,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     };
     // union walk over the two ascending key lists (wave-uniform scalars); shl is
     // the logit shift of this wave's block for the tile, in log2 units
-    auto next_tile = [&](int& j, bool& ka, bool& kb, float& shl) {
+    auto next_tile = [&](int& j, int& mine, float& shl) {
       const int ja = peek_a();
       const int jb = peek_b();
       j = min(ja, jb);
-      ka = ja == j;
-      kb = jb == j;
+      const bool ka = ja == j;
+      const bool kb = jb == j;
+      mine = qb == 0 ? (int)ka : (int)kb;   // an int: a bool carried across steps becomes a lane mask
       shl = 0.f;
       if (has_shift) {
         const float sha = ka ? __int_as_float(__builtin_amdgcn_readlane(sa, pa - wa_base)) : 0.f;
@@ -308,10 +309,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     // products, V^T one step ahead (issued first, so a step's wait can leave the
     // newest K in flight)
     int j, j1, j2;
-    bool ka, kb, ka1, kb1, ka2, kb2;
+    int m0, m1, m2;
     float shl, shl1, shl2;
-    next_tile(j, ka, kb, shl);
-    next_tile(j1, ka1, kb1, shl1);
+    next_tile(j, m0, shl);
+    next_tile(j1, m1, shl1);
     issue_v(j, std::integral_constant<int, 0>{});
     issue_k(j, std::integral_constant<int, 0>{});
     issue_k(j1, std::integral_constant<int, 1>{});
@@ -323,13 +324,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     auto step = [&](auto ks_c, auto vs_c) {
       constexpr int KS = decltype(ks_c)::value;
       constexpr int VS = decltype(vs_c)::value;
-      next_tile(j2, ka2, kb2, shl2);
+      next_tile(j2, m2, shl2);
       wait_barrier4();                                        // K(j) and V(j) resident everywhere
       issue_v(j1, std::integral_constant<int, VS ^ 1>{});     // into the slot V(j-1) used
       issue_k(j2, std::integral_constant<int, (KS + 2) % 3>{});   // into the slot K(j-1) used
-      const bool mine = qb == 0 ? ka : kb;
       bf16x8 pbv[4];
-      if (mine) {
+      if (m0) {
         f32x16 sacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -381,8 +381,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           }
         }
       }
-      j = j1; ka = ka1; kb = kb1; shl = shl1;
-      j1 = j2; ka1 = ka2; kb1 = kb2; shl1 = shl2;
+      j = j1; m0 = m1; shl = shl1;
+      j1 = j2; m1 = m2; shl1 = shl2;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -462,7 +462,8 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.counters = counters;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-  a.magic_wp = (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.pxmul = g.layout == 1 ? 64 : 8;
   a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
