@@ -18,7 +18,7 @@ BSA_ORDER_FRACTAL, BSA_ORDER_TILE_MAJOR, BSA_ORDER_HILBERT = 0, 1, 2
 
 # every symbol declared in include/bsa.h
 EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
-            "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_attend",
+            "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_query_attend_ws", "bsa_attend",
             "bsa_query_backward_ws", "bsa_backward", "bsa_query_group_sizes", "bsa_build_group_mask",
             "bsa_forward_groups", "bsa_prepare_v_groups", "bsa_attend_groups", "bsa_status_str", "bsa_last_error",
             "bsa_version"]
@@ -73,6 +73,7 @@ def lib():
     l.bsa_build_mask.argtypes = [P(Problem), P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
     l.bsa_forward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_prepare_v.argtypes = [P(Problem), vp, vp, vp]
+    l.bsa_query_attend_ws.argtypes = [P(Problem), P(i64)]
     l.bsa_attend.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_query_backward_ws.argtypes = [P(Problem), P(i64)]
     l.bsa_backward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, vp, i64, vp]
@@ -87,8 +88,8 @@ def lib():
     l.bsa_last_error.restype = ctypes.c_char_p
     l.bsa_version.argtypes = []
     for name in ("bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
-                 "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_attend",
-                 "bsa_query_backward_ws", "bsa_backward", "bsa_version"):
+                 "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_query_attend_ws",
+                 "bsa_attend", "bsa_query_backward_ws", "bsa_backward", "bsa_version"):
         getattr(l, name).restype = ctypes.c_int
     _lib = l
     return l

@@ -103,6 +103,13 @@ def backward_workspace_bytes(prob: _lib.Problem) -> int:
     return nbytes.value
 
 
+def attend_workspace_bytes(prob: _lib.Problem) -> int:
+    """Bytes of device workspace bsa_attend needs for this problem (work counters and order)."""
+    nbytes = ctypes.c_int64()
+    check(lib().bsa_query_attend_ws(ctypes.byref(prob), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes or ws.data_ptr() % 256:
@@ -256,7 +263,7 @@ def attend(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, 
         raise ValueError("vp must be a contiguous tensor with q's dtype and size")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    ws = _workspace(256, q.device, workspace)
+    ws = _workspace(attend_workspace_bytes(prob), q.device, workspace)
     csr = mask.as_struct()
     check(lib().bsa_attend(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), vp.data_ptr(), ctypes.byref(csr),
                            o.data_ptr(), lse.data_ptr() if lse is not None else None,

@@ -57,7 +57,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 300; }
+int bsa_version(void) { return 400; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -213,7 +213,7 @@ static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const
       !aligned(mask->shift, 4))
     return fail(BSA_ERR_INVALID_ARG, std::string(who) + ": misaligned pointer");
   const FwdWs w = fwd_ws_layout(*g);
-  const int64_t need = whole_forward ? w.total : w.vt;   // bsa_attend only uses the counter block
+  const int64_t need = whole_forward ? w.total : w.vt;   // bsa_attend: counters and work order only
   if (!ws || ws_bytes < need)
     return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(need) + " bytes");
   if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, std::string(who) + ": workspace must be 256-byte aligned");
@@ -229,14 +229,28 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
     const int st = current_cu_count(&ncu);
     if (st != BSA_OK) return st;
     int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
+    int32_t* bounds = reinterpret_cast<int32_t*>(ws + w.bounds);
+    int32_t* cost = reinterpret_cast<int32_t*>(ws + w.cost);
+    int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
     e = launch_zero_i32(counter, 8, stream);   // one work counter per XCD
+    if (e == hipSuccess) e = launch_attn_schedule(g, mask->row_ptr, mask->col_idx, cost, order, bounds, stream);
     if (e == hipSuccess)
-      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, ncu, stream);
+      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, order, bounds,
+                           ncu, stream);
   } else {
     e = launch_attn_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
                         mask->col_idx, mask->shift, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return BSA_OK;
+}
+
+int bsa_query_attend_ws(const bsa_problem* p, int64_t* attend_ws) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!attend_ws) return fail(BSA_ERR_INVALID_ARG, "bsa_query_attend_ws: null output");
+  *attend_ws = fwd_ws_layout(g).vt;
   return BSA_OK;
 }
 

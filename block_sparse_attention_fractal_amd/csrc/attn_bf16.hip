@@ -15,15 +15,17 @@
 //   * 256-thread workgroups: waves 0-1 own block i, waves 2-3 own block i+1,
 //     32 queries per wave, the Q operand held in registers;
 //   * persistent grid, two workgroups per CU; workgroup b runs on XCD b % 8 and
-//     pulls items from its XCD's own contiguous range (split by cumulative
-//     kept-tile count), so concurrently running items of one XCD share a head and
-//     its K/V tiles in that XCD's L2;
+//     pulls items from its XCD's own stretch of a work order built by two small
+//     kernels before it: the items are split into 8 contiguous ranges of about
+//     equal cost (distinct key blocks of the pair plus a fixed per-item cost),
+//     so concurrently running items of one XCD share a head and its K/V tiles in
+//     that XCD's L2, and each range runs its longest items first;
 //   * K (64 x 128) and V^T (128 x 64) tiles move global -> LDS with direct
-//     (VGPR-free) 16-byte buffer loads into a double buffer: the per-lane part
-//     of each address is a constant register, the tile part a scalar offset;
-//     the next tile's loads are issued right after the barrier that publishes
-//     the current one, and the loop is unrolled over the two stages so every
-//     LDS address is a per-lane constant plus an immediate;
+//     (VGPR-free) 16-byte buffer loads into a ring of three K and two V^T tiles:
+//     the per-lane part of each address is a constant register, the tile part a
+//     scalar offset; at step j the workgroup issues V^T of tile j+1 and K of
+//     tile j+2, and the loop is unrolled over the ring positions so every LDS
+//     address is a per-lane constant plus an immediate;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
 //     columns from registers): each lane's accumulator holds 32 keys of ONE
 //     query, so the online-softmax state is per lane;
@@ -41,6 +43,8 @@
 // pair "element e of half h" of A and B, so the physical k order inside the
 // instruction does not matter.
 #include <math.h>
+
+#include <algorithm>
 
 #include <type_traits>
 
@@ -64,6 +68,8 @@ struct AttnBf16Args {
   const int32_t* col_idx;
   const float* shift;  // per-entry natural-log logit shift, or null
   int32_t* counters;   // 8 per-XCD item counters
+  const int32_t* order;    // items in processing order: XCD x takes order[bounds[x] .. bounds[x+1])
+  const int32_t* bounds;   // 9 entries
   Geom g;
   float c_log2;        // log2(e) / sqrt(D)
   uint32_t magic_wp, magic_hp;   // floor(2^32/d)+1: exact n/d = (n*magic)>>32 for n, d < 2^16
@@ -117,15 +123,6 @@ __device__ __forceinline__ int block_base_row(const AttnBf16Args& a, int j) {
   return (t * g.H + py * 8) * g.W + px * a.pxmul;
 }
 
-// Cumulative kept tiles of the rows before item t (items ordered head-major).
-__device__ __forceinline__ int64_t item_cost_prefix(const AttnBf16Args& a, int64_t t) {
-  const int64_t bh = t / a.pairs;
-  const int64_t p = t - bh * a.pairs;
-  int64_t row = bh * a.g.S + 2 * p;
-  if (row > a.g.rows) row = a.g.rows;
-  return a.row_ptr[row];
-}
-
 template <bool kShift>   // whether the CSR carries per-entry logit shifts
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // K ring (3 slots) + V^T ring (2 slots)
@@ -169,28 +166,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(vaddr[s]));
 
-  // this workgroup's XCD and its item range (balanced by cumulative kept tiles)
+  // this workgroup's XCD and its stretch of the item order (the schedule kernels
+  // below balance the stretches by estimated cost and put long items first)
   const int xcd = blockIdx.x & 7;
-  const int64_t total = a.row_ptr[g.rows];
-  int64_t lo_t, hi_t;
-  {
-    auto first_item_with_cost = [&](int64_t target) {
-      int64_t lo = 0, hi = a.items;
-      while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (item_cost_prefix(a, mid + 1) > target) hi = mid; else lo = mid + 1;
-      }
-      return lo;
-    };
-    lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
-    hi_t = xcd == 7 ? a.items : first_item_with_cost(total * (xcd + 1) / 8);
-  }
+  const int lo_t = a.bounds[xcd], hi_t = a.bounds[xcd + 1];
 
   for (;;) {
-    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    if (tid == 0) s_item = lo_t + atomicAdd(&a.counters[xcd], 1);
     __syncthreads();
-    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= hi_t) break;
+    const int idx = __builtin_amdgcn_readfirstlane(s_item);
+    if (idx >= hi_t) break;
+    const int64_t item = a.order[idx];
     const int64_t bh = item / a.pairs;
     const int i0 = 2 * (int)(item - bh * a.pairs);
     const int64_t r0 = bh * g.S + i0;
@@ -447,9 +433,156 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work order.  An item's cost is the number of distinct key blocks its two query
+// blocks keep (the steps of its union walk) plus a fixed per-item cost.  The
+// order splits the items, in index order, into 8 ranges of about equal total
+// cost (one per XCD; splitting by kept tiles instead left the ranges of heads
+// with many short, less overlapping rows ~8 % longer) and starts each range with
+// its long items, so that the short ones fill the end (a long item started last
+// would otherwise decide when the kernel ends).
+// ---------------------------------------------------------------------------
+constexpr int kItemOverhead = 4;   // per-item cost in tile steps (Q load, ring prologue, output)
+constexpr int kMaxBitmapWords = 128;   // S <= 4096 blocks
+
+// cost[it] for every item: the pair's two key lists marked in an LDS bitmap and counted
+__global__ void __launch_bounds__(256) item_cost_kernel(const int32_t* __restrict__ row_ptr,
+                                                        const int32_t* __restrict__ col_idx, int S, int pairs,
+                                                        int items, int32_t* __restrict__ cost) {
+  __shared__ uint32_t bits[kMaxBitmapWords];
+  __shared__ int part[4];
+  const int tid = threadIdx.x;
+  const int words = (S + 31) >> 5;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int bh = it / pairs, p = it - bh * pairs;
+    const int64_t r0 = (int64_t)bh * S + 2 * p;
+    const int64_t e = row_ptr[r0 + (2 * p + 1 < S ? 2 : 1)];   // the two rows' entries are contiguous
+    for (int w = tid; w < words; w += 256) bits[w] = 0u;
+    __syncthreads();
+    for (int64_t x = row_ptr[r0] + tid; x < e; x += 256) {
+      const int c = col_idx[x];
+      if (c >= 0 && c < S) atomicOr(&bits[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    int n = 0;
+    for (int w = tid; w < words; w += 256) n += __popc(bits[w]);
+    for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m, 64);
+    if ((tid & 63) == 0) part[tid >> 6] = n;
+    __syncthreads();
+    if (tid == 0) cost[it] = part[0] + part[1] + part[2] + part[3] + kItemOverhead;
+    __syncthreads();
+  }
+}
+
+// One workgroup: XCD x gets order[bounds[x] .. bounds[x+1]); an item goes to the
+// XCD whose eighth of the total cost its exclusive cost prefix falls in.  Inside
+// a range the long items (at least four times the mean cost) come first, then
+// the rest, each class in item order (neighbouring items share key tiles, so
+// they stay together; a finer sort by cost scattered them and cost L2 hits).
+// No atomics: the order is deterministic.
+__global__ void __launch_bounds__(1024) schedule_kernel(const int32_t* __restrict__ cost, int items,
+                                                        int32_t* __restrict__ order, int32_t* __restrict__ bounds) {
+  constexpr int NB = 2;             // long items, then the rest
+  __shared__ int64_t psum[1024];
+  __shared__ int cnt[1024][NB];      // per-chunk class counts, then their inclusive prefix over chunks
+  __shared__ int lo[9];              // first item of each XCD range (lo[8] = items)
+  __shared__ int plo[9][NB];         // items of each class before lo[x]
+  const int t = threadIdx.x;
+  const int chunk = (items + 1023) / 1024;
+  const int b0 = min(items, t * chunk), b1 = min(items, b0 + chunk);
+  int64_t own = 0;
+  int local[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) local[b] = 0;
+  for (int i = b0; i < b1; ++i) own += cost[i];
+  psum[t] = own;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan of the chunk sums
+    const int64_t v = t >= off ? psum[t - off] : 0;
+    __syncthreads();
+    psum[t] += v;
+    __syncthreads();
+  }
+  // long items: at least four times the mean cost
+  const int64_t tlong = 4 * psum[1023] / items;
+  auto bucket_of = [&](int c) { return c >= tlong ? 0 : 1; };
+  for (int i = b0; i < b1; ++i) ++local[bucket_of(cost[i])];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) cnt[t][b] = local[b];
+  if (t < 9) lo[t] = -1;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan of the class counts over the chunks
+    int w[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) w[b] = t >= off ? cnt[t - off][b] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cnt[t][b] += w[b];
+    __syncthreads();
+  }
+  const int64_t total = psum[1023];
+  const int64_t pre0 = psum[t] - own;
+  auto xcd_of = [&](int64_t pre) { return (int)min((int64_t)7, pre * 8 / total); };
+  // range starts and the class counts before them
+  {
+    int run[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) run[b] = cnt[t][b] - local[b];
+    int64_t pre = pre0;
+    int xp = b0 == 0 ? -1 : (b0 < b1 ? xcd_of(pre0 - cost[b0 - 1]) : 7);
+    for (int i = b0; i < b1; ++i) {
+      const int c = cost[i];
+      const int x = xcd_of(pre);
+      for (int y = xp + 1; y <= x; ++y) {
+        lo[y] = i;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) plo[y][b] = run[b];
+      }
+      xp = x;
+      ++run[bucket_of(c)];
+      pre += c;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {   // ranges left empty at the end (one item holding more than an eighth of the cost)
+    for (int y = 0; y <= 8; ++y)
+      if (lo[y] < 0) {
+        lo[y] = items;
+        for (int b = 0; b < NB; ++b) plo[y][b] = cnt[1023][b];
+      }
+  }
+  __syncthreads();
+  if (t <= 8) bounds[t] = lo[t];
+  {
+    int run[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) run[b] = cnt[t][b] - local[b];
+    int64_t pre = pre0;
+    for (int i = b0; i < b1; ++i) {
+      const int c = cost[i];
+      const int x = xcd_of(pre);
+      const int bk = bucket_of(c);
+      int pos = lo[x] + run[bk] - plo[x][bk];
+      for (int b = 0; b < bk; ++b) pos += plo[x + 1][b] - plo[x][b];
+      order[pos] = i;
+      ++run[bk];
+      pre += c;
+    }
+  }
+}
+
+hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, int32_t* cost,
+                                int32_t* order, int32_t* bounds, hipStream_t s) {
+  const int pairs = (g.S + 1) / 2;
+  const int items = (int)((int64_t)g.B * g.nh * pairs);
+  item_cost_kernel<<<std::min(items, 4096), 256, 0, s>>>(row_ptr, col_idx, g.S, pairs, items, cost);
+  schedule_kernel<<<1, 1024, 0, s>>>(cost, items, order, bounds);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
-                            int num_cu, hipStream_t s) {
+                            const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s) {
   AttnBf16Args a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -460,6 +593,8 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.col_idx = col_idx;
   a.shift = shift;
   a.counters = counters;
+  a.order = order;
+  a.bounds = bounds;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
   a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);

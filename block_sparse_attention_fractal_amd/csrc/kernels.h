@@ -41,9 +41,13 @@ hipError_t launch_compact_sip(const Geom& g, const uint32_t* bitmap, int words, 
                               int32_t* col_idx, float* shift, const double* z, const double* rowstat, double thr,
                               int win_t, int win_h, int win_w, hipStream_t s);
 // Block-sparse attention forward (shift: per-CSR-entry natural-log logit shift, or null).
+// Work order of the bf16 attention kernel: per-item costs (cost: one int per
+// item), the item order and the 9 XCD bounds (order: one int per item).
+hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, int32_t* cost,
+                                int32_t* order, int32_t* bounds, hipStream_t s);
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
-                            int num_cu, hipStream_t s);
+                            const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s);
 // Backward: per-token (lse*log2e, dO.o) into ld, and the transposed mask's bitmap

@@ -16,8 +16,8 @@ struct MaskWs {       // byte offsets into the mask workspace
   int64_t qp, kp, z, counts, bitmap, chunk_sums, rowstat, total;   // rowstat: SIP (max, sum, c, top) per row
   int32_t words;      // 32-bit words per bitmap row
 };
-struct FwdWs {
-  int64_t counter, vt, total;
+struct FwdWs {         // work counters and XCD bounds, per-item costs and order (bf16), prepared V (bf16)
+  int64_t counter, bounds, cost, order, vt, total;
 };
 struct BwdWs {        // transposed mask, per-token dO.o, work counters, prepared transposes (bf16)
   int64_t delta, counter, tcounts, tchunks, tbitmap, tcolptr, trowidx, qt, dot, total;

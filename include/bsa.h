@@ -214,9 +214,14 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
  * order 0-3, 8-11, 4-7, 12-15.  vt: device buffer of batch*heads*L*head_dim
  * bf16 elements (the size of V), 16-byte aligned.
  * bsa_attend runs the attention kernel; `vp` is the output of bsa_prepare_v for
- * bf16, or the V tensor itself (p->layout order) for f32.  ws: at least 256
- * bytes, 256-byte aligned (work counters; contents on entry do not matter). */
+ * bf16, or the V tensor itself (p->layout order) for f32.  ws: at least
+ * attend_ws bytes (bsa_query_attend_ws), 256-byte aligned; contents on entry do
+ * not matter (it holds the work counters and, for bf16, the work order: each
+ * item's cost, its position in the order and the per-XCD bounds; 8 bytes per
+ * query-block pair plus 256).  bsa_query_attend_ws is a pure host computation;
+ * null output -> BSA_ERR_INVALID_ARG. */
 int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream);
+int bsa_query_attend_ws(const bsa_problem* p, int64_t* attend_ws);
 int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
                void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
 
@@ -295,7 +300,8 @@ const char* bsa_status_str(int status);
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* bsa_last_error(void);
 /* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
- * token-order tables and the backward pass; 300 adds the 4-token key-group path. */
+ * token-order tables and the backward pass; 300 adds the 4-token key-group path; 400 adds
+ * bsa_query_attend_ws (bsa_attend's workspace holds the work order). */
 int bsa_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 300
+    assert lib.bsa_version() == 400
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -65,8 +65,22 @@ def test_query_sizes(lib, B, nh, T, H, W):
     a = lambda x: (x + 255) // 256 * 256
     assert mws == (a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
                    + a((rows + 1023) // 1024 * 4) + a(rows * 32))
-    assert fws == 256 + a(B * nh * T * H * W * D * 2)
+    # forward workspace: work counters and XCD bounds, per-item cost and order (one int32 each
+    # per query-block pair), prepared V
+    items = B * nh * ((S + 1) // 2)
+    assert fws == 256 + 2 * a(items * 4) + a(B * nh * T * H * W * D * 2)
     assert mws % 256 == 0 and fws % 256 == 0
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_ws(ctypes.byref(P(B, nh, T, H, W, D)), ctypes.byref(aws)) == 0
+    assert aws.value == 256 + 2 * a(items * 4)
+
+
+def test_query_attend_ws(lib):
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_ws(ctypes.byref(P(dtype=0)), ctypes.byref(aws)) == 0
+    assert aws.value == 256                     # float32: work counters only
+    assert lib.bsa_query_attend_ws(ctypes.byref(P()), None) == 1
+    assert lib.bsa_query_attend_ws(ctypes.byref(P(dtype=7)), ctypes.byref(aws)) == 3
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -133,6 +147,18 @@ def test_forward_rejects_before_launch(lib):
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, fws, None) == 3
     shifted = _lib.CSR(FAKE, FAKE, max_nnz, None, FAKE + 2)          # misaligned shift array
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(shifted), FAKE, None, FAKE, fws, None) == 1
+
+
+def test_attend_rejects_a_small_workspace(lib):
+    p = P()
+    st, (rows, max_nnz, mws, fws) = sizes(lib, p)
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_ws(ctypes.byref(p), ctypes.byref(aws)) == 0
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
+    f = lib.bsa_attend
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value - 1, None) == 6
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE + 64, aws.value, None) == 6
+    assert f(ctypes.byref(p), FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value, None) == 1
 
 
 def test_struct_layouts_match_the_header():
