@@ -304,7 +304,9 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
   if (e == hipSuccess) e = launch_zero_i32(counters, 16, stream);
   if (e == hipSuccess)
     e = launch_backward(g, q, k, v, dout, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
-                        mask->col_idx, tcolptr, trowidx, counters, ncu, stream);
+                        mask->col_idx, tcolptr, trowidx, counters, reinterpret_cast<int32_t*>(base + w.cost),
+                        reinterpret_cast<int32_t*>(base + w.order_q), reinterpret_cast<int32_t*>(base + w.order_k),
+                        reinterpret_cast<int32_t*>(base + w.bounds), ncu, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return BSA_OK;
 }

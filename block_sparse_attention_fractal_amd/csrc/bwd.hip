@@ -65,6 +65,8 @@ struct Args {
   const int32_t* ptr;      // CSR (dQ pass) or transposed CSR (dK/dV pass)
   const int32_t* idx;
   int32_t* counters;       // 8 per-XCD item counters
+  const int32_t* order;    // items in processing order: XCD x takes order[bounds[x] .. bounds[x+1])
+  const int32_t* bounds;   // 9 entries
   Geom g;
   float c_log2;            // log2(e) / sqrt(D)
   float inv_sqrt_d;
@@ -79,29 +81,6 @@ __device__ __forceinline__ int block_base_row(const Geom& g, int j) {
   const int py = rest % g.Hp;
   const int t = rest / g.Hp;
   return (t * g.H + py * 8) * g.W + px * 8;
-}
-
-__device__ __forceinline__ int64_t item_cost_prefix(const Args& a, int64_t t) {
-  const int64_t bh = t / a.pairs;
-  const int64_t p = t - bh * a.pairs;
-  int64_t row = bh * a.g.S + 2 * p;
-  if (row > a.g.rows) row = a.g.rows;
-  return a.ptr[row];
-}
-
-// XCD-partitioned item range of this workgroup (balanced by cumulative entries)
-__device__ __forceinline__ void item_range(const Args& a, int xcd, int64_t& lo_t, int64_t& hi_t) {
-  const int64_t total = a.ptr[a.g.rows];
-  auto first_item_with_cost = [&](int64_t target) {
-    int64_t lo = 0, hi = a.items;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (item_cost_prefix(a, mid + 1) > target) hi = mid; else lo = mid + 1;
-    }
-    return lo;
-  };
-  lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
-  hi_t = xcd == 7 ? a.items : first_item_with_cost(total * (xcd + 1) / 8);
 }
 
 // Union walk over the ascending lists of rows r0 and r0+1 (wave-uniform).  Each
@@ -217,14 +196,14 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
   }
   auto tr_off = [&](int u, int s, int r2) { return trp[u ^ (2 * r2)] + 2048 * r2 + 4096 * s; };
   const int xcd = blockIdx.x & 7;
-  int64_t lo_t, hi_t;
-  item_range(a, xcd, lo_t, hi_t);
+  const int lo_t = a.bounds[xcd], hi_t = a.bounds[xcd + 1];   // this XCD's stretch of the work order
 
   for (;;) {
-    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    if (tid == 0) s_item = lo_t + atomicAdd(&a.counters[xcd], 1);
     __syncthreads();
-    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= hi_t) break;
+    const int idx = __builtin_amdgcn_readfirstlane(s_item);
+    if (idx >= hi_t) break;
+    const int64_t item = a.order[idx];
     const int64_t bh = item / a.pairs;
     const int i0 = 2 * (int)(item - bh * a.pairs);
     const int64_t r0 = bh * g.S + i0;
@@ -376,14 +355,14 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Args a) {
   const int ldm = 2 * (lane & 31);
   const int ldoff = (((ldm >> 3) * rs + (ldm & 7))) * 8;
   const int xcd = blockIdx.x & 7;
-  int64_t lo_t, hi_t;
-  item_range(a, xcd, lo_t, hi_t);
+  const int lo_t = a.bounds[xcd], hi_t = a.bounds[xcd + 1];   // this XCD's stretch of the work order
 
   for (;;) {
-    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    if (tid == 0) s_item = lo_t + atomicAdd(&a.counters[xcd], 1);
     __syncthreads();
-    const int64_t item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= hi_t) break;
+    const int idx = __builtin_amdgcn_readfirstlane(s_item);
+    if (idx >= hi_t) break;
+    const int64_t item = a.order[idx];
     const int64_t bh = item / a.pairs;
     const int j0 = 2 * (int)(item - bh * a.pairs);
     const int64_t r0 = bh * g.S + j0;
@@ -725,7 +704,8 @@ hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, 
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
                            const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
-                           const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s) {
+                           const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
+                           int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s) {
   const double scale = 1.0 / sqrt((double)g.D);
   if (g.dtype == BSA_F32) {
     const unsigned grid = (unsigned)g.rows;
@@ -761,13 +741,23 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
   const int grid = ((num_cu + 7) / 8) * 8;        // one workgroup per CU (LDS-limited), a multiple of 8 XCDs
+  // work orders as for the forward (pairs of query blocks over the CSR, pairs of
+  // key blocks over the transposed one); the cost scratch is reused in stream order
+  hipError_t e = launch_attn_schedule(g, row_ptr, col_idx, cost, order_q, bounds, s);
+  if (e != hipSuccess) return e;
   a.ptr = row_ptr;
   a.idx = col_idx;
   a.counters = counters;
+  a.order = order_q;
+  a.bounds = bounds;
   bwd::dq_bf16_kernel<<<((num_cu * 2 + 7) / 8) * 8, 256, 0, s>>>(a);   // two workgroups per CU
+  e = launch_attn_schedule(g, tcolptr, trowidx, cost, order_k, bounds + 16, s);
+  if (e != hipSuccess) return e;
   a.ptr = tcolptr;
   a.idx = trowidx;
   a.counters = counters + 8;
+  a.order = order_k;
+  a.bounds = bounds + 16;
   bwd::dkdv_bf16_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -60,7 +60,8 @@ hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, 
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
                            const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
-                           const int32_t* trowidx, int32_t* counters, int num_cu, hipStream_t s);
+                           const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
+                           int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s);
 // Logits of query-block means against Sk key columns (blocks or 4-token groups)
 // for heads h0 .. h0+nheads-1; z holds those heads' rows only.
 hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,

@@ -105,6 +105,11 @@ BwdWs bwd_ws_layout(const Geom& g) {
   int64_t off = 0;
   w.delta = off; off = align256(off + tok * 8);     // float2 per token
   w.counter = off; off = align256(off + 64);
+  w.bounds = off; off = align256(off + 32 * 4);   // two sets of 9 XCD bounds (at 0 and 16)
+  const int64_t items = g.dtype == BSA_BF16 ? (int64_t)g.B * g.nh * ((g.S + 1) / 2) : 0;
+  w.cost = off; off = align256(off + items * 4);
+  w.order_q = off; off = align256(off + items * 4);
+  w.order_k = off; off = align256(off + items * 4);
   w.tcounts = off; off = align256(off + g.rows * 4);
   w.tchunks = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
   w.tbitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
