@@ -128,7 +128,7 @@ def time_groups(bsa, cfg, q, k, v, g, steps, warmup, stream):
     prob = bsa.make_problem(qs[0], g)
     gs = bsa.query_group_sizes(prob)
     mws = torch.empty(gs["mask_ws"], dtype=torch.uint8, device=q.device)
-    fws = torch.empty(256, dtype=torch.uint8, device=q.device)
+    fws = torch.empty(bsa.attend_groups_workspace_bytes(prob), dtype=torch.uint8, device=q.device)
     vg = torch.empty(qs[0].numel(), dtype=q.dtype, device=q.device)
     outs = [torch.empty_like(x) for x in qs]
     masks = [None] * len(parts)

@@ -20,7 +20,7 @@ BSA_ORDER_FRACTAL, BSA_ORDER_TILE_MAJOR, BSA_ORDER_HILBERT = 0, 1, 2
 EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
             "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_query_attend_ws", "bsa_attend",
             "bsa_query_backward_ws", "bsa_backward", "bsa_query_group_sizes", "bsa_build_group_mask",
-            "bsa_forward_groups", "bsa_prepare_v_groups", "bsa_attend_groups", "bsa_status_str", "bsa_last_error",
+            "bsa_forward_groups", "bsa_prepare_v_groups", "bsa_query_attend_groups_ws", "bsa_attend_groups", "bsa_status_str", "bsa_last_error",
             "bsa_version"]
 
 
@@ -81,6 +81,7 @@ def lib():
     l.bsa_build_group_mask.argtypes = [P(Problem), ctypes.c_int, P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
     l.bsa_forward_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_prepare_v_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp]
+    l.bsa_query_attend_groups_ws.argtypes = [P(Problem), ctypes.c_int, P(i64)]
     l.bsa_attend_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_status_str.argtypes = [ctypes.c_int]
     l.bsa_status_str.restype = ctypes.c_char_p

@@ -110,6 +110,13 @@ def attend_workspace_bytes(prob: _lib.Problem) -> int:
     return nbytes.value
 
 
+def attend_groups_workspace_bytes(prob: _lib.Problem) -> int:
+    """Bytes of device workspace bsa_attend_groups needs for this problem (work counters and order)."""
+    nbytes = ctypes.c_int64()
+    check(lib().bsa_query_attend_groups_ws(ctypes.byref(prob), KEY_GROUP, ctypes.byref(nbytes)))
+    return nbytes.value
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes or ws.data_ptr() % 256:
@@ -369,7 +376,7 @@ def attend_groups(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: Bloc
         raise ValueError("vp must be a contiguous tensor with q's dtype and size")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    ws = _workspace(256, q.device, workspace)
+    ws = _workspace(attend_groups_workspace_bytes(prob), q.device, workspace)
     csr = mask.as_struct()
     check(lib().bsa_attend_groups(ctypes.byref(prob), KEY_GROUP, q.data_ptr(), k.data_ptr(), vp.data_ptr(),
                                   ctypes.byref(csr), o.data_ptr(), lse.data_ptr() if lse is not None else None,

@@ -453,12 +453,23 @@ static int enqueue_attend_groups(const Geom& g, const void* q, const void* k, co
     int32_t* counter = reinterpret_cast<int32_t*>(ws + w.counter);
     e = launch_zero_i32(counter, 8, stream);
     if (e == hipSuccess)
-      e = launch_attn_groups_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter, ncu, stream);
+      e = launch_attn_groups_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, counter,
+                                  reinterpret_cast<int32_t*>(ws + w.cost), reinterpret_cast<int32_t*>(ws + w.order),
+                                  reinterpret_cast<int32_t*>(ws + w.bounds), ncu, stream);
   } else {
     e = launch_attn_groups_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
                                mask->col_idx, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "group attention launch");
+  return BSA_OK;
+}
+
+int bsa_query_attend_groups_ws(const bsa_problem* p, int group, int64_t* attend_ws) {
+  Geom g;
+  int st = group_geom(p, group, &g);
+  if (st != BSA_OK) return st;
+  if (!attend_ws) return fail(BSA_ERR_INVALID_ARG, "bsa_query_attend_groups_ws: null output");
+  *attend_ws = grp_fwd_ws_layout(g).vg;
   return BSA_OK;
 }
 

@@ -580,6 +580,11 @@ hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int
   return hipGetLastError();
 }
 
+hipError_t launch_schedule_costs(const int32_t* cost, int items, int32_t* order, int32_t* bounds, hipStream_t s) {
+  schedule_kernel<<<1, 1024, 0, s>>>(cost, items, order, bounds);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
                             const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s) {

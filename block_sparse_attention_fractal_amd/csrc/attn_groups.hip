@@ -13,8 +13,9 @@
 //     workgroups, wave w owns queries 32*(w&1).. and the 32 keys of slots
 //     8*(w>>1).. of every tile; the two waves of a query range merge their
 //     online-softmax states at the end;
-//   * persistent grid, two workgroups per CU, XCD-partitioned item ranges
-//     balanced by cumulative kept groups (as in the block kernel);
+//   * persistent grid, two workgroups per CU; the rows are split into 8 XCD
+//     ranges of equal cost (64-key tiles plus a fixed per-row cost) and each
+//     range runs its long rows first (the block kernel's work order);
 //   * a K tile slot is 4 key rows (1 KB) loaded with ONE direct-to-LDS 16-byte
 //     buffer load per wave (lane -> row lane/16, chunk lane%16, swizzled
 //     chunk c ^ (row & 15)); a V slot is the group's 128 x 4 transposed block
@@ -64,6 +65,8 @@ struct Args {
   const int32_t* row_ptr;
   const int32_t* col_idx;  // group ids
   int32_t* counters;
+  const int32_t* order;    // rows in processing order: XCD x takes order[bounds[x] .. bounds[x+1])
+  const int32_t* bounds;   // 9 entries
   Geom g;
   float c_log2;
   uint32_t magic_wp, magic_hp;   // fractal order: magic_wp = 0
@@ -148,27 +151,14 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
   asm volatile("" : "+v"(vaddr));
 
   const int xcd = blockIdx.x & 7;
-  const int64_t items = g.rows;
-  const int64_t total = a.row_ptr[items];
-  int64_t lo_t, hi_t;
-  {
-    auto first_item_with_cost = [&](int64_t target) {
-      int64_t lo = 0, hi = items;
-      while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (a.row_ptr[mid + 1] > target) hi = mid; else lo = mid + 1;
-      }
-      return lo;
-    };
-    lo_t = xcd == 0 ? 0 : first_item_with_cost(total * xcd / 8);
-    hi_t = xcd == 7 ? items : first_item_with_cost(total * (xcd + 1) / 8);
-  }
+  const int lo_t = a.bounds[xcd], hi_t = a.bounds[xcd + 1];   // this XCD's stretch of the work order
 
   for (;;) {
-    if (tid == 0) s_item = (int)(lo_t + atomicAdd(&a.counters[xcd], 1));
+    if (tid == 0) s_item = lo_t + atomicAdd(&a.counters[xcd], 1);
     __syncthreads();
-    const int64_t r = __builtin_amdgcn_readfirstlane(s_item);
-    if (r >= hi_t) break;
+    const int idx = __builtin_amdgcn_readfirstlane(s_item);
+    if (idx >= hi_t) break;
+    const int64_t r = a.order[idx];
     const int64_t bh = r / g.S;
     const int i = (int)(r - bh * g.S);
     const int p0 = a.row_ptr[r], e0 = a.row_ptr[r + 1];
@@ -431,6 +421,13 @@ __global__ void __launch_bounds__(256) prep_vg_kernel(const uint16_t* __restrict
   }
 }
 
+// cost of every row: its 64-key tiles plus a fixed per-row cost (Q load, ring prologue, output)
+__global__ void __launch_bounds__(256) row_cost_kernel(const int32_t* __restrict__ row_ptr, int64_t rows,
+                                                       int32_t* __restrict__ cost) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r < rows) cost[r] = (row_ptr[r + 1] - row_ptr[r] + 15) / 16 + 4;
+}
+
 }  // namespace grp
 
 hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s) {
@@ -440,8 +437,11 @@ hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s)
 }
 
 hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, const void* vg, void* o, float* lse,
-                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
-                                   hipStream_t s) {
+                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int32_t* cost,
+                                   int32_t* order, int32_t* bounds, int num_cu, hipStream_t s) {
+  grp::row_cost_kernel<<<(unsigned)((g.rows + 255) / 256), 256, 0, s>>>(row_ptr, g.rows, cost);
+  hipError_t e = launch_schedule_costs(cost, (int)g.rows, order, bounds, s);
+  if (e != hipSuccess) return e;
   grp::Args a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -451,6 +451,8 @@ hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, 
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.counters = counters;
+  a.order = order;
+  a.bounds = bounds;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
   a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);

@@ -45,6 +45,8 @@ hipError_t launch_compact_sip(const Geom& g, const uint32_t* bitmap, int words, 
 // item), the item order and the 9 XCD bounds (order: one int per item).
 hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, int32_t* cost,
                                 int32_t* order, int32_t* bounds, hipStream_t s);
+// The same order from given per-item costs (each >= 1).
+hipError_t launch_schedule_costs(const int32_t* cost, int items, int32_t* order, int32_t* bounds, hipStream_t s);
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
                             const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s);
@@ -78,8 +80,8 @@ int group_select_max_groups();
 hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s);
 // Attention over a CSR of 4-token key groups (bf16 needs the prepared vg; f32 reads v).
 hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, const void* vg, void* o, float* lse,
-                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int num_cu,
-                                   hipStream_t s);
+                                   const int32_t* row_ptr, const int32_t* col_idx, int32_t* counters, int32_t* cost,
+                                   int32_t* order, int32_t* bounds, int num_cu, hipStream_t s);
 hipError_t launch_attn_groups_f32(const Geom& g, const float* q, const float* k, const float* v, float* o,
                                   float* lse, const int32_t* row_ptr, const int32_t* col_idx, hipStream_t s);
 // Zero a small device counter (a fill kernel, safe under stream capture).

@@ -156,7 +156,12 @@ GrpMaskWs grp_mask_ws_layout(const Geom& g) {
 GrpFwdWs grp_fwd_ws_layout(const Geom& g) {
   GrpFwdWs w{};
   int64_t off = 0;
-  w.counter = off; off = align256(off + 64);
+  w.counter = off;
+  w.bounds = off + 64;
+  off = align256(off + 128);
+  const int64_t items = g.dtype == BSA_BF16 ? g.rows : 0;
+  w.cost = off; off = align256(off + items * 4);
+  w.order = off; off = align256(off + items * 4);
   w.vg = off;
   if (g.dtype == BSA_BF16) off = align256(off + (int64_t)g.B * g.nh * g.L * g.D * 2);
   w.total = off;

@@ -28,8 +28,8 @@ struct GrpMaskWs {     // key-group mask: query-block means, group means, a head
   int64_t chunk_heads;  // heads whose group logits are computed together
   int32_t words;        // 32-bit words per bitmap row (L/4 bits)
 };
-struct GrpFwdWs {
-  int64_t counter, vg, total;
+struct GrpFwdWs {      // work counters and XCD bounds, per-row cost and order (bf16), prepared V (bf16)
+  int64_t counter, bounds, cost, order, vg, total;
 };
 // Checks the key-group size and the limits of the group path.
 int check_group(const Geom& g, int group, std::string* msg);

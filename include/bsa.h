@@ -288,10 +288,14 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
  * bsa_prepare_v_groups (bf16 only) writes V as [batch, heads, L/4, head_dim, 4]:
  * each group's 4 tokens stored channel-major (vg: the size of V, 16-byte
  * aligned); bsa_attend_groups then runs the attention on it (f32: pass V itself)
- * with ws of at least 256 bytes. */
+ * with ws of at least attend_ws bytes (bsa_query_attend_groups_ws: the work
+ * counters and, for bf16, each row's cost, its position in the work order and the
+ * per-XCD bounds, 8 bytes per row plus 256; pure host computation, null output ->
+ * BSA_ERR_INVALID_ARG), 256-byte aligned, contents on entry irrelevant. */
 int bsa_forward_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* v,
                        const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
 int bsa_prepare_v_groups(const bsa_problem* p, int group, const void* v, void* vg, hipStream_t stream);
+int bsa_query_attend_groups_ws(const bsa_problem* p, int group, int64_t* attend_ws);
 int bsa_attend_groups(const bsa_problem* p, int group, const void* q, const void* k, const void* vp,
                       const bsa_csr* mask, void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
 
@@ -301,7 +305,8 @@ const char* bsa_status_str(int status);
 const char* bsa_last_error(void);
 /* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
  * token-order tables and the backward pass; 300 adds the 4-token key-group path; 400 adds
- * bsa_query_attend_ws (bsa_attend's workspace holds the work order). */
+ * bsa_query_attend_ws and bsa_query_attend_groups_ws (the attention workspaces hold the work
+ * order). */
 int bsa_version(void);
 
 #ifdef __cplusplus

@@ -197,7 +197,12 @@ def test_query_group_sizes(lib, B, nh, T, H, W):
     chunk = max(1, min(B * nh, (1 << 31) // per_head))
     assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(rows * 4)
                    + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
-    assert fws == 256 + a(B * nh * L * D * 2)
+    assert fws == 256 + 2 * a(rows * 4) + a(B * nh * L * D * 2)
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_groups_ws(ctypes.byref(P(B, nh, T, H, W, D)), 4, ctypes.byref(aws)) == 0
+    assert aws.value == 256 + 2 * a(rows * 4)
+    assert lib.bsa_query_attend_groups_ws(ctypes.byref(P(B, nh, T, H, W, D)), 4, None) == 1
+    assert lib.bsa_query_attend_groups_ws(ctypes.byref(P(B, nh, T, H, W, D)), 8, ctypes.byref(aws)) == 4
 
 
 def test_group_path_rejects_before_launch(lib):
