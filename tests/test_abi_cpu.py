@@ -233,5 +233,12 @@ def test_group_path_rejects_before_launch(lib):
     assert f(ctypes.byref(p), 4, FAKE, FAKE, FAKE, ctypes.byref(shifted), FAKE, None, FAKE, fws, None) == 4
     assert lib.bsa_attend_groups(ctypes.byref(p), 3, FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, 256,
                                  None) == 4
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_groups_ws(ctypes.byref(p), 4, ctypes.byref(aws)) == 0
+    assert 256 < aws.value < fws                  # work order, without the prepared V
+    a = lib.bsa_attend_groups
+    assert a(ctypes.byref(p), 4, FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value - 1, None) == 6
+    assert a(ctypes.byref(p), 4, FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE + 64, aws.value, None) == 6
+    assert a(ctypes.byref(p), 4, FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value, None) == 1
     f32 = P(dtype=0, D=64)
     assert lib.bsa_prepare_v_groups(ctypes.byref(f32), 4, FAKE, FAKE + 256, None) == 4
