@@ -56,8 +56,25 @@ def traffic_for_current_kernel(cfg_idx: int):
     return t.get("bytes_per_launch")
 
 
+def density_by_class(cfg, mask):
+    """Kept-block density of the local heads (positional term) and of the diffuse
+    (pure N(0,1)) heads, from the GPU CSR."""
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    per_head = np.diff(rp[::cfg.S]).reshape(cfg.batch, cfg.heads) / float(cfg.S * cfg.S)
+    nl = cfg.n_local_heads()
+    out = {"local": round(float(per_head[:, :nl].mean()), 5)}
+    if nl < cfg.heads:
+        out["diffuse"] = round(float(per_head[:, nl:].mean()), 5)
+    out["heads"] = f"local {nl}, diffuse {cfg.heads - nl} per batch item"
+    return out
+
+
 def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
-    """Time the oracle on a bounded sample and extrapolate to one full call."""
+    """Time the oracle on a bounded sample and extrapolate to one full call.  The
+    whole-head masks the sample builds are also compared with the GPU's CSR:
+    returns (baseline, mask_check) where mask_check counts the blocks whose oracle
+    exclusive cumulative mass lies within 1e-4 of 1 - thr (the band) and the
+    blocks on which the two masks differ (all of which must lie in the band)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -71,14 +88,27 @@ def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
         wmask = oracle.sta_window(cfg.T, cfg.H // cfg.patch, cfg.W // cfg.patch, cfg.window)
     # mask: whole heads
     t0 = time.perf_counter()
+    t_check = 0.0
     n_heads = 0
+    band = mism = out_of_band = 0
     while True:
         b, h = divmod(n_heads, cfg.heads)
-        oracle.head_mask(inputs["q"][b, h][src], inputs["k"][b, h][src], N, cfg.thr, wmask)
+        m = oracle.head_mask(inputs["q"][b, h][src], inputs["k"][b, h][src], N, cfg.thr, wmask)
+        tc = time.perf_counter()
+        r0 = n_heads * S
+        got = np.zeros((S, S), dtype=bool)
+        lo = int(row_ptr[r0])
+        got[np.repeat(np.arange(S), np.diff(row_ptr[r0:r0 + S + 1])), col_idx[lo:int(row_ptr[r0 + S])]] = True
+        in_band = np.abs(m["cexcl"] - (1.0 - cfg.thr)) <= 1e-4 if cfg.thr > 0 else np.zeros((S, S), dtype=bool)
+        diff = got != m["keep"]
+        band += int(in_band.sum())
+        mism += int(diff.sum())
+        out_of_band += int((diff & ~in_band).sum())
+        t_check += time.perf_counter() - tc
         n_heads += 1
-        if time.perf_counter() - t0 > budget_s / 3 or n_heads >= cfg.batch * cfg.heads:
+        if time.perf_counter() - t0 - t_check > budget_s / 3 or n_heads >= cfg.batch * cfg.heads:
             break
-    t_mask = (time.perf_counter() - t0) / n_heads * cfg.batch * cfg.heads
+    t_mask = (time.perf_counter() - t0 - t_check) / n_heads * cfg.batch * cfg.heads
     # attention: random CSR rows until the budget is used
     rng = np.random.default_rng(cfg.seed)
     order = rng.permutation(cfg.rows)
@@ -103,6 +133,8 @@ def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
             break
     t_attn = (time.perf_counter() - t0) / flops * exec_flops
     total = t_mask + t_attn
+    check = {"heads": n_heads, "band_blocks": band, "mismatches": mism, "mismatches_outside_band": out_of_band,
+             "what": "GPU CSR vs the oracle's whole-head masks built for the baseline sample"}
     return {
         "value": cfg.dense_flops / total / 1e12,
         "unit": "TFLOP/s (dense-equivalent)",
@@ -111,7 +143,7 @@ def cpu_baseline(cfg, inputs, row_ptr, col_idx, exec_flops, budget_s):
         "sample": (f"float64 numpy oracle: mask of {n_heads} of {cfg.batch * cfg.heads} heads and attention of "
                    f"{n_rows} of {cfg.rows} CSR rows ({flops / 1e9:.1f} GFLOP), extrapolated to one full call "
                    f"by head count and executed-FLOP share = {total:.1f} s per call"),
-    }
+    }, check
 
 
 def time_groups(bsa, cfg, q, k, v, g, steps, warmup, stream):
@@ -168,11 +200,11 @@ def time_groups(bsa, cfg, q, k, v, g, steps, warmup, stream):
 
 
 def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
-    """Event-timed bsa_backward calls (one call = row-term prep, transposed mask,
-    operand transposes, the dQ kernel and the dK/dV kernel) on the bench's mask, with a
-    seeded N(0,1) dout.  Executed FLOPs count the 7 tile products of 64 x 64 x D
-    (dQ: S, dP, dQ; dK/dV: S, dP, dV, dK) per kept tile; the dQ kernel's second
-    (low-part) dZ product is extra work on top."""
+    """Event-timed bsa_backward calls (one call = lse prep, transposed mask, operand
+    transposes, the Delta walk, the dQ kernel and the dK/dV kernel) on the bench's mask,
+    with a seeded N(0,1) dout.  Executed FLOPs count the 7 tile products of 64 x 64 x D
+    (dQ: S, dP, dQ; dK/dV: S, dP, dV, dK) per kept tile; the Delta walk's two products
+    (S, dP again) and the dQ kernel's second (low-part) dZ product are extra work on top."""
     import torch
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     o = torch.empty_like(q)
@@ -186,12 +218,12 @@ def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
     prob = bsa.make_problem(q, g)
     ws = torch.empty(max(bsa.backward_workspace_bytes(prob), 256), dtype=torch.uint8, device=q.device)
     for _ in range(max(1, warmup)):
-        bsa.backward(q, k, v, mask, g, o, lse, dout, workspace=ws, out=grads)
+        bsa.backward(q, k, v, mask, g, lse, dout, workspace=ws, out=grads)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
-        bsa.backward(q, k, v, mask, g, o, lse, dout, workspace=ws, out=grads)
+        bsa.backward(q, k, v, mask, g, lse, dout, workspace=ws, out=grads)
     ev[1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
@@ -206,8 +238,11 @@ def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--scratch-mb", type=int, default=512,
+                    help="MB of scratch written between timed steps so that the 256 MB MALL holds none of the "
+                         "inputs when a step starts (0 disables)")
     ap.add_argument("--config", type=int, default=4, help="workload index (default 4: HunyuanVideo-scale hybrid)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -269,20 +304,33 @@ def main():
             ev[3].record(stream)
         return mask
 
-    for _ in range(args.warmup):
+    scratch = torch.empty(max(args.scratch_mb, 0) << 20, dtype=torch.uint8, device=dev)
+
+    def flush(i):
+        if scratch.numel():
+            scratch.fill_(i & 0xFF)   # a plain write kernel on the same stream, outside the step's events
+
+    for i in range(args.warmup):
+        flush(i)
         mask = step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        flush(s)
         mask = step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    per_stage = [np.array([e[i].elapsed_time(e[i + 1]) for e in events]) for i in range(3)]
+    per_step = np.array([e[0].elapsed_time(e[3]) for e in events])
+    attn_ms = float(per_stage[2].mean())                            # the roofline uses the average launch
+    mask_ms, prep_ms = (float(np.median(x)) for x in per_stage[:2])  # HBM figures from the median
+
+    def stats(x):
+        return {"median": round(float(np.median(x)), 4), "min": round(float(x.min()), 4),
+                "mean": round(float(x.mean()), 4)}
 
     nnz = mask.nnz()
     rows, S = mask.rows, mask.S
@@ -329,12 +377,16 @@ def main():
             "flops_per_launch": exec_flops,
             "avg_launch_ms": round(attn_ms, 4),
         },
-        "stages_ms": {"build_mask": round(mask_ms, 4), "prepare_v": round(prep_ms, 4), "attend": round(attn_ms, 4)},
+        "stages_ms": {"build_mask": stats(per_stage[0]), "prepare_v": stats(per_stage[1]),
+                      "attend": stats(per_stage[2]), "step_events": stats(per_step),
+                      "timing": f"HIP events over {args.steps} steps, {args.scratch_mb} MB scratch written "
+                                f"between steps (outside the events, inside ms_per_step)"},
         "mask_stage": {"algorithmic_bytes": mask_bytes, "gbs": round(mask_gbs, 1),
-                       "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4)},
+                       "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4), "from": "median build_mask time"},
         "prepare_v": {"gbs": round(prep_gbs, 1), "hbm_frac": round(prep_gbs / HBM_PEAK_GBS, 4)},
         "mask_mode": "cdf" if args.sip_seed is None else f"sip(seed={args.sip_seed})",
         "density": round(density, 5),
+        "density_by_head_class": density_by_class(cfg, mask),
         "nnz": nnz,
         "executed_tflop": round(exec_flops / 1e12, 3),
         "input_gen_s": round(t_gen, 1),
@@ -346,7 +398,7 @@ def main():
     if not args.no_cpu_baseline:
         rp = mask.row_ptr.cpu().numpy().astype(np.int64)
         ci = mask.col_idx[:nnz].cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(cfg, inputs, rp, ci, exec_flops, args.cpu_seconds)
+        line["cpu_baseline"], line["mask_check"] = cpu_baseline(cfg, inputs, rp, ci, exec_flops, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

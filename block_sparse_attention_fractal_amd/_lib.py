@@ -76,7 +76,7 @@ def lib():
     l.bsa_query_attend_ws.argtypes = [P(Problem), P(i64)]
     l.bsa_attend.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
     l.bsa_query_backward_ws.argtypes = [P(Problem), P(i64)]
-    l.bsa_backward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, vp, i64, vp]
+    l.bsa_backward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, i64, vp]
     l.bsa_query_group_sizes.argtypes = [P(Problem), ctypes.c_int, P(i64), P(i64), P(i64)]
     l.bsa_build_group_mask.argtypes = [P(Problem), ctypes.c_int, P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
     l.bsa_forward_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]

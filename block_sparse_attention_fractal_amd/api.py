@@ -287,11 +287,12 @@ def attention(q, k, v, grid: VideoGrid, thr: float, window=None, layout: str = "
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
-             o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, layout: str = "original",
+             lse: torch.Tensor, dout: torch.Tensor, layout: str = "original",
              workspace: Optional[torch.Tensor] = None, out=None):
-    """Gradients (dq, dk, dv) of sum(o * dout) for forward(q, k, v, mask) with its o and lse.
+    """Gradients (dq, dk, dv) of sum(o * dout) for o = forward(q, k, v, mask), given the
+    forward's lse (the row term is recomputed from P and dP, so o is not needed).
     `out` = (dq, dk, dv) tensors shaped like q to write into (else new ones)."""
-    _check_qkv(q, k, v, o, dout)
+    _check_qkv(q, k, v, dout)
     if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
         raise ValueError("lse must be float32 [batch, heads, L] as forward(return_lse=True) gives it")
     prob = make_problem(q, grid, layout)
@@ -303,8 +304,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask,
         _check_qkv(q, dq, dk, dv)
     csr = mask.as_struct()
     check(lib().bsa_backward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
-                             o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
+                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             ws.data_ptr(), ws.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -57,7 +57,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 400; }
+int bsa_version(void) { return 500; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -183,15 +183,37 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
   const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)g.S) - std::log(mp->thr) : 0.0;
   const int wt = win ? mp->win_t : -1, wh = win ? mp->win_h : -1, ww = win ? mp->win_w : -1;
   double* rowstat = reinterpret_cast<double*>(base + w.rowstat);
-  hipError_t e = launch_pool(g, q, k, qp, kp, stream);
-  if (e == hipSuccess) e = launch_block_logits(g, qp, kp, z, stream);
-  // SIP: the CDF cut without the window gives each row's budget, then the
-  // sampling replaces the bitmap and unions the window
-  if (e == hipSuccess)
-    e = launch_select(g, z, mp->thr, lambda, sip ? -1 : wt, sip ? -1 : wh, sip ? -1 : ww, bitmap, counts, w.words,
-                      stream);
-  if (e == hipSuccess && sip)
-    e = launch_sip(g, z, mp->thr, mp->seed, wt, wh, ww, bitmap, counts, rowstat, w.words, stream);
+  hipError_t e = hipSuccess;
+  if (!sip) {
+    // the screened cut keeps the map on chip; rows it cannot decide take the float64 path
+    ScreenOps ops;
+    ops.qs = reinterpret_cast<_Float16*>(base + w.qs);
+    ops.ks = reinterpret_cast<_Float16*>(base + w.ks);
+    ops.qmu = reinterpret_cast<double*>(base + w.qmu);
+    ops.kmu = reinterpret_cast<double*>(base + w.kmu);
+    ops.qn = reinterpret_cast<double*>(base + w.qn);
+    ops.qe = reinterpret_cast<int32_t*>(base + w.qe);
+    ops.ke = reinterpret_cast<int32_t*>(base + w.ke);
+    ops.hstat = reinterpret_cast<uint64_t*>(base + w.hstat);
+    int32_t* flags = reinterpret_cast<int32_t*>(base + w.flags);
+    int32_t* nflag = reinterpret_cast<int32_t*>(base + w.nflag);
+    e = launch_pool(g, q, k, qp, kp, stream);
+    if (e == hipSuccess) e = launch_screen_ops(g, qp, kp, ops, nflag, stream);
+    if (e == hipSuccess)
+      e = launch_screen_select(g, ops, qp, kp, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words, flags, nflag,
+                               stream);
+    if (e == hipSuccess)
+      e = launch_fallback_select(g, qp, kp, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words, flags, nflag,
+                                 stream);
+  } else {
+    // SIP: the float64 map and the CDF cut without the window give each row's
+    // budget, then the sampling replaces the bitmap and unions the window
+    e = launch_pool(g, q, k, qp, kp, stream);
+    if (e == hipSuccess) e = launch_block_logits(g, qp, kp, z, stream);
+    if (e == hipSuccess) e = launch_select(g, z, mp->thr, lambda, -1, -1, -1, bitmap, counts, w.words, stream);
+    if (e == hipSuccess)
+      e = launch_sip(g, z, mp->thr, mp->seed, wt, wh, ww, bitmap, counts, rowstat, w.words, stream);
+  }
   if (e == hipSuccess)
     e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
   if (e == hipSuccess && !sip) e = launch_compact(g, bitmap, w.words, out->row_ptr, out->col_idx, stream);
@@ -264,18 +286,21 @@ int bsa_query_backward_ws(const bsa_problem* p, int64_t* bwd_ws) {
 }
 
 int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
-                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
-                 int64_t ws_bytes, hipStream_t stream) {
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, int64_t ws_bytes,
+                 hipStream_t stream) {
   Geom g;
   int st = geom_or_fail(p, &g);
   if (st != BSA_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !mask || !mask->row_ptr || !mask->col_idx)
+  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !mask || !mask->row_ptr || !mask->col_idx)
     return fail(BSA_ERR_INVALID_ARG, "bsa_backward: null pointer");
-  const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
+  const void* t16[] = {q, k, v, dout, dq, dk, dv};
   for (const void* t : t16)
     if (!aligned(t, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: tensors must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: misaligned lse");
   if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: masks with logit shifts are not supported");
+  if (g.dtype == BSA_BF16 && g.D != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: bf16 head_dim " + std::to_string(g.D) +
+                                         " (only 128 is implemented; float32 supports 64 and 128)");
   const BwdWs w = bwd_ws_layout(g);
   if (!ws || ws_bytes < w.total)
     return fail(BSA_ERR_WORKSPACE, "bsa_backward: workspace needs " + std::to_string(w.total) + " bytes");
@@ -292,8 +317,7 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
   uint32_t* tbits = reinterpret_cast<uint32_t*>(base + w.tbitmap);
   int32_t* tcolptr = reinterpret_cast<int32_t*>(base + w.tcolptr);
   int32_t* trowidx = reinterpret_cast<int32_t*>(base + w.trowidx);
-  hipError_t e = launch_backward_prep(g, o, dout, lse, ld, mask->row_ptr, mask->col_idx, tbits, w.words, tcounts,
-                                      stream);
+  hipError_t e = launch_backward_prep(g, lse, ld, mask->row_ptr, mask->col_idx, tbits, w.words, tcounts, stream);
   if (e == hipSuccess)
     e = launch_scan(g, tcounts, tcolptr, reinterpret_cast<int32_t*>(base + w.tchunks), nullptr, stream);
   if (e == hipSuccess) e = launch_compact(g, tbits, w.words, tcolptr, trowidx, stream);
@@ -301,7 +325,7 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
     e = launch_prep_vt(g, q, base + w.qt, stream);
     if (e == hipSuccess) e = launch_prep_vt(g, dout, base + w.dot, stream);
   }
-  if (e == hipSuccess) e = launch_zero_i32(counters, 16, stream);
+  if (e == hipSuccess) e = launch_zero_i32(counters, 24, stream);
   if (e == hipSuccess)
     e = launch_backward(g, q, k, v, dout, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
                         mask->col_idx, tcolptr, trowidx, counters, reinterpret_cast<int32_t*>(base + w.cost),

@@ -72,26 +72,34 @@ struct AttnBf16Args {
   const int32_t* bounds;   // 9 entries
   Geom g;
   float c_log2;        // log2(e) / sqrt(D)
-  uint32_t magic_wp, magic_hp;   // floor(2^32/d)+1: exact n/d = (n*magic)>>32 for n, d < 2^16
+  uint32_t magic_wp, magic_hp;   // floor(2^31/d)+1: exact n/d = (n*magic)>>31 for n, d <= 4096 (d = 1 included)
   int32_t pxmul;                 // rows per patch column step: 8 (original order) or 64 (fractal, magic_wp = 0)
   int32_t pairs;       // query-block pairs per head = ceil(S/2)
   int32_t items;       // B*heads*pairs
 };
 
-constexpr int kD = 128;
-constexpr int kVt = 16384;             // V^T offset inside a stage
-constexpr int kTile = 16384;           // one K or V^T tile
-constexpr int kVRing = 3 * kTile;      // K ring: 3 slots at 0; V^T ring: 2 slots from here
-constexpr int kLds = 5 * kTile;        // 80 KB: two workgroups fill a CU's 160 KB
-constexpr int kItemSlot = kLds - 4;    // the item index, only live between items (last word of V^T slot 1)
+// Tile geometry for head dim D (128 or 64): a K tile is 64 rows x 2D bytes, a V^T
+// tile D rows x 128 bytes; both are moved by kLoads direct 16-byte loads per thread.
+template <int D>
+struct Shape {
+  static constexpr int kTile = 64 * D * 2;            // one K or V^T tile (bytes)
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per K row
+  static constexpr int kLoads = kTile / (256 * 16);   // direct loads per thread per tile
+  static constexpr int kVRing = 3 * kTile;            // K ring: 3 slots at 0; V^T ring: 2 slots from here
+  static constexpr int kLds = 5 * kTile;              // 80 KB at D = 128: two workgroups fill a CU's 160 KB
+  static constexpr int kItemSlot = kLds - 4;          // the item index, only live between items
+};
 constexpr float kLazy = 8.0f;          // log2 slack before the reference max is raised
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-// K tile: 64 rows x 256 B, 16-byte chunk c of row k stored at chunk c ^ (k & 15).
-__device__ __forceinline__ int k_lds(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-// V^T tile: 128 rows x 128 B, chunk c of row d stored at c ^ ((d >> 1) & 7).
-__device__ __forceinline__ int v_lds(int row, int chunk) {
-  return kVt + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+// K tile: 64 rows x 2D bytes, 16-byte chunk c of row k stored at chunk c ^ (k mod D/8).
+template <int D>
+__device__ __forceinline__ int k_lds(int row, int chunk) {
+  return row * (2 * D) + ((chunk ^ (row & (D / 8 - 1))) << 4);
 }
+// V^T tile: 128 rows x 128 B, chunk c of row d stored at c ^ ((d >> 1) & 7).
+__device__ __forceinline__ int v_lds(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -108,12 +116,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic) {
-  return (uint32_t)(((uint64_t)n * magic) >> 32);
+  return (uint32_t)(((uint64_t)n * magic) >> 31);
 }
 
 // First token row (in the tensor's own layout) of block j; token m of the block
 // sits rs*(m/8) + m%8 rows further (rs = W for original order, 8 for fractal).
-// Block ids and patch counts are < 2^16, so the divisions use multiply-high.
+// Block ids and patch counts are <= 4096, so the divisions use multiply-high
+// with a 31-bit shift (exact for every divisor, 1 included).
 __device__ __forceinline__ int block_base_row(const AttnBf16Args& a, int j) {
   const Geom& g = a.g;
   const int rest = (int)div_magic((uint32_t)j, a.magic_wp);   // 0 in fractal order (magic_wp = 0)
@@ -123,9 +132,22 @@ __device__ __forceinline__ int block_base_row(const AttnBf16Args& a, int j) {
   return (t * g.H + py * 8) * g.W + px * a.pxmul;
 }
 
-template <bool kShift>   // whether the CSR carries per-entry logit shifts
+// Hides a value from the optimiser (a VGPR operand of an empty asm statement).  A
+// plain device function, so that the VGPR constraint is never checked for the host
+// inside the kernel template.
+__device__ __forceinline__ void opaque_vgpr(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// The body is compiled for the device only: instantiated in the host pass, its
+// LDS address-space casts and VGPR asm operands (dependent on D) would make the
+// instantiation invalid there and drop the launch stub.
+template <int D, bool kShift>   // head dim; whether the CSR carries per-entry logit shifts
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // K ring (3 slots) + V^T ring (2 slots)
+#if defined(__HIP_DEVICE_COMPILE__)
+  using Sh = Shape<D>;
+  constexpr int kTile = Sh::kTile, kVRing = Sh::kVRing, kLoads = Sh::kLoads, kItemSlot = Sh::kItemSlot;
+  constexpr int kQS = D / 16;      // k-steps of the QK product
+  constexpr int kOU = D / 32;      // 32-channel blocks of the output
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Sh::kLds];   // K ring (3 slots) + V^T ring (2 slots)
   int& s_item = *(int*)(smem + kItemSlot);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,13 +160,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   const int rs = g.layout == 1 ? 8 : g.W;
 
   // per-thread byte offsets of this thread's direct-load chunks (independent of the tile)
-  int koff[4], voff[4];
+  int koff[kLoads], voff[kLoads];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = (4 * wave + u) * 64 + lane;
-    const int m = c >> 4;                                   // key row in the tile
-    const int lc = (lane & 15) ^ (m & 15);                  // logical chunk stored at this slot
-    koff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
+  for (int u = 0; u < kLoads; ++u) {
+    const int c = (kLoads * wave + u) * 64 + lane;
+    const int m = c / Sh::kChunks;                          // key row in the tile
+    const int lc = (c % Sh::kChunks) ^ (m & (Sh::kChunks - 1));   // logical chunk stored at this slot
+    koff[u] = (((m >> 3) * rs + (m & 7)) * D + lc * 8) * 2;
     const int d = c >> 3;                                   // V^T row
     const int lv = (lane & 7) ^ ((d >> 1) & 7);
     voff[u] = d * 128 + lv * 16;
@@ -153,18 +175,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
   // LDS addresses of this lane's MFMA operands in stage 0: the row term of the
   // swizzle is the same for both key halves (K) and all four row blocks (V^T), so
   // a K read is kaddr[s] plus an immediate and a V^T read vaddr[s] plus one
-  uint32_t kaddr[8], vaddr[4];
+  uint32_t kaddr[kQS], vaddr[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) kaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + k_lds(l32, 2 * s + h));
+  for (int s = 0; s < kQS; ++s) kaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + k_lds<D>(l32, 2 * s + h));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) vaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + kVRing - kVt + v_lds(l32, 2 * s + h));
+  for (int s = 0; s < 4; ++s) vaddr[s] = (uint32_t)(uintptr_t)(lds_void*)(smem + kVRing + v_lds(l32, 2 * s + h));
   // opaque to the optimiser: otherwise it splits each address back into the array
   // base (a relocated symbol, so never an immediate) plus the offset, and adds the
   // two before every read
 #pragma unroll
-  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kaddr[s]));
+  for (int s = 0; s < kQS; ++s) opaque_vgpr(kaddr[s]);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(vaddr[s]));
+  for (int s = 0; s < 4; ++s) opaque_vgpr(vaddr[s]);
 
   // this workgroup's XCD and its stretch of the item order (the schedule kernels
   // below balance the stretches by estimated cost and put long items first)
@@ -185,8 +207,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     int pa = a.row_ptr[r0], ea = a.row_ptr[r0 + 1];
     int pb = two ? a.row_ptr[r0 + 1] : 0, eb = two ? a.row_ptr[r0 + 2] : 0;
 
-    const uint8_t* kh = (const uint8_t*)(a.k + (size_t)bh * g.L * kD);
-    const uint8_t* vth = (const uint8_t*)(a.vt + (size_t)bh * g.S * kD * 64);
+    const uint8_t* kh = (const uint8_t*)(a.k + (size_t)bh * g.L * D);
+    const uint8_t* vth = (const uint8_t*)(a.vt + (size_t)bh * g.S * D * 64);
 
     // Each key list is read through a 64-entry window held one entry per lane and
     // indexed with readlane, so the union walk costs no memory round trip per tile;
@@ -247,49 +269,57 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     // is a constant VGPR offset, the tile part a scalar offset; loads past the
     // head's extent return zeros instead of touching other memory
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, g.L * kD * 2, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, g.L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vth, (short)0, g.S * kD * 64 * 2, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)vth, (short)0, g.S * D * 64 * 2, 0x00020000);
     // a tile id past the end of the walk is clamped: every step issues exactly
-    // four K and four V^T loads per thread, which keeps the vmcnt arithmetic exact
+    // kLoads K and kLoads V^T loads per thread, which keeps the vmcnt arithmetic exact
     auto issue_k = [&](int j, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
       const int jc = min(max(j, 0), g.S - 1);
-      const int ks = block_base_row(a, jc) * kD * 2;
+      const int ks = block_base_row(a, jc) * D * 2;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * kTile + (4 * wave + u) * 1024), 16,
+      for (int u = 0; u < kLoads; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * kTile + (kLoads * wave + u) * 1024), 16,
                                                  koff[u], ks, 0, 0);
     };
     auto issue_v = [&](int j, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
       const int jc = min(max(j, 0), g.S - 1);
-      const int vs = jc * kD * 64 * 2;
+      const int vs = jc * D * 64 * 2;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + kVRing + slot * kTile + (4 * wave + u) * 1024),
+      for (int u = 0; u < kLoads; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + kVRing + slot * kTile + (kLoads * wave + u) * 1024),
                                                  16, voff[u], vs, 0, 0);
     };
     // wait for this thread's older loads, then a plain barrier (the compiler's own
     // barrier would first wait for every outstanding load, including the ones
     // meant to stay in flight); lgkmcnt(0) keeps LDS writes ordered as well
-    auto wait_barrier4 = [&]() {
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto wait_barrier4 = [&]() {   // the newest kLoads K loads stay in flight
+      if constexpr (kLoads == 4)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    bf16x8 qreg[8];
+    bf16x8 qreg[kQS];
     if (has_q) {
       const int qtok = block_base_row(a, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
-      const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
+      const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * D + 8 * h;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qreg[s] = *(const bf16x8*)(qrow + 16 * s);
+      for (int s = 0; s < kQS; ++s) qreg[s] = *(const bf16x8*)(qrow + 16 * s);
     }
-    f32x16 oacc[4];
+    f32x16 oacc[kOU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kOU; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+    // l_run: sum of the float32 P (for the LSE); l_pv: sum of the bf16-rounded P that
+    // the PV product uses, so that O = sum bf16(P) v / sum bf16(P) is a convex
+    // combination of the kept V rows with exactly the weights the MFMA applied (P of
+    // the dominant key is not exactly 1 under the lazy reference, and its 2^-9
+    // rounding would otherwise show at full size in O)
+    float m_ref = -INFINITY, l_run = 0.f, l_pv = 0.f;
 
     // tiles j (current), j1, j2: K of a tile is loaded two steps ahead of its QK
     // products, V^T one step ahead (issued first, so a step's wait can leave the
@@ -322,8 +352,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * 8192);
+          for (int s = 0; s < kQS; ++s) {
+            const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * (kTile / 2));
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
           }
         }
@@ -344,8 +374,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
           m_ref = m_new;
           l_run *= alpha;
+          l_pv *= alpha;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < kOU; ++u)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
         }
@@ -360,8 +391,15 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
+          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
+          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
+          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int u = 0; u < kOU; ++u) {
             const bf16x8 av = *(lds_bf16x8*)(uintptr_t)(vaddr[s] + VS * kTile + u * 4096);
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
           }
@@ -393,17 +431,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     const int qrow = 32 * wq + l32;
     if (has_q) {
       l_run = pair_sum(l_run);
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // an empty row yields zeros
-      uint8_t* ob = smem + qb * 16384;
+      l_pv = pair_sum(l_pv);
+      const float inv = l_pv > 0.f ? 1.f / l_pv : 0.f;   // an empty row yields zeros
+      uint8_t* ob = smem + qb * (kTile);       // block qb's 64 x 2D bytes of O
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kOU; ++u) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int unit = 8 * u + 2 * rq + h;
           uint2 w;
           w.x = pack_bf16x2(oacc[u][4 * rq + 0] * inv, oacc[u][4 * rq + 1] * inv);
           w.y = pack_bf16x2(oacc[u][4 * rq + 2] * inv, oacc[u][4 * rq + 3] * inv);
-          *(uint2*)(ob + qrow * 256 + ((unit ^ (qrow & 31)) << 3)) = w;
+          *(uint2*)(ob + qrow * (2 * D) + ((unit ^ (qrow & (D / 4 - 1))) << 3)) = w;
         }
       }
       if (a.lse && h == 0) {
@@ -415,22 +454,25 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     {
       const int sb = tid >> 7;                 // block of the pair this thread stores
       if (sb == 0 || two) {
+        constexpr int kCh = D / 8;             // 16-byte chunks per output row
+        constexpr int kRowsPer = 128 / kCh;    // rows one pass of 128 threads covers
         const int t7 = tid & 127;
-        const int lchunk = t7 & 15;
+        const int lchunk = t7 % kCh;
         const int base = block_base_row(a, i0 + sb);
-        uint16_t* oh = a.o + (size_t)bh * g.L * kD;
-        const uint8_t* ob = smem + sb * 16384;
+        uint16_t* oh = a.o + (size_t)bh * g.L * D;
+        const uint8_t* ob = smem + sb * kTile;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = (t7 >> 4) + 8 * u;
-          const uint2 lo = *(const uint2*)(ob + row * 256 + (((2 * lchunk) ^ (row & 31)) << 3));
-          const uint2 hi = *(const uint2*)(ob + row * 256 + (((2 * lchunk + 1) ^ (row & 31)) << 3));
+        for (int u = 0; u < 64 / kRowsPer; ++u) {
+          const int row = t7 / kCh + kRowsPer * u;
+          const uint2 lo = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk) ^ (row & (D / 4 - 1))) << 3));
+          const uint2 hi = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk + 1) ^ (row & (D / 4 - 1))) << 3));
           const int tok = base + (row >> 3) * rs + (row & 7);
-          *(uint4*)(oh + (size_t)tok * kD + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          *(uint4*)(oh + (size_t)tok * D + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
       }
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -602,16 +644,23 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.bounds = bounds;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
+  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 31) / (uint64_t)g.Wp + 1);
   a.pxmul = g.layout == 1 ? 64 : 8;
-  a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
+  a.magic_hp = (uint32_t)((1ull << 31) / (uint64_t)g.Hp + 1);
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
   const int grid = ((num_cu * 2 + 7) / 8) * 8;   // two resident workgroups per CU, a multiple of 8 XCDs
-  if (shift)
-    attn_bf16_kernel<true><<<grid, 256, 0, s>>>(a);
-  else
-    attn_bf16_kernel<false><<<grid, 256, 0, s>>>(a);
+  if (g.D == 64) {
+    if (shift)
+      attn_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    else
+      attn_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (shift)
+      attn_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else
+      attn_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -55,6 +55,8 @@ constexpr int kVRing = 3 * kTile;  // K ring: 3 tiles at 0; V ring: 2 tiles from
 constexpr int kLds = 5 * kTile;    // 80 KB: two workgroups fill a CU's 160 KB
 constexpr int kItemSlot = kLds - 4;     // the item index, only live between items (last word of V slot 1)
 constexpr float kLazy = 8.0f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct Args {
   const uint16_t* q;
@@ -69,7 +71,7 @@ struct Args {
   const int32_t* bounds;   // 9 entries
   Geom g;
   float c_log2;
-  uint32_t magic_wp, magic_hp;   // fractal order: magic_wp = 0
+  uint32_t magic_wp, magic_hp;   // floor(2^31/d)+1 (exact n/d = (n*magic)>>31 for n, d <= 4096); fractal order: magic_wp = 0
   int32_t pxmul, rs;             // row offset of patch column px (8 or 64) and of patch row m / 8 (W or 8)
   int32_t groups;                // L / 4 per head
 };
@@ -89,11 +91,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic) {
-  return (uint32_t)(((uint64_t)n * magic) >> 32);
+  return (uint32_t)(((uint64_t)n * magic) >> 31);
 }
 
 // First row (tensor layout) of block j: fractal order -> 64 j; original order ->
-// the patch's top-left token (block ids and patch counts < 2^16: multiply-high).
+// the patch's top-left token (block ids and patch counts <= 4096: multiply-high).
 __device__ __forceinline__ int block_base_row(const Args& a, int j) {
   const Geom& g = a.g;
   if (g.layout == 1) return j * 64;
@@ -219,7 +221,10 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+    // l_run: sum of the float32 P (for the LSE); l_pv: sum of the bf16-rounded P the
+    // PV product uses, the normaliser of O (O is then a convex combination of the
+    // kept V rows with exactly the weights the MFMA applied)
+    float m_ref = -INFINITY, l_run = 0.f, l_pv = 0.f;
 
     if (ntiles > 0) {
       // ids: tile t+1 as scalars (its V is issued at step t), tile t+2 in a VGPR
@@ -283,6 +288,7 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
             const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
             m_ref = m_new;
             l_run *= alpha;
+            l_pv *= alpha;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -294,6 +300,13 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -m_ref));
             l_run += p;
             pbv[e >> 3][e & 7] = (__bf16)p;
+          }
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
           }
 #pragma unroll
           for (int s = 0; s < 2; ++s)
@@ -331,17 +344,17 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
     // merge the two key halves of each query range, then normalise and store
     __syncthreads();
     float* xo = (float*)smem + wq * (64 * 64);               // partner accumulators, [reg][lane]
-    float2* xm = (float2*)(smem + 32768) + wq * 64;          // partner (m_ref, l_run)
+    float4* xm = (float4*)(smem + 32768) + wq * 64;          // partner (m_ref, l_run, l_pv)
     if (kh == 1) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 16; ++e) xo[(16 * u + e) * 64 + lane] = oacc[u][e];
-      xm[lane] = make_float2(m_ref, l_run);
+      xm[lane] = make_float4(m_ref, l_run, l_pv, 0.f);
     }
     __syncthreads();
     if (kh == 0) {
-      const float2 pm = xm[lane];
+      const float4 pm = xm[lane];
       const float m_tot = fmaxf(m_ref, pm.x);
       const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_tot);
       const float a1 = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - m_tot);
@@ -350,12 +363,13 @@ __global__ void __launch_bounds__(256, 2) attn_groups_bf16_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[u][e] = a0 * oacc[u][e] + a1 * xo[(16 * u + e) * 64 + lane];
       l_run = pair_sum(a0 * l_run + a1 * pm.y);
+      l_pv = pair_sum(a0 * l_pv + a1 * pm.z);
       m_ref = m_tot;
     }
     __syncthreads();
     const int qrow = 32 * wq + l32;
     if (kh == 0) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;     // an empty row yields zeros
+      const float inv = l_pv > 0.f ? 1.f / l_pv : 0.f;       // an empty row yields zeros
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -455,8 +469,8 @@ hipError_t launch_attn_groups_bf16(const Geom& g, const void* q, const void* k, 
   a.bounds = bounds;
   a.g = g;
   a.c_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)g.Wp + 1);
-  a.magic_hp = (uint32_t)((1ull << 32) / (uint64_t)g.Hp + 1);
+  a.magic_wp = g.layout == 1 ? 0u : (uint32_t)((1ull << 31) / (uint64_t)g.Wp + 1);
+  a.magic_hp = (uint32_t)((1ull << 31) / (uint64_t)g.Hp + 1);
   a.pxmul = g.layout == 1 ? 64 : 8;
   a.rs = g.layout == 1 ? 8 : g.W;
   a.groups = g.L / 4;

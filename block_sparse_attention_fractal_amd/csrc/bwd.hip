@@ -4,22 +4,32 @@
 //
 //   P = softmax over the kept keys of z = q.k / sqrt(D)   (recomputed from lse)
 //   dV_k = sum_n P[n,k] dO_n          dP[n,k] = dO_n . v_k
-//   dZ[n,k] = P[n,k] (dP[n,k] - Delta_n),   Delta_n = dO_n . o_n
+//   dZ[n,k] = P[n,k] (dP[n,k] - Delta_n),   Delta_n = sum_k P[n,k] dP[n,k]
 //   dQ_n = sum_k dZ[n,k] k_k / sqrt(D)      dK_k = sum_n dZ[n,k] q_n / sqrt(D)
 //
-// Two passes, no atomics on the gradients (deterministic):
+// The row term Delta is formed here from the very P and dP values the dQ pass
+// uses (Delta = sum P dP / sum P over the query's kept keys), not as dO . o from
+// a stored output: the dZ of one query then sum to zero up to float32 rounding,
+// so a component common to every key (the positional term of the video tokens)
+// cancels from dQ.  A rounded output in the row term breaks that sum and leaks
+// the common component into dQ at the percent level.
+//
+// Three passes, no atomics on the gradients (deterministic):
+//   * Delta: query-major over the CSR, the dQ pass's walk and products without
+//     the dQ product (S^T = K Q^T and dP^T = V dO^T), sums per query;
 //   * dQ: query-major over the CSR, a pair of query blocks per workgroup (the
 //     forward kernel's schedule): S^T = K Q^T and dP^T = V dO^T with the
 //     32x32x16 bf16 MFMA (each lane holds 32 keys of one query), dZ^T in
-//     registers, then dQ^T += K^T dZ^T with K^T pre-transposed in HBM in the
-//     same key order as the forward's V^T;
+//     registers, then dQ^T += K^T dZ^T with K^T read from the natural K tile by
+//     transposing LDS reads;
 //   * dK, dV: key-major over the transposed mask (built here: a bitmap per key
 //     block, counted, scanned and compacted), a pair of key blocks per
 //     workgroup: S = Q K^T and dP = dO V^T with the key fragments in registers
 //     (each lane holds 32 queries of one key), then dV^T += dO^T P and
 //     dK^T += Q^T dZ with Q^T and dO^T pre-transposed.
 // float32 tensors take two plain kernels with float64 arithmetic (accuracy
-// rather than speed, as in the forward's float32 path).
+// rather than speed, as in the forward's float32 path); their dQ kernel forms
+// Delta the same way in a first walk over the row.
 #include <math.h>
 
 #include <algorithm>
@@ -58,7 +68,7 @@ struct Args {
   const uint16_t* dout;
   const uint16_t* qt;      // prepared transposes [B*nh, S, D, 64]
   const uint16_t* dot;
-  const float2* ld;        // per token: (lse * log2 e, Delta)
+  float2* ld;              // per token: (lse * log2 e, Delta); Delta written by the Delta pass
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -160,7 +170,12 @@ __device__ __forceinline__ void store_pair(uint8_t* stage, const f32x16 (&acc)[4
 // dQ pass (bf16).  Stage: natural K | natural V, 32 KB; two stages; two
 // workgroups per CU (249 VGPRs).  The K^T operand of the dQ product comes from
 // the natural K tile through gfx950's transposing LDS reads.
+// kDelta: the Delta pass -- the same walk, loads and S / dP products, but only
+// sum P and sum P dP per query are kept, and Delta = sum P dP / sum P is stored
+// (P computed by the same instructions as in the dQ pass, so both passes see
+// bit-identical P and dP).
 // ---------------------------------------------------------------------------
+template <bool kDelta>
 __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_dq[4 * kTile];
   uint8_t* const stage0 = smem_dq;
@@ -229,8 +244,9 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
 
     bf16x8 qreg[8], doreg[8];
     float lse2 = 0.f, dlt = 0.f;
+    float sum_p = 0.f, sum_pdp = 0.f;   // Delta pass: per-lane partial sums
+    const int qtok = block_base_row(g, min(i0 + qb, g.S - 1)) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
     if (has_q) {
-      const int qtok = block_base_row(g, i0 + qb) + ((32 * wq + l32) >> 3) * rs + (l32 & 7);
       const uint16_t* qrow = a.q + ((size_t)bh * g.L + qtok) * kD + 8 * h;
       const uint16_t* drow = a.dout + ((size_t)bh * g.L + qtok) * kD + 8 * h;
 #pragma unroll
@@ -240,7 +256,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
       }
       const float2 ld = a.ld[(size_t)bh * g.L + qtok];
       lse2 = ld.x;
-      dlt = ld.y;
+      if (!kDelta) dlt = ld.y;
     }
     f32x16 acc[4];
 #pragma unroll
@@ -277,33 +293,42 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
             const bf16x8 av = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
             pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc, 0, 0, 0);
           }
-          // dZ = hi + lo, two bf16 terms: the dZ of one query sum to zero, so dQ is a
-          // small difference of large terms when K has a large common part, and a
-          // single bf16 rounding of dZ (2^-9) would show in it at the percent level.
-          bf16x8 dsh[2], dsl[2];
+          if constexpr (kDelta) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -lse2));
-            const float ds = p * (pacc[e] - dlt);
-            const __bf16 hi = (__bf16)ds;
-            dsh[e >> 3][e & 7] = hi;
-            dsl[e >> 3][e & 7] = (__bf16)(ds - (float)hi);
-          }
-          // K^T operand straight from the natural K tile with transposing LDS reads:
-          // in each 16-lane group, source lane j reads keys-row kbase + j/4 at channels
-          // dbase + 4(j%4) .. +3 and lane i receives keys kbase .. kbase+3 of channel
-          // dbase + i; two reads give the 8 keys of a lane's operand
+            for (int e = 0; e < 16; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -lse2));
+              sum_p += p;
+              sum_pdp = fmaf(p, pacc[e], sum_pdp);
+            }
+          } else {
+            // dZ = hi + lo, two bf16 terms: the dZ of one query sum to zero, so dQ is a
+            // small difference of large terms when K has a large common part, and a
+            // single bf16 rounding of dZ (2^-9) would show in it at the percent level.
+            bf16x8 dsh[2], dsl[2];
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int s = 2 * t + s2;
+            for (int e = 0; e < 16; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -lse2));
+              const float ds = p * (pacc[e] - dlt);
+              const __bf16 hi = (__bf16)ds;
+              dsh[e >> 3][e & 7] = hi;
+              dsl[e >> 3][e & 7] = (__bf16)(ds - (float)hi);
+            }
+            // K^T operand straight from the natural K tile with transposing LDS reads:
+            // in each 16-lane group, source lane j reads keys-row kbase + j/4 at channels
+            // dbase + 4(j%4) .. +3 and lane i receives keys kbase .. kbase+3 of channel
+            // dbase + i; two reads give the 8 keys of a lane's operand
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 0)));
-              const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 1)));
-              const bf16x8 at =
-                  __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsh[s2], acc[u], 0, 0, 0);
-              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsl[s2], acc[u], 0, 0, 0);
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int s = 2 * t + s2;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 0)));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 1)));
+                const bf16x8 at =
+                    __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsh[s2], acc[u], 0, 0, 0);
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, dsl[s2], acc[u], 0, 0, 0);
+              }
             }
           }
         }
@@ -317,7 +342,14 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
       if (j == 0x7fffffff) break;
       step(stage1, stage0);
     }
-    store_pair(stage0, acc, a.inv_sqrt_d, has_q, wave, lane, tid, g, i0, two, a.dq + (size_t)bh * g.L * kD);
+    if constexpr (kDelta) {
+      // lanes l32 and l32 + 32 hold complementary keys of the same query
+      sum_p += __shfl_xor(sum_p, 32);
+      sum_pdp += __shfl_xor(sum_pdp, 32);
+      if (has_q && h == 0) a.ld[(size_t)bh * g.L + qtok].y = sum_pdp / sum_p;
+    } else {
+      store_pair(stage0, acc, a.inv_sqrt_d, has_q, wave, lane, tid, g, i0, two, a.dq + (size_t)bh * g.L * kD);
+    }
   }
 }
 
@@ -499,7 +531,7 @@ using ZT = typename std::conditional<D == 64, double, float>::type;
 template <int D>
 __global__ void __launch_bounds__(256) dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                      const float* __restrict__ v, const float* __restrict__ dout,
-                                                     const float2* __restrict__ ld, float* __restrict__ dq,
+                                                     float2* __restrict__ ld, float* __restrict__ dq,
                                                      const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
                                                      Geom g, double scale) {
   constexpr int DS = D / 4;
@@ -520,8 +552,39 @@ __global__ void __launch_bounds__(256) dq_f32_kernel(const float* __restrict__ q
     Qs[row][d] = q[off];
     Os[row][d] = dout[off];
   }
-  const float2 l = ld[(size_t)bh * g.L + qtok];
-  const double lse = (double)l.x * 0.69314718055994530942, dlt = l.y;
+  const double lse = (double)ld[(size_t)bh * g.L + qtok].x * 0.69314718055994530942;
+  // Delta = sum P dP / sum P over the row's keys, from the P and dP the main walk
+  // recomputes below (thread (qi, sl) sums keys sl, sl + 4, ...; the four slices
+  // of a query are neighbouring lanes)
+  double sp = 0.0, spd = 0.0;
+  for (int it = ptr[r]; it < ptr[r + 1]; ++it) {
+    const int j = min(max(idx[it], 0), g.S - 1);
+    __syncthreads();
+    for (int e = tid; e < 64 * D; e += 256) {
+      const int row = e / D, d = e % D;
+      const size_t off = hoff + (size_t)block_token_row(g, j, row) * D + d;
+      Ks[row][d] = k[off];
+      Vs[row][d] = v[off];
+    }
+    __syncthreads();
+    for (int c = 0; c < 16; ++c) {
+      const int kk = sl + 4 * c;
+      double s = 0.0, dp = 0.0;
+      for (int d = 0; d < D; ++d) {
+        s = __fma_rn((double)Qs[qi][d], (double)Ks[kk][d], s);
+        dp = __fma_rn((double)Os[qi][d], (double)Vs[kk][d], dp);
+      }
+      const double p = exp(s * scale - lse);
+      sp += p;
+      spd = __fma_rn(p, dp, spd);
+    }
+  }
+  sp += __shfl_xor(sp, 1, 4);
+  sp += __shfl_xor(sp, 2, 4);
+  spd += __shfl_xor(spd, 1, 4);
+  spd += __shfl_xor(spd, 2, 4);
+  const double dlt = spd / sp;
+  if (sl == 0) ld[(size_t)bh * g.L + qtok].y = (float)dlt;   // for the dK/dV kernel
   double acc[DS];
 #pragma unroll
   for (int d = 0; d < DS; ++d) acc[d] = 0.0;
@@ -626,30 +689,12 @@ __global__ void __launch_bounds__(256) dkdv_f32_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// helpers: per-token (lse * log2 e, dO.o), the transposed mask
+// helpers: per-token lse * log2 e, the transposed mask
 // ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ float to_f(T x);
-template <>
-__device__ __forceinline__ float to_f<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-template <>
-__device__ __forceinline__ float to_f<float>(float x) { return x; }
-
-// 16 lanes per token row, each summing D/16 products in float32
-template <typename T>
-__global__ void __launch_bounds__(256) delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                    const float* __restrict__ lse, float2* __restrict__ ld,
-                                                    int64_t ntok, int D) {
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-  const int sub = threadIdx.x & 15;
-  float s = 0.f;
-  if (row < ntok)
-    for (int d = sub; d < D; d += 16) s = fmaf(to_f<T>(o[row * D + d]), to_f<T>(dout[row * D + d]), s);
-  s += __shfl_xor(s, 1, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 8, 16);
-  if (row < ntok && sub == 0) ld[row] = make_float2(lse[row] * 1.44269504088896341f, s);
+// per token: lse * log2(e) (the Delta half is written by the Delta pass)
+__global__ void __launch_bounds__(256) lse2_kernel(const float* __restrict__ lse, float2* __restrict__ ld, int64_t ntok) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row < ntok) ld[row] = make_float2(lse[row] * 1.44269504088896341f, 0.f);
 }
 
 __global__ void __launch_bounds__(256) zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -684,15 +729,10 @@ __global__ void __launch_bounds__(256) popcount_rows_kernel(const uint32_t* __re
 
 }  // namespace bwd
 
-hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, const float* lse, float2* ld,
-                                const int32_t* row_ptr, const int32_t* col_idx, uint32_t* tbits, int words,
-                                int32_t* tcounts, hipStream_t s) {
+hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, const int32_t* row_ptr,
+                                const int32_t* col_idx, uint32_t* tbits, int words, int32_t* tcounts, hipStream_t s) {
   const int64_t ntok = (int64_t)g.B * g.nh * g.L;
-  const unsigned dgrid = (unsigned)((ntok * 16 + 255) / 256);
-  if (g.dtype == BSA_BF16)
-    bwd::delta_kernel<uint16_t><<<dgrid, 256, 0, s>>>((const uint16_t*)o, (const uint16_t*)dout, lse, ld, ntok, g.D);
-  else
-    bwd::delta_kernel<float><<<dgrid, 256, 0, s>>>((const float*)o, (const float*)dout, lse, ld, ntok, g.D);
+  bwd::lse2_kernel<<<(unsigned)((ntok + 255) / 256), 256, 0, s>>>(lse, ld, ntok);
   const int64_t nbits = g.rows * words;
   bwd::zero_u32_kernel<<<(unsigned)std::min<int64_t>((nbits + 255) / 256, 65536), 256, 0, s>>>(tbits, nbits);
   const unsigned rgrid = (unsigned)((g.rows + 3) / 4);
@@ -702,7 +742,7 @@ hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, 
 }
 
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           const void* qt, const void* dot, float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s) {
@@ -747,10 +787,13 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   if (e != hipSuccess) return e;
   a.ptr = row_ptr;
   a.idx = col_idx;
-  a.counters = counters;
+  a.counters = counters + 16;
   a.order = order_q;
   a.bounds = bounds;
-  bwd::dq_bf16_kernel<<<((num_cu * 2 + 7) / 8) * 8, 256, 0, s>>>(a);   // two workgroups per CU
+  const int grid2 = ((num_cu * 2 + 7) / 8) * 8;   // two workgroups per CU
+  bwd::dq_bf16_kernel<true><<<grid2, 256, 0, s>>>(a);    // Delta
+  a.counters = counters;
+  bwd::dq_bf16_kernel<false><<<grid2, 256, 0, s>>>(a);   // dQ
   e = launch_attn_schedule(g, tcolptr, trowidx, cost, order_k, bounds + 16, s);
   if (e != hipSuccess) return e;
   a.ptr = tcolptr;

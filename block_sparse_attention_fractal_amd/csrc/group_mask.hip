@@ -381,9 +381,9 @@ __global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restr
     }
   }
   __syncthreads();
-  if (win_t >= 0)
-    for (int j = tid; j < SG; j += kNT)
-      if (in_window(g, i, j / gpb, win_t, win_h, win_w)) set_bit(j);
+  if (win_t >= 0)   // every group of every window block (gpb groups per block)
+    for (int x = 0; x < gpb; ++x)
+      for_each_window_block(g, i, win_t, win_h, win_w, tid, kNT, [&](int jb) { set_bit(jb * gpb + x); });
   __syncthreads();
   unsigned long long pc = 0;
   for (int x = tid; x < words; x += kNT) {

@@ -18,6 +18,32 @@ hipError_t launch_permute_table(const Geom& g, const int32_t* table, const void*
 hipError_t launch_prep_vt(const Geom& g, const void* v, void* vt, hipStream_t s);
 // Block means of Q and K in float64 -> qp, kp [B*nh, S, D].
 hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, double* kp, hipStream_t s);
+// Screen operands of the pooled blocks (see mask_screen.hip): fp16 hi / lo of the
+// power-of-two scaled centred vectors ([rows][2][D]), channel means, scale
+// exponents, query-block norms, and per head (max mean, min mean, max norm) of
+// the key blocks as order-preserving 64-bit keys.
+struct ScreenOps {
+  _Float16* qs;
+  _Float16* ks;
+  double* qmu;
+  double* kmu;
+  double* qn;
+  int32_t* qe;
+  int32_t* ke;
+  uint64_t* hstat;
+};
+// The screen operands of the pooled blocks (launch_pool's qp, kp); also clears nflag.
+hipError_t launch_screen_ops(const Geom& g, const double* qp, const double* kp, const ScreenOps& ops, int32_t* nflag,
+                             hipStream_t s);
+// Screened reduced map + CDF cut + window union -> bitmap rows and counts; rows it
+// cannot decide are appended to flag_list (count in nflag) for the float64 path.
+hipError_t launch_screen_select(const Geom& g, const ScreenOps& ops, const double* qp, const double* kp, double thr,
+                                double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+                                int words, int32_t* flag_list, int32_t* nflag, hipStream_t s);
+// The float64 cut of the listed rows (float64 logits computed per row on the fly).
+hipError_t launch_fallback_select(const Geom& g, const double* qp, const double* kp, double thr, double lambda,
+                                  int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts, int words,
+                                  const int32_t* flag_list, const int32_t* nflag, hipStream_t s);
 // Block logits z[bh, i, j] = qp_i . kp_j / sqrt(D) in float64.
 hipError_t launch_block_logits(const Geom& g, const double* qp, const double* kp, double* z, hipStream_t s);
 // Row softmax of z -> probs (inspection entry point).
@@ -52,15 +78,15 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
                             const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s);
-// Backward: per-token (lse*log2e, dO.o) into ld, and the transposed mask's bitmap
+// Backward: per-token lse*log2e into ld (.x), and the transposed mask's bitmap
 // and per-key-block counts (scan and compact them to get the transposed CSR).
-hipError_t launch_backward_prep(const Geom& g, const void* o, const void* dout, const float* lse, float2* ld,
-                                const int32_t* row_ptr, const int32_t* col_idx, uint32_t* tbits, int words,
-                                int32_t* tcounts, hipStream_t s);
-// Backward: dQ over the CSR, dK/dV over the transposed CSR (qt, dot: prepared
-// transposes of K, Q, dO for bf16; counters: 16 ints, zeroed).
+hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, const int32_t* row_ptr,
+                                const int32_t* col_idx, uint32_t* tbits, int words, int32_t* tcounts, hipStream_t s);
+// Backward: the row term Delta (into ld .y) and dQ over the CSR, dK/dV over the
+// transposed CSR (qt, dot: prepared transposes of Q, dO for bf16; counters: 24
+// ints, zeroed).
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* qt, const void* dot, const float2* ld, void* dq, void* dk,
+                           const void* qt, const void* dot, float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s);

@@ -228,80 +228,16 @@ hipError_t launch_block_softmax(const Geom& g, const double* z, double* probs, h
 // ---------------------------------------------------------------------------
 constexpr int kMaxS = 4096;
 
-// Wavefront-wide reduction with DPP moves inside each row of 16 lanes and lane
-// swaps across rows and halves; every lane ends with the result.
-__device__ __forceinline__ uint32_t dpp_step(uint32_t v, int step) {
-  switch (step) {
-    case 0: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);   // lanes ^ 1
-    case 1: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);   // lanes ^ 2
-    case 2: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
-    default: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false); // row mirror
-  }
-}
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_reduce(T v, int lane, Op op) {
-  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
-  constexpr int kWords = sizeof(T) / 4;
-  auto as_words = [](T x, uint32_t* w) { __builtin_memcpy(w, &x, sizeof(T)); };
-  auto from_words = [](const uint32_t* w) {
-    T x;
-    __builtin_memcpy(&x, w, sizeof(T));
-    return x;
-  };
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    uint32_t w[kWords];
-    as_words(v, w);
-#pragma unroll
-    for (int q = 0; q < kWords; ++q) w[q] = dpp_step(w[q], st);
-    v = op(v, from_words(w));
-  }
-  {
-    uint32_t w[kWords];
-    as_words(v, w);
-#pragma unroll
-    for (int q = 0; q < kWords; ++q) {
-      const auto r = __builtin_amdgcn_permlane16_swap(w[q], w[q], false, false);
-      w[q] = (lane & 16) ? r[0] : r[1];   // the other row of the pair
-    }
-    v = op(v, from_words(w));
-  }
-  {
-    uint32_t w[kWords];
-    as_words(v, w);
-#pragma unroll
-    for (int q = 0; q < kWords; ++q) {
-      const auto r = __builtin_amdgcn_permlane32_swap(w[q], w[q], false, false);
-      w[q] = (lane & 32) ? r[0] : r[1];   // the other half
-    }
-    v = op(v, from_words(w));
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
+// The cut of row r from its float64 logits zr[0 .. S) (global memory or LDS),
+// by one wavefront; umass / ucount / bm: that wavefront's LDS scratch.
 template <int NS>
-__global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ z, Geom g, double thr, double lambda,
-                                                     int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
-                                                     int32_t* __restrict__ counts, int words) {
-  __shared__ uint64_t umass_all[4][256];
-  __shared__ uint32_t ucount_all[4][256];
-  __shared__ uint32_t bm_all[4][kMaxS / 32];
+__device__ __forceinline__ void select_row(const double* zr, int64_t r, const Geom& g, double thr, double lambda,
+                                           int win_t, int win_h, int win_w, uint64_t* umass, uint32_t* ucount,
+                                           uint32_t* bm, uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts,
+                                           int words) {
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
-  if (r >= g.rows) return;                     // whole wavefront; nothing below waits on other waves
-  uint64_t* umass = umass_all[wv];
-  uint32_t* ucount = ucount_all[wv];
-  uint32_t* bm = bm_all[wv];
   const int S = g.S;
   const int i = (int)(r % S);
-  const double* zr = z + r * S;
   auto u64max = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
   auto u64min = [](uint64_t a, uint64_t b) { return a < b ? a : b; };
   auto u64add = [](uint64_t a, uint64_t b) { return a + b; };
@@ -549,9 +485,7 @@ __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ 
       }
     }
   }
-  if (win_t >= 0)
-    for (int j = lane; j < S; j += 64)
-      if (in_window(g, i, j, win_t, win_h, win_w)) set_bit(j);
+  if (win_t >= 0) for_each_window_block(g, i, win_t, win_h, win_w, lane, 64, set_bit);
   __builtin_amdgcn_wave_barrier();
   uint32_t pc = 0;
   for (int x = lane; x < words; x += 64) {
@@ -561,6 +495,70 @@ __global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ 
   }
   pc = wave_reduce(pc, lane, [](uint32_t a, uint32_t b) { return a + b; });
   if (lane == 0) counts[r] = (int32_t)pc;
+}
+
+template <int NS>
+__global__ void __launch_bounds__(256) select_kernel(const double* __restrict__ z, Geom g, double thr, double lambda,
+                                                     int win_t, int win_h, int win_w, uint32_t* __restrict__ bitmap,
+                                                     int32_t* __restrict__ counts, int words) {
+  __shared__ uint64_t umass_all[4][256];
+  __shared__ uint32_t ucount_all[4][256];
+  __shared__ uint32_t bm_all[4][kMaxS / 32];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= g.rows) return;                     // whole wavefront; nothing below waits on other waves
+  select_row<NS>(z + r * g.S, r, g, thr, lambda, win_t, win_h, win_w, umass_all[wv], ucount_all[wv], bm_all[wv],
+                 bitmap, counts, words);
+}
+
+// Rows the screened cut left undecided (see mask_screen.hip): their float64 logits
+// are computed into LDS and cut by select_row.  A persistent grid walks the list
+// the screened cut filled (its length is read on the device).
+template <int NS>
+__global__ void __launch_bounds__(256) fallback_select_kernel(const double* __restrict__ qp,
+                                                              const double* __restrict__ kp, Geom g, double thr,
+                                                              double lambda, int win_t, int win_h, int win_w,
+                                                              uint32_t* __restrict__ bitmap,
+                                                              int32_t* __restrict__ counts, int words,
+                                                              const int32_t* __restrict__ flag_list,
+                                                              const int32_t* __restrict__ nflag, double inv_sqrt_d) {
+  __shared__ double zrow[kMaxS];
+  __shared__ uint64_t umass[256];
+  __shared__ uint32_t ucount[256];
+  __shared__ uint32_t bm[kMaxS / 32];
+  const int n = *nflag;
+  for (int x = blockIdx.x; x < n; x += gridDim.x) {
+    const int64_t r = flag_list[x];
+    const int64_t bh = r / g.S;
+    const double* qrow = qp + (size_t)r * g.D;
+    __syncthreads();                     // the previous row's cut has finished with zrow
+    for (int j = threadIdx.x; j < g.S; j += 256) {
+      const double* krow = kp + (size_t)(bh * g.S + j) * g.D;
+      double z = 0.0;
+      for (int d = 0; d < g.D; ++d) z = fma(qrow[d], krow[d], z);
+      zrow[j] = z * inv_sqrt_d;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64)
+      select_row<NS>(zrow, r, g, thr, lambda, win_t, win_h, win_w, umass, ucount, bm, bitmap, counts, words);
+  }
+}
+
+hipError_t launch_fallback_select(const Geom& g, const double* qp, const double* kp, double thr, double lambda,
+                                  int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts, int words,
+                                  const int32_t* flag_list, const int32_t* nflag, hipStream_t s) {
+  const double inv = 1.0 / sqrt((double)g.D);
+  const unsigned grid = 512;
+#define BSA_FALLBACK(NS_)                                                                                      \
+  fallback_select_kernel<NS_><<<grid, 256, 0, s>>>(qp, kp, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, \
+                                                   words, flag_list, nflag, inv)
+  if (g.S <= 128) BSA_FALLBACK(2);
+  else if (g.S <= 512) BSA_FALLBACK(8);
+  else if (g.S <= 1024) BSA_FALLBACK(16);
+  else if (g.S <= 2048) BSA_FALLBACK(32);
+  else BSA_FALLBACK(64);
+#undef BSA_FALLBACK
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Geom& g, const double* z, double thr, double lambda, int win_t, int win_h, int win_w,
@@ -726,9 +724,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
       }
     }
   }
-  if (win_t >= 0)
-    for (int j = lane; j < S; j += 64)
-      if (in_window(g, i, j, win_t, win_h, win_w)) set_bit(j);
+  if (win_t >= 0) for_each_window_block(g, i, win_t, win_h, win_w, lane, 64, set_bit);
   __builtin_amdgcn_wave_barrier();
   uint32_t pc = 0;
   for (int x = lane; x < words; x += 64) {

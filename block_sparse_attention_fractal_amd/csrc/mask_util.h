@@ -14,6 +14,63 @@ __device__ __forceinline__ uint64_t order_key(double z) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
+// Wavefront-wide reduction with DPP moves inside each row of 16 lanes and lane
+// swaps across rows and halves; every lane ends with the result.
+__device__ __forceinline__ uint32_t dpp_step(uint32_t v, int step) {
+  switch (step) {
+    case 0: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);   // lanes ^ 1
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);   // lanes ^ 2
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+    default: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false); // row mirror
+  }
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, int lane, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  constexpr int kWords = sizeof(T) / 4;
+  auto as_words = [](T x, uint32_t* w) { __builtin_memcpy(w, &x, sizeof(T)); };
+  auto from_words = [](const uint32_t* w) {
+    T x;
+    __builtin_memcpy(&x, w, sizeof(T));
+    return x;
+  };
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) w[q] = dpp_step(w[q], st);
+    v = op(v, from_words(w));
+  }
+  {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const auto r = __builtin_amdgcn_permlane16_swap(w[q], w[q], false, false);
+      w[q] = (lane & 16) ? r[0] : r[1];   // the other row of the pair
+    }
+    v = op(v, from_words(w));
+  }
+  {
+    uint32_t w[kWords];
+    as_words(v, w);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const auto r = __builtin_amdgcn_permlane32_swap(w[q], w[q], false, false);
+      w[q] = (lane & 32) ? r[0] : r[1];   // the other half
+    }
+    v = op(v, from_words(w));
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Sliding-tile window (NABLA page, Metodologia item 3): block ids are tiles
 // (t, y, x) of Hp x Wp patches per frame; ids i and j are within the window when
 // every coordinate differs by at most the given extent.
@@ -22,6 +79,26 @@ __device__ __forceinline__ bool in_window(const Geom& g, int i, int j, int win_t
   const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
   const int tj = j / HW, yj = (j / g.Wp) % g.Hp, xj = j % g.Wp;
   return abs(ti - tj) <= win_t && abs(yi - yj) <= win_h && abs(xi - xj) <= win_w;
+}
+
+// Calls f(j) for every block j in the (clipped) window of block i, the threads of
+// a group splitting the work: thread `first` of `stride` takes entries first,
+// first + stride, ...  Enumerates the box of at most (2w_t+1)(2w_h+1)(2w_w+1)
+// tiles directly, so the cost does not grow with the number of blocks per row.
+template <typename F>
+__device__ __forceinline__ void for_each_window_block(const Geom& g, int i, int win_t, int win_h, int win_w, int first,
+                                                      int stride, F f) {
+  const int HW = g.Hp * g.Wp, T = g.S / HW;
+  const int ti = i / HW, yi = (i / g.Wp) % g.Hp, xi = i % g.Wp;
+  const int wt = min(win_t, T), wh = min(win_h, g.Hp), ww = min(win_w, g.Wp);   // no overflow below
+  const int t0 = max(ti - wt, 0), t1 = min(ti + wt, T - 1);
+  const int y0 = max(yi - wh, 0), y1 = min(yi + wh, g.Hp - 1);
+  const int x0 = max(xi - ww, 0), x1 = min(xi + ww, g.Wp - 1);
+  const int nx = x1 - x0 + 1, nyx = (y1 - y0 + 1) * nx, n = (t1 - t0 + 1) * nyx;
+  for (int e = first; e < n; e += stride) {
+    const int dt = e / nyx, rem = e - dt * nyx, dy = rem / nx, dx = rem - dy * nx;
+    f(((t0 + dt) * g.Hp + y0 + dy) * g.Wp + x0 + dx);
+  }
 }
 
 }  // namespace bsa

@@ -67,7 +67,7 @@ hipError_t launch_permute_table(const Geom& g, const int32_t* table, const void*
   return hipGetLastError();
 }
 
-// Vt[bh][j][d][p] = V[bh][token(j, key(p))][d] with D = 128, 64 keys per block.
+// Vt[bh][j][d][p] = V[bh][token(j, key(p))][d] with D = 128 or 64, 64 keys per block.
 // Inside every group of 16 keys, stored position p holds key perm(p) with
 // perm = 0,1,2,3, 8,9,10,11, 4,5,6,7, 12,13,14,15: the key order in which the
 // softmax probabilities come out of the 32x32 MFMA accumulator, so the PV
@@ -78,27 +78,28 @@ __device__ __forceinline__ int vt_key_of_pos(int p) {
   return (p & ~15) | q;
 }
 
+template <int D>
 __global__ void __launch_bounds__(256) prep_vt_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, Geom g) {
-  constexpr int D = 128;
-  __shared__ uint16_t tile[64][D + 8];  // +8 halves: rows 272 B apart, spreads banks on the column reads
+  constexpr int CH = D / 8;             // 16-byte chunks per token row
+  __shared__ uint16_t tile[64][D + 8];  // +8 halves: rows 2D + 16 bytes apart, spreads banks on the column reads
   const int64_t blk = blockIdx.x;       // bh*S + j
   const int64_t bh = blk / g.S;
   const int32_t j = (int32_t)(blk - bh * g.S);
   const uint16_t* vb = v + (size_t)bh * g.L * D;
   const int tid = threadIdx.x;
-  // 64 rows x 16 chunks of 16 B; 256 threads -> 4 chunks each
+  // 64 rows x CH chunks of 16 B; 256 threads -> D / 32 chunks each
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < D / 32; ++it) {
     const int c = tid + it * 256;
-    const int row = c >> 4, part = c & 15;
+    const int row = c / CH, part = c % CH;
     const uint4 val = *(const uint4*)(vb + (size_t)block_token_row(g, j, row) * D + part * 8);
     *(uint4*)(&tile[row][part * 8]) = val;
   }
   __syncthreads();
-  // output: 128 d-rows x 64 keys = 128 rows x 8 chunks of 8 halves
+  // output: D d-rows x 64 keys = D rows x 8 chunks of 8 halves
   uint16_t* ob = vt + (size_t)blk * D * 64;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < D / 32; ++it) {
     const int c = tid + it * 256;
     const int d = c >> 3, part = c & 7;
     uint16_t h[8];
@@ -115,7 +116,10 @@ __global__ void __launch_bounds__(256) prep_vt_kernel(const uint16_t* __restrict
 
 hipError_t launch_prep_vt(const Geom& g, const void* v, void* vt, hipStream_t s) {
   const int64_t blocks = (int64_t)g.B * g.nh * g.S;
-  prep_vt_kernel<<<(unsigned)blocks, 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vt, g);
+  if (g.D == 64)
+    prep_vt_kernel<64><<<(unsigned)blocks, 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vt, g);
+  else
+    prep_vt_kernel<128><<<(unsigned)blocks, 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vt, g);
   return hipGetLastError();
 }
 

@@ -78,7 +78,9 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
 
 hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, double* kp, hipStream_t s) {
   dim3 grid((unsigned)g.rows);
-  if (g.dtype == 1)
+  if (g.dtype == 1 && g.D == 64)
+    pool_kernel<uint16_t, 64><<<grid, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, qp, kp, g);
+  else if (g.dtype == 1)
     pool_kernel<uint16_t, 128><<<grid, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, qp, kp, g);
   else if (g.D == 64)
     pool_kernel<float, 64><<<grid, 256, 0, s>>>((const float*)q, (const float*)k, qp, kp, g);

@@ -28,17 +28,19 @@ int make_geom(const bsa_problem* p, Geom* g, std::string* msg) {
     return fail(msg, BSA_ERR_SHAPE, "all sizes must be positive");
   if (p->H % p->patch || p->W % p->patch)
     return fail(msg, BSA_ERR_SHAPE, "H=%lld and W=%lld must be multiples of the patch size", p->H, p->W);
-  const long long L = (long long)p->T * p->H * p->W;
+  // T*H*W in two steps so that no product can overflow (each factor < 2^31)
+  const long long TH = (long long)p->T * p->H;
+  if (TH > (1LL << 30) || TH * p->W > (1LL << 30))
+    return fail(msg, BSA_ERR_UNSUPPORTED, "T*H*W exceeds 2^30 tokens per head");
+  const long long L = TH * p->W;
   if (L % p->block)
     return fail(msg, BSA_ERR_SHAPE, "L=%lld is not a multiple of the block size %lld", L, p->block);
   if (p->block != 64)
     return fail(msg, BSA_ERR_UNSUPPORTED, "block size %lld: only N = 64 is implemented", p->block);
   if (p->layout == BSA_LAYOUT_ORIGINAL && (long long)p->patch * p->patch != p->block)
     return fail(msg, BSA_ERR_UNSUPPORTED, "original layout needs P*P == N (P=%lld, N=%lld)", p->patch, p->block);
-  if (p->dtype == BSA_BF16 && p->head_dim != 128)
-    return fail(msg, BSA_ERR_UNSUPPORTED, "bf16 head_dim %lld: only 128 is implemented", p->head_dim);
-  if (p->dtype == BSA_F32 && p->head_dim != 64 && p->head_dim != 128)
-    return fail(msg, BSA_ERR_UNSUPPORTED, "f32 head_dim %lld: only 64 and 128 are implemented", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "head_dim %lld: only 64 and 128 are implemented", p->head_dim);
   const long long S = L / p->block;
   if (S > 4096)
     return fail(msg, BSA_ERR_UNSUPPORTED, "S=%lld blocks per head exceeds 4096", S);
@@ -79,6 +81,16 @@ MaskWs mask_ws_layout(const Geom& g) {
   w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
   w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
   w.rowstat = off; off = align256(off + g.rows * 4 * 8);
+  w.qs = off; off = align256(off + g.rows * 2 * g.D * 2);
+  w.ks = off; off = align256(off + g.rows * 2 * g.D * 2);
+  w.qmu = off; off = align256(off + g.rows * 8);
+  w.kmu = off; off = align256(off + g.rows * 8);
+  w.qn = off; off = align256(off + g.rows * 8);
+  w.qe = off; off = align256(off + g.rows * 4);
+  w.ke = off; off = align256(off + g.rows * 4);
+  w.hstat = off; off = align256(off + (int64_t)g.B * g.nh * 3 * 8);
+  w.flags = off; off = align256(off + g.rows * 4);
+  w.nflag = off; off = align256(off + 4);
   w.total = off;
   return w;
 }
@@ -104,7 +116,7 @@ BwdWs bwd_ws_layout(const Geom& g) {
   const int64_t tok = (int64_t)g.B * g.nh * g.L;
   int64_t off = 0;
   w.delta = off; off = align256(off + tok * 8);     // float2 per token
-  w.counter = off; off = align256(off + 64);
+  w.counter = off; off = align256(off + 24 * 4);   // per-XCD item counters of the three passes
   w.bounds = off; off = align256(off + 32 * 4);   // two sets of 9 XCD bounds (at 0 and 16)
   const int64_t items = g.dtype == BSA_BF16 ? (int64_t)g.B * g.nh * ((g.S + 1) / 2) : 0;
   w.cost = off; off = align256(off + items * 4);
@@ -127,6 +139,8 @@ BwdWs bwd_ws_layout(const Geom& g) {
 int check_group(const Geom& g, int group, std::string* msg) {
   if (group != BSA_KEY_GROUP)
     return fail(msg, BSA_ERR_UNSUPPORTED, "key group size %lld: only %lld is implemented", group, BSA_KEY_GROUP);
+  if (g.dtype == BSA_BF16 && g.D != 128)
+    return fail(msg, BSA_ERR_UNSUPPORTED, "bf16 key-group attention: head_dim %lld (only 128 is implemented)", g.D);
   const long long SG = g.L / BSA_KEY_GROUP;
   if (g.rows * SG >= (1LL << 31))
     return fail(msg, BSA_ERR_UNSUPPORTED,

@@ -14,12 +14,15 @@ int check_mask_params(const Geom& g, const bsa_mask_params* mp, std::string* msg
 
 struct MaskWs {       // byte offsets into the mask workspace
   int64_t qp, kp, z, counts, bitmap, chunk_sums, rowstat, total;   // rowstat: SIP (max, sum, c, top) per row
+  // screened cut: fp16 operands, means, norms, exponents, per-head stats, the list of
+  // rows left to the float64 path and its length
+  int64_t qs, ks, qmu, kmu, qn, qe, ke, hstat, flags, nflag;
   int32_t words;      // 32-bit words per bitmap row
 };
 struct FwdWs {         // work counters and XCD bounds, per-item costs and order (bf16), prepared V (bf16)
   int64_t counter, bounds, cost, order, vt, total;
 };
-struct BwdWs {        // transposed mask, per-token dO.o, work counters and orders, prepared transposes (bf16)
+struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work counters and orders, prepared transposes (bf16)
   int64_t delta, counter, bounds, cost, order_q, order_k, tcounts, tchunks, tbitmap, tcolptr, trowidx, qt, dot, total;
   int32_t words;
 };

@@ -41,7 +41,7 @@
  *
  * Supported shapes (else BSA_ERR_SHAPE / BSA_ERR_UNSUPPORTED):
  *   N == 64; H % P == 0, W % P == 0, L % N == 0; layout ORIGINAL needs P*P == N;
- *   head_dim in {64, 128} for f32, == 128 for bf16; S <= 4096;
+ *   head_dim in {64, 128} (bf16 backward and bf16 key-group attention: 128 only); S <= 4096;
  *   batch*heads*S*S < 2^31 (int32 CSR offsets).
  */
 #ifndef BSA_H
@@ -230,21 +230,25 @@ int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v
  * item 2 "Expansion"): with P = softmax over each query's kept keys of
  * q.k / sqrt(D),
  *   dV_k = sum_n P[n,k] dO_n,   dP[n,k] = dO_n . v_k,
- *   dZ[n,k] = P[n,k] (dP[n,k] - dO_n . o_n),
+ *   dZ[n,k] = P[n,k] (dP[n,k] - Delta_n),   Delta_n = sum_k P[n,k] dP[n,k],
  *   dQ_n = sum_k dZ[n,k] k_k / sqrt(D),   dK_k = sum_n dZ[n,k] q_n / sqrt(D).
- * q, k, v, o, dout, dq, dk, dv: [batch, heads, L, head_dim] in p->layout order
- * (o and lse as returned by bsa_forward for the same mask; lse float32
- * [batch, heads, L], required).  mask: the forward's CSR; per-entry shifts are
- * not supported here (BSA_ERR_UNSUPPORTED when mask->shift is not NULL).  Every
- * output element is written (key blocks no query keeps get zero dK, dV); the
- * result is deterministic (no atomics on the gradients: dQ is summed per query
- * block, dK and dV per key block over the transposed mask, which the call
- * builds in its workspace).  ws: at least bwd_ws bytes (bsa_query_backward_ws),
- * 256-byte aligned. */
+ * The row term Delta_n is computed by the call from P and dP themselves (a
+ * first walk over the kept tiles), not from a stored output, so that the dZ of
+ * one query sum to zero in the arithmetic the kernels use; the forward's output
+ * is therefore not an argument.
+ * q, k, v, dout, dq, dk, dv: [batch, heads, L, head_dim] in p->layout order;
+ * lse: float32 [batch, heads, L] as returned by bsa_forward for the same mask
+ * (required).  mask: the forward's CSR; per-entry shifts are not supported here
+ * (BSA_ERR_UNSUPPORTED when mask->shift is not NULL).  Every output element is
+ * written (key blocks no query keeps get zero dK, dV); the result is
+ * deterministic (no atomics on the gradients: dQ is summed per query block, dK
+ * and dV per key block over the transposed mask, which the call builds in its
+ * workspace).  ws: at least bwd_ws bytes (bsa_query_backward_ws), 256-byte
+ * aligned, contents on entry irrelevant. */
 int bsa_query_backward_ws(const bsa_problem* p, int64_t* bwd_ws);
 int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
-                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
-                 int64_t ws_bytes, hipStream_t stream);
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, int64_t ws_bytes,
+                 hipStream_t stream);
 
 /* ---- 4-token key groups ---------------------------------------------
  * Fine-grained key selection gathered into full tiles (AB-Attention page,
@@ -306,7 +310,7 @@ const char* bsa_last_error(void);
 /* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
  * token-order tables and the backward pass; 300 adds the 4-token key-group path; 400 adds
  * bsa_query_attend_ws and bsa_query_attend_groups_ws (the attention workspaces hold the work
- * order). */
+ * order); 500 drops the forward output from bsa_backward (the row term is recomputed). */
 int bsa_version(void);
 
 #ifdef __cplusplus

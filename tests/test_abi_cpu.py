@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 400
+    assert lib.bsa_version() == 500
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -60,11 +60,15 @@ def test_query_sizes(lib, B, nh, T, H, W):
     assert st == 0
     S = T * H * W // 64
     assert rows == B * nh * S and max_nnz == rows * S
-    # mask workspace: qp, kp (float64), logits (float64), counts, bitmap, scan chunk sums,
-    # SIP row statistics (4 float64 per row), each 256-aligned
+    # mask workspace: qp, kp (float64), logits (float64, SIP mode), counts, bitmap, scan chunk
+    # sums, SIP row statistics (4 float64 per row); the screened cut's fp16 hi/lo operands of
+    # queries and keys, their means, query norms, scale exponents, per-head statistics
+    # (3 x 8 bytes), the list of rows for the float64 path and its length; each 256-aligned
     a = lambda x: (x + 255) // 256 * 256
     assert mws == (a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
-                   + a((rows + 1023) // 1024 * 4) + a(rows * 32))
+                   + a((rows + 1023) // 1024 * 4) + a(rows * 32)
+                   + 2 * a(rows * 2 * D * 2) + 3 * a(rows * 8) + 2 * a(rows * 4) + a(B * nh * 24)
+                   + a(rows * 4) + a(4))
     # forward workspace: work counters and XCD bounds, per-item cost and order (one int32 each
     # per query-block pair), prepared V
     items = B * nh * ((S + 1) // 2)
@@ -91,7 +95,7 @@ def test_query_attend_ws(lib):
     (dict(T=0), 2),                             # non-positive
     (dict(N=32), 4),                            # only N = 64
     (dict(Pp=4, N=64), 4),                      # original layout needs P*P == N
-    (dict(D=64), 4),                            # bf16 needs D = 128
+    (dict(D=96), 4),                            # bf16 D in {64, 128}
     (dict(dtype=0, D=96), 4),                   # f32 D in {64, 128}
     (dict(T=65, H=64, W=64), 4),                # S > 4096
     (dict(T=1, H=8, W=12, Pp=4, N=64, layout=1), 2),   # L % N
@@ -100,6 +104,22 @@ def test_query_sizes_rejects(lib, kw, code):
     st, _ = sizes(lib, P(**kw))
     assert st == code, lib.bsa_last_error().decode()
     assert lib.bsa_last_error().decode() != ""
+
+
+def test_bf16_head_dim_64_limits(lib):
+    """bf16 head_dim 64 is a valid problem (mask, permute, forward); the bf16 backward
+    and the bf16 key-group path implement head_dim 128 only and say so on the host."""
+    p = P(D=64)
+    st, (rows, max_nnz, mws, fws) = sizes(lib, p)
+    assert st == 0
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
+    bws = ctypes.c_int64()
+    assert lib.bsa_query_backward_ws(ctypes.byref(p), ctypes.byref(bws)) == 0
+    assert lib.bsa_backward(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, bws.value, None) == 4
+    assert "head_dim" in lib.bsa_last_error().decode()
+    vals = [ctypes.c_int64() for _ in range(3)]
+    assert lib.bsa_query_group_sizes(ctypes.byref(p), 4, *[ctypes.byref(v) for v in vals]) == 4
 
 
 def test_fractal_layout_allows_other_patch_sizes(lib):

@@ -1,17 +1,17 @@
-"""GPU parity of the backward pass (dQ, dK, dV) against the float64 oracle
-(oracle.block_sparse_attention_backward) on the GPU's own mask.
+"""GPU parity of the backward pass (dQ, dK, dV) against the exact float64
+gradient of the oracle (oracle.block_sparse_attention_backward with no stored
+output: the row term is sum_k P dP from the exact P), on the GPU's own mask.
 
-Like any kernel that stores O rather than P, the backward forms the row term
-Delta_n = dO_n . o_n from the forward's output, so the oracle is given the same
-(rounded) O; with the exact O the two forms agree (pinned on the CPU).
-Tolerances, derived from the arithmetic: float32 tensors go through float64
-kernels, so the error is the float32 rounding of the lse the kernels read back
-(P's relative error is 2^-24 |lse|): max-abs (1e-5 + 2^-23 max|lse|) of the
-gradient's scale.  bf16 tensors take the forward's bar (mean-relative 5e-3,
-max-abs 2e-2) relative to the gradient's scale (max |reference|): dV and dK
-round P and dZ to bf16 once (2^-9 per term, no cancellation, ~2e-3 measured on
-the CPU by rounding the oracle's own P and dZ), and dQ, whose dZ terms of one
-query sum to zero, carries dZ as a hi + lo pair of bf16 values."""
+The kernels recompute the row term from their own P and dP as well, so nothing
+of the forward's rounded output enters the gradient.  Tolerances, derived from
+the arithmetic: float32 tensors go through float64 kernels, so the error is the
+float32 rounding of the lse the kernels read back (P's relative error is
+2^-24 |lse|): max-abs (1e-5 + 2^-23 max|lse|) of the gradient's scale.  bf16
+tensors take the forward's bar (mean-relative 5e-3, max-abs 2e-2) relative to
+the gradient's scale (max |reference|): dV and dK round P and dZ to bf16 once
+(2^-9 per term, no cancellation, ~2e-3 measured on the CPU by rounding the
+oracle's own P and dZ), and dQ, whose dZ terms of one query sum to zero,
+carries dZ as a hi + lo pair of bf16 values."""
 import numpy as np
 import pytest
 import torch
@@ -41,9 +41,9 @@ def small_cfg(dtype="bf16", B=1, nh=2, T=3, H=24, W=40, D=128, thr=0.1, amp=3.0,
     return Config(99, "edge", dtype, B, nh, T, H, W, D, 8, 64, thr, None, amp, seed=seed)
 
 
-def dout_for(cfg, seed=123):
+def dout_for(cfg, seed=123, batch=None):
     rng = np.random.default_rng(seed)
-    d = rng.standard_normal((cfg.batch, cfg.heads, cfg.L, cfg.head_dim)).astype(np.float32)
+    d = rng.standard_normal((cfg.batch if batch is None else batch, cfg.heads, cfg.L, cfg.head_dim)).astype(np.float32)
     return bf16_bits_to_f32(bf16_round(d)) if cfg.dtype == "bf16" else d
 
 
@@ -74,16 +74,15 @@ def run_case(cfg, inputs, row_ptr=None, col_idx=None, thr=None):
     else:
         mask = bsa.mask_from_csr(torch.from_numpy(row_ptr.astype(np.int32)).cuda(),
                                  torch.from_numpy(col_idx.astype(np.int32)).cuda(), cfg.S)
-    o, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+    _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
     do_np = dout_for(cfg)
-    dq, dk, dv = bsa.backward(q, k, v, mask, g, o, lse, to_dev(do_np, cfg.dtype))
+    dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
     torch.cuda.synchronize()
     rp = mask.row_ptr.cpu().numpy().astype(np.int64)
     ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
     src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
     qf, kf, vf, dof = (x[:, :, src] for x in (inputs["q"], inputs["k"], inputs["v"], do_np))
-    of = to_host_f64(o)[:, :, src]
-    rdq, rdk, rdv = oracle.block_sparse_attention_backward(qf, kf, vf, rp, ci, dof, cfg.block, O=of)
+    rdq, rdk, rdv = oracle.block_sparse_attention_backward(qf, kf, vf, rp, ci, dof, cfg.block)
     lse_max = float(lse.abs().max())
     res = []
     for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
@@ -122,54 +121,70 @@ def test_backward_dense_mask_bf16():
     run_case(cfg, make_inputs(cfg), thr=0.0)
 
 
-def test_backward_fullsize_sampled():
-    """The Wan2.1-scale workload (40 heads, 21 x 32 x 48 tokens) at full size, as the
-    benchmark's backward leg runs it: dQ on sampled query blocks (the oracle needs
-    only that row's keys) and dK, dV on sampled key blocks (the oracle sums exactly
-    the rows whose CSR keeps the block), on three heads."""
-    cfg = get_config(2)
-    inputs = make_inputs(cfg)
+def test_backward_strong_common_key_component():
+    """Local heads with the HunyuanVideo-scale positional amplitude (4): every key
+    carries a large common component, the case in which a row term that does not
+    match the kernel's own P would leak into dQ."""
+    cfg = Config(98, "edge", "bf16", 1, 2, 4, 48, 80, 128, 8, 64, 0.05, None, 4.0, seed=17)
+    run_case(cfg, make_inputs(cfg))
+
+
+@pytest.mark.parametrize("ci,dq_heads,dkv_heads", [(2, (0, 17, 39), (0, 17, 39)), (4, (0, 20), (0, 16))])
+def test_backward_fullsize_sampled(ci, dq_heads, dkv_heads):
+    """Full-size workloads as the benchmark's backward leg runs them: the Wan2.1-scale
+    one (40 heads, 21 x 32 x 48 tokens) and one batch item of the HunyuanVideo-scale
+    hybrid one (24 heads, 33 x 48 x 80 tokens, sliding-tile window; local heads 0-16,
+    diffuse 17-23).  dQ on sampled query blocks (the oracle needs only that row's
+    keys) and dK, dV on sampled key blocks (the oracle sums exactly the rows whose
+    CSR keeps the block), against the exact gradient.  dQ covers a local and a
+    diffuse head; dK, dV cover local heads only at the HunyuanVideo scale, where a
+    diffuse head's key block is kept by ~1800 rows of ~1900 blocks each (minutes of
+    oracle time per block)."""
+    cfg = get_config(ci)
+    inputs = make_inputs(cfg, batch=1)
     g = grid_of(cfg)
     q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
     for n in ("q_bits", "k_bits", "v_bits"):
         inputs.pop(n)
     mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window)
-    o, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
-    do_np = dout_for(cfg)
-    dq, dk, dv = bsa.backward(q, k, v, mask, g, o, lse, to_dev(do_np, cfg.dtype))
+    _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+    do_np = dout_for(cfg, batch=1)
+    dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
     torch.cuda.synchronize()
+    del q, k, v, lse
     S = cfg.S
     rp = mask.row_ptr.cpu().numpy().astype(np.int64)
     src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
-    o_h = to_host_f64(o)
-    grads = [to_host_f64(x) for x in (dq, dk, dv)]
     rng = np.random.default_rng(8)
     got = {"dq": [], "dk": [], "dv": []}
     ref = {"dq": [], "dk": [], "dv": []}
-    for h in (0, 17, 39):
+    for h in sorted(set(dq_heads) | set(dkv_heads)):
         r0 = h * S
         lo, hi = int(rp[r0]), int(rp[r0 + S])
-        ci = mask.col_idx[lo:hi].cpu().numpy()
+        ci_ = mask.col_idx[lo:hi].cpu().numpy()
         prp = rp[r0:r0 + S + 1] - lo
         qf, kf, vf, dof = (x[0:1, h:h + 1][:, :, src] for x in (inputs["q"], inputs["k"], inputs["v"], do_np))
-        of = o_h[0:1, h:h + 1][:, :, src]
-        qrows = sorted(rng.choice(S, 8, replace=False).tolist())
-        rdq, _, _ = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci, dof, 64, rows=qrows, O=of)
-        for i in qrows:
-            tok = src[i * 64:(i + 1) * 64]
-            got["dq"].append(grads[0][0, h, tok])
-            ref["dq"].append(rdq[0, 0, i * 64:(i + 1) * 64])
-        rows_of = np.repeat(np.arange(S), np.diff(prp))
-        for j in rng.choice(S, 4, replace=False):
-            krows = sorted(set(rows_of[ci == j].tolist()))
-            if not krows:
-                continue
-            _, rdk, rdv = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci, dof, 64, rows=krows, O=of)
-            tok = src[j * 64:(j + 1) * 64]
-            got["dk"].append(grads[1][0, h, tok])
-            ref["dk"].append(rdk[0, 0, j * 64:(j + 1) * 64])
-            got["dv"].append(grads[2][0, h, tok])
-            ref["dv"].append(rdv[0, 0, j * 64:(j + 1) * 64])
+        gh = [to_host_f64(x[0, h]) for x in (dq, dk, dv)]
+        if h in dq_heads:
+            qrows = sorted(rng.choice(S, 8 if ci == 2 else 4, replace=False).tolist())
+            rdq, _, _ = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci_, dof, 64, rows=qrows)
+            for i in qrows:
+                tok = src[i * 64:(i + 1) * 64]
+                got["dq"].append(gh[0][tok])
+                ref["dq"].append(rdq[0, 0, i * 64:(i + 1) * 64])
+        if h in dkv_heads:
+            rows_of = np.repeat(np.arange(S), np.diff(prp))
+            for j in rng.choice(S, 4, replace=False):
+                krows = sorted(set(rows_of[ci_ == j].tolist()))
+                if not krows:
+                    continue
+                _, rdk, rdv = oracle.block_sparse_attention_backward(qf, kf, vf, prp, ci_, dof, 64, rows=krows)
+                tok = src[j * 64:(j + 1) * 64]
+                got["dk"].append(gh[1][tok])
+                ref["dk"].append(rdk[0, 0, j * 64:(j + 1) * 64])
+                got["dv"].append(gh[2][tok])
+                ref["dv"].append(rdv[0, 0, j * 64:(j + 1) * 64])
+        print(f"head {h} compared", flush=True)
     res = [grad_errors(np.stack(got[n]), np.stack(ref[n]), cfg.dtype, n) for n in ("dq", "dk", "dv")]
     msg = "; ".join(m for _, m in res)
     print(msg)

@@ -57,6 +57,8 @@ CASES = {
     "bf16-local": small(),
     "bf16-window-odd": small(T=3, H=24, W=40, thr=0.1, window=(1, 1, 1), seed=12),
     "bf16-diffuse": small(amp=0.0, thr=0.05, seed=13),
+    "bf16-one-patch-column": small(T=3, H=16, W=8, thr=0.1, seed=15),
+    "bf16-one-patch-row": small(T=2, H=8, W=24, thr=0.1, seed=16),
     "f32-cfg0": get_config(0),
     "f32-window": small(dtype="f32", D=64, T=2, H=16, W=24, thr=0.3, window=(0, 1, 1), amp=1.0, seed=14),
 }

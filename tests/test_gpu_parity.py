@@ -181,9 +181,12 @@ def test_forward_on_oracle_mask(ci):
     compare_outputs(to_host_f64(o), O, cfg.dtype)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_thr_zero_is_dense_attention(dtype):
-    cfg = small_cfg(dtype=dtype, nh=2, T=2, H=16, W=24, D=128 if dtype == "bf16" else 64, thr=0.0)
+DTYPE_DIMS = [("f32", 64), ("bf16", 128), ("bf16", 64)]
+
+
+@pytest.mark.parametrize("dtype,D", DTYPE_DIMS)
+def test_thr_zero_is_dense_attention(dtype, D):
+    cfg = small_cfg(dtype=dtype, nh=2, T=2, H=16, W=24, D=D, thr=0.0)
     inputs = make_inputs(cfg)
     res = run_all(cfg, inputs, thr=0.0)
     assert res["row_ptr"][-1] == (len(res["row_ptr"]) - 1) * cfg.S
@@ -191,18 +194,18 @@ def test_thr_zero_is_dense_attention(dtype):
     compare_outputs(res["o"], O, dtype)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_single_block_sequence_is_dense(dtype):
-    cfg = small_cfg(dtype=dtype, nh=3, T=1, H=8, W=8, D=128 if dtype == "bf16" else 64, thr=0.5)
+@pytest.mark.parametrize("dtype,D", DTYPE_DIMS)
+def test_single_block_sequence_is_dense(dtype, D):
+    cfg = small_cfg(dtype=dtype, nh=3, T=1, H=8, W=8, D=D, thr=0.5)
     inputs = make_inputs(cfg)
     res = run_all(cfg, inputs)
     O, _ = oracle.dense_attention(inputs["q"], inputs["k"], inputs["v"])
     compare_outputs(res["o"], O, dtype)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_fractal_layout_matches_original(dtype):
-    cfg = small_cfg(dtype=dtype, nh=2, T=3, H=16, W=24, D=128 if dtype == "bf16" else 64, thr=0.2)
+@pytest.mark.parametrize("dtype,D", DTYPE_DIMS)
+def test_fractal_layout_matches_original(dtype, D):
+    cfg = small_cfg(dtype=dtype, nh=2, T=3, H=16, W=24, D=D, thr=0.2)
     inputs = make_inputs(cfg)
     a = run_all(cfg, inputs)
     b = run_all(cfg, inputs, layout="fractal")
@@ -290,3 +293,76 @@ def test_mask_partial_ties():
     rp = mask.row_ptr.cpu().numpy()
     ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
     compare_masks(rp, ci, oracle_mask(cfg, inputs), cfg.thr, cfg.S)
+
+
+@pytest.mark.parametrize("T,H,W", [(2, 16, 8), (3, 8, 24), (4, 8, 8)], ids=["one-patch-column", "one-patch-row",
+                                                                          "one-patch-frame"])
+def test_grids_with_one_patch_per_axis(T, H, W):
+    """Frames one patch wide or tall (Wp = 1 or Hp = 1) in the original layout: the
+    block-row arithmetic divides by a patch count of 1, which must stay exact."""
+    cfg = small_cfg(nh=2, T=T, H=H, W=W, thr=0.1, seed=41)
+    inputs = make_inputs(cfg)
+    res = run_all(cfg, inputs)
+    compare_masks(res["row_ptr"], res["col_idx"], oracle_mask(cfg, inputs), cfg.thr, cfg.S)
+    O, LSE = oracle_full_attention(cfg, inputs, res["row_ptr"], res["col_idx"])
+    compare_outputs(res["o"], O, "bf16")
+    assert np.abs(res["lse"] - LSE).max() < 2e-3
+
+
+def _scaled_inputs(cfg, q_scale_frames, scale):
+    """Inputs whose queries in the first q_scale_frames frames are multiplied by
+    `scale`: large channel-wise variation of those query blocks, which the screened
+    cut cannot resolve to the band, so their rows go through the float64 path."""
+    from workloads import bf16_bits_to_f32, bf16_round
+    inputs = make_inputs(cfg)
+    x = inputs["q"].copy()
+    x[:, :, : q_scale_frames * cfg.H * cfg.W] *= scale
+    bits = bf16_round(x)
+    inputs["q_bits"], inputs["q"] = bits, bf16_bits_to_f32(bits)
+    return inputs
+
+
+@pytest.mark.parametrize("frames", [4, 2], ids=["every-row-float64", "half-the-rows-float64"])
+def test_mask_rows_beyond_the_screen(frames):
+    """Rows whose screened logits cannot be trusted to the band are cut from float64
+    logits; the CSR must still match the oracle, alone and mixed with screened rows."""
+    cfg = small_cfg(nh=2, T=4, H=24, W=40, thr=0.1, window=(1, 1, 1), amp=0.0, local=0, seed=51)
+    inputs = _scaled_inputs(cfg, frames, 96.0)
+    g = grid_of(cfg)
+    q, k = to_device(inputs, "q", "bf16"), to_device(inputs, "k", "bf16")
+    mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window)
+    rp = mask.row_ptr.cpu().numpy()
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    n_mis, n_band = compare_masks(rp, ci, oracle_mask(cfg, inputs), cfg.thr, cfg.S)
+    print(f"frames scaled {frames}: nnz={rp[-1]} mismatches={n_mis} band={n_band}")
+
+
+BF16_D64 = {
+    "local": small_cfg(nh=4, T=8, H=32, W=32, D=64, thr=0.2, seed=71),
+    "hybrid": small_cfg(B=2, nh=3, T=5, H=24, W=40, D=64, thr=0.1, window=(1, 1, 1), amp=4.0, local=2, seed=72),
+    "diffuse": small_cfg(nh=2, T=6, H=32, W=32, D=64, thr=0.05, amp=0.0, local=0, seed=73),
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_D64))
+def test_bf16_head_dim_64_matches_oracle(name):
+    """bf16 with head_dim 64 (the second head size the boundary supports): the mask
+    against the oracle's, attention on the GPU mask and on the oracle's mask against
+    the float64 oracle, LSE included."""
+    cfg = BF16_D64[name]
+    inputs = make_inputs(cfg)
+    res = run_all(cfg, inputs)
+    ref = oracle_mask(cfg, inputs)
+    n_mis, n_band = compare_masks(res["row_ptr"], res["col_idx"], ref, cfg.thr, cfg.S)
+    O, LSE = oracle_full_attention(cfg, inputs, res["row_ptr"], res["col_idx"])
+    ma, mr = compare_outputs(res["o"], O, "bf16")
+    assert np.abs(res["lse"] - LSE).max() < 2e-3
+    g = grid_of(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    rp = torch.from_numpy(ref["row_ptr"].astype(np.int32)).cuda()
+    cidx = torch.from_numpy(ref["col_idx"].astype(np.int32)).cuda()
+    o2 = bsa.forward(q, k, v, bsa.mask_from_csr(rp, cidx, cfg.S), g)
+    O2, _ = oracle_full_attention(cfg, inputs, ref["row_ptr"], ref["col_idx"])
+    compare_outputs(to_host_f64(o2), O2, "bf16")
+    print(f"bf16 D=64 {name}: nnz={res['row_ptr'][-1]} mismatches={n_mis} band={n_band} max_abs={ma:.3e} "
+          f"mean_rel={mr:.3e}")
