@@ -278,6 +278,22 @@ def attend(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, 
     return (o, lse) if return_lse else o
 
 
+def attend_static(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+                  layout: str = "original", return_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """attend() through bsa_attend_static: no workspace argument (the library's static
+    scratch holds the work order), for callers that cannot allocate device memory."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    if vp.numel() != q.numel() or vp.dtype != q.dtype or not vp.is_contiguous():
+        raise ValueError("vp must be a contiguous tensor with q's dtype and size")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    csr = mask.as_struct()
+    check(lib().bsa_attend_static(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), vp.data_ptr(), ctypes.byref(csr),
+                                  o.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
 def attention(q, k, v, grid: VideoGrid, thr: float, window=None, layout: str = "original",
               return_lse: bool = False):
     """The whole hot path: mask from (q, k), then block-sparse attention."""

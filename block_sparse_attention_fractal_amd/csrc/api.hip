@@ -57,7 +57,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 500; }
+int bsa_version(void) { return 510; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -535,3 +535,55 @@ int bsa_forward_groups(const bsa_problem* p, int group, const void* q, const voi
 }
 
 }  // extern "C"
+
+// ---- attention with a static scratch buffer (no allocation) ---------------
+// The work counters, XCD bounds and work order that bsa_attend keeps in its
+// workspace argument live here in a file-scope device array instead.  In host
+// code `g_attend_scratch` only names the symbol; its device address (one per
+// GPU, each holding its own copy) comes from hipGetSymbolAddress on the first
+// call on that device and is the only form passed to kernels.
+namespace {
+
+constexpr int64_t kAttendScratchBytes = int64_t(4) << 20;
+__device__ __attribute__((aligned(256))) uint8_t g_attend_scratch[kAttendScratchBytes];
+
+int attend_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(BSA_ERR_HIP, "device id out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_attend_scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(attend scratch)");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" int bsa_attend_static(const bsa_problem* p, const void* q, const void* k, const void* vp,
+                                 const bsa_csr* mask, void* o, float* lse, hipStream_t stream) {
+  Geom g;
+  int st = geom_or_fail(p, &g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !vp || !o || !mask || !mask->row_ptr || !mask->col_idx)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_attend_static: null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vp, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(mask->shift, 4))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_attend_static: misaligned pointer");
+  const int64_t need = fwd_ws_layout(g).vt;
+  if (need > kAttendScratchBytes)
+    return fail(BSA_ERR_WORKSPACE, "bsa_attend_static: the problem needs " + std::to_string(need) +
+                                       " bytes of scratch; the static scratch holds " +
+                                       std::to_string(kAttendScratchBytes) + " (use bsa_attend with a workspace)");
+  void* ws = nullptr;
+  st = attend_scratch(&ws);
+  if (st != BSA_OK) return st;
+  return enqueue_attend(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream);
+}

@@ -225,6 +225,22 @@ int bsa_query_attend_ws(const bsa_problem* p, int64_t* attend_ws);
 int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
                void* o, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
 
+/* bsa_attend without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics and kernels as bsa_attend,
+ * except that the work counters and work order live in a static scratch array
+ * of the library, 4 MiB per GPU (held from the library's first use on a device
+ * until the process ends).  The call allocates nothing: problems whose order
+ * needs more (bsa_query_attend_ws > 4 MiB, i.e. more than about 524,000 bf16
+ * query-block pairs batch*heads*ceil(S/2)) are rejected with BSA_ERR_WORKSPACE
+ * before anything is enqueued.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (different streams, or
+ * threads) race and must be serialised by the caller; each call clears the
+ * counters it needs with a fill kernel on `stream`, and the scratch keeps the
+ * last call's contents afterwards. */
+int bsa_attend_static(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
+                      void* o, float* lse, hipStream_t stream);
+
 /* Backward of the block-sparse attention (the gradient of sum(O * dO) with
  * respect to Q, K and V, for training with the mask, NABLA page, Metodologia
  * item 2 "Expansion"): with P = softmax over each query's kept keys of
@@ -310,7 +326,8 @@ const char* bsa_last_error(void);
 /* ABI version (major*10000 + minor*100 + patch): 200 adds the SIP mask mode and CSR shifts,
  * token-order tables and the backward pass; 300 adds the 4-token key-group path; 400 adds
  * bsa_query_attend_ws and bsa_query_attend_groups_ws (the attention workspaces hold the work
- * order); 500 drops the forward output from bsa_backward (the row term is recomputed). */
+ * order); 500 drops the forward output from bsa_backward (the row term is recomputed); 510
+ * adds bsa_attend_static. */
 int bsa_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 500
+    assert lib.bsa_version() == 510
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -179,6 +179,23 @@ def test_attend_rejects_a_small_workspace(lib):
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value - 1, None) == 6
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE + 64, aws.value, None) == 6
     assert f(ctypes.byref(p), FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, FAKE, aws.value, None) == 1
+
+
+def test_attend_static_rejects_before_touching_the_gpu(lib):
+    """bsa_attend_static: null and misaligned pointers, and problems whose work order
+    does not fit its 4 MiB static scratch, are rejected on the host."""
+    p = P()
+    st, (rows, max_nnz, mws, fws) = sizes(lib, p)
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
+    f = lib.bsa_attend_static
+    assert f(ctypes.byref(p), FAKE, None, FAKE, ctypes.byref(csr), FAKE, None, None) == 1
+    assert f(ctypes.byref(p), FAKE, FAKE + 8, FAKE, ctypes.byref(csr), FAKE, None, None) == 1
+    big = P(B=10, nh=110, T=16, H=64, W=64)                  # 1100 heads x 512 query-block pairs
+    aws = ctypes.c_int64()
+    assert lib.bsa_query_attend_ws(ctypes.byref(big), ctypes.byref(aws)) == 0
+    assert aws.value > 4 << 20
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, None) == 6
+    assert "static scratch" in lib.bsa_last_error().decode()
 
 
 def test_struct_layouts_match_the_header():
