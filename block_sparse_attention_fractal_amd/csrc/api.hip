@@ -190,15 +190,14 @@ int bsa_build_mask(const bsa_problem* p, const bsa_mask_params* mp, const void* 
     ops.qs = reinterpret_cast<_Float16*>(base + w.qs);
     ops.ks = reinterpret_cast<_Float16*>(base + w.ks);
     ops.qmu = reinterpret_cast<double*>(base + w.qmu);
-    ops.kmu = reinterpret_cast<double*>(base + w.kmu);
+    ops.krec = reinterpret_cast<double2*>(base + w.krec);
     ops.qn = reinterpret_cast<double*>(base + w.qn);
     ops.qe = reinterpret_cast<int32_t*>(base + w.qe);
-    ops.ke = reinterpret_cast<int32_t*>(base + w.ke);
     ops.hstat = reinterpret_cast<uint64_t*>(base + w.hstat);
     int32_t* flags = reinterpret_cast<int32_t*>(base + w.flags);
     int32_t* nflag = reinterpret_cast<int32_t*>(base + w.nflag);
-    e = launch_pool(g, q, k, qp, kp, stream);
-    if (e == hipSuccess) e = launch_screen_ops(g, qp, kp, ops, nflag, stream);
+    e = launch_screen_init(g, ops, nflag, stream);
+    if (e == hipSuccess) e = launch_pool_screen(g, q, k, qp, kp, ops, stream);
     if (e == hipSuccess)
       e = launch_screen_select(g, ops, qp, kp, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words, flags, nflag,
                                stream);

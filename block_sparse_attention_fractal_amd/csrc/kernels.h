@@ -19,22 +19,24 @@ hipError_t launch_prep_vt(const Geom& g, const void* v, void* vt, hipStream_t s)
 // Block means of Q and K in float64 -> qp, kp [B*nh, S, D].
 hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, double* kp, hipStream_t s);
 // Screen operands of the pooled blocks (see mask_screen.hip): fp16 hi / lo of the
-// power-of-two scaled centred vectors ([rows][2][D]), channel means, scale
-// exponents, query-block norms, and per head (max mean, min mean, max norm) of
-// the key blocks as order-preserving 64-bit keys.
+// power-of-two scaled centred vectors ([rows][2][D]), channel means and scale
+// exponents (key blocks: one (mean, exponent) pair per block), query-block norms,
+// and per head (max mean, min mean, max norm) of the key blocks as
+// order-preserving 64-bit keys.
 struct ScreenOps {
   _Float16* qs;
   _Float16* ks;
   double* qmu;
-  double* kmu;
+  double2* krec;
   double* qn;
   int32_t* qe;
-  int32_t* ke;
   uint64_t* hstat;
 };
-// The screen operands of the pooled blocks (launch_pool's qp, kp); also clears nflag.
-hipError_t launch_screen_ops(const Geom& g, const double* qp, const double* kp, const ScreenOps& ops, int32_t* nflag,
-                             hipStream_t s);
+// Resets the per-head statistics of the screen and the flagged-row count.
+hipError_t launch_screen_init(const Geom& g, const ScreenOps& ops, int32_t* nflag, hipStream_t s);
+// launch_pool plus the screen operands in the same pass (after launch_screen_init).
+hipError_t launch_pool_screen(const Geom& g, const void* q, const void* k, double* qp, double* kp,
+                              const ScreenOps& ops, hipStream_t s);
 // Screened reduced map + CDF cut + window union -> bitmap rows and counts; rows it
 // cannot decide are appended to flag_list (count in nflag) for the float64 path.
 hipError_t launch_screen_select(const Geom& g, const ScreenOps& ops, const double* qp, const double* kp, double thr,

@@ -14,9 +14,10 @@
 // The rank-one part is evaluated in float64; the centred part, which no longer
 // carries a component common to all channels (the positional term of video
 // latents), goes through the MFMA as c = c_hi + c_lo in fp16 (each vector scaled
-// by a power of two into [2^13, 2^14)), three products per k-step accumulated in
-// float32.  Its error is at most 2^-15 |c_i| |e_j| (split error 3 * 2^-22 plus
-// 384 float32 additions), so every screened logit of row i is within
+// by a power of two into [2^13, 2^14); the pooling pass writes these operands),
+// three products per k-step accumulated in float32.  Its error is at most
+// 2^-15 |c_i| |e_j| (split error 3 * 2^-22 plus 384 float32 additions), so every
+// screened logit of row i is within
 //   eps_i = 2^-15 |c_i| max_j |e_j| / sqrt(D)
 // of the exact one.  Rows whose eps (plus the float32 rounding of the stored
 // offsets) would move a mass by more than the band allows are handed to an exact
@@ -40,107 +41,17 @@ namespace scr {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxS = 4096;
 constexpr double kScreenErr = 0x1p-15;   // relative error of the screened centred dot product
 constexpr float kTrust = 4e-5f;          // largest offset error (logit units) a screened row may carry
+constexpr int kWaves = 8;
 
 __device__ __forceinline__ double key_to_double(uint64_t k) {
   const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
   return __longlong_as_double((long long)b);
 }
 
-// ---------------------------------------------------------------------------
-// Screen operands of the pooled blocks: channel mean, power-of-two scale
-// exponent, fp16 hi / lo of the scaled centred vector and (query blocks) its
-// norm; per head the max / min key-block mean and the largest key-block norm
-// (order-preserving 64-bit keys, one atomic per workgroup and statistic).
-// grid = (ceil(S / 32), B * heads, 2): z = 0 query blocks, z = 1 key blocks;
-// each wave takes 8 consecutive blocks of one head, one block per step.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void split_fp16(double x, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)(float)x;
-  lo = (_Float16)(float)(x - (double)hi);
-}
-
-template <int D>
-__global__ void __launch_bounds__(256) screen_ops_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
-                                                         ScreenOps ops, Geom g) {
-  constexpr int PL = D / 64;             // channels per lane
-  __shared__ uint64_t red[3][4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t bh = blockIdx.y;
-  const bool keys = blockIdx.z == 1;
-  const double* src = keys ? kp : qp;
-  uint64_t kmax = 0ull, kmin = ~0ull, nmax = 0ull;   // head statistics of this wave's key blocks
-  for (int b = 0; b < 8; ++b) {
-    const int i = (blockIdx.x * 4 + wave) * 8 + b;
-    if (i >= g.S) break;
-    const int64_t r = bh * g.S + i;
-    double v[PL];
-#pragma unroll
-    for (int x = 0; x < PL; ++x) v[x] = src[(size_t)r * D + lane + 64 * x];
-    double sum = 0.0;
-#pragma unroll
-    for (int x = 0; x < PL; ++x) sum += v[x];
-    const double mu = wave_reduce(sum, lane, [](double a, double c) { return a + c; }) * (1.0 / D);
-    double amax = 0.0, n2 = 0.0;
-#pragma unroll
-    for (int x = 0; x < PL; ++x) {
-      v[x] -= mu;
-      amax = fmax(amax, fabs(v[x]));
-      n2 = fma(v[x], v[x], n2);
-    }
-    amax = wave_reduce(amax, lane, [](double a, double c) { return fmax(a, c); });
-    n2 = wave_reduce(n2, lane, [](double a, double c) { return a + c; });
-    const int ex = amax > 0.0 ? 13 - ilogb(amax) : 0;   // scaled magnitudes in [2^13, 2^14)
-    _Float16* dst = (keys ? ops.ks : ops.qs) + (size_t)r * 2 * D;
-#pragma unroll
-    for (int x = 0; x < PL; ++x) {
-      _Float16 hi, lo;
-      split_fp16(ldexp(v[x], ex), hi, lo);
-      dst[lane + 64 * x] = hi;
-      dst[D + lane + 64 * x] = lo;
-    }
-    const double nrm = sqrt(n2) * (1.0 + 0x1p-50);    // rounded up: an upper bound of |c|
-    if (lane == 0) {
-      if (keys) {
-        ops.kmu[r] = mu;
-        ops.ke[r] = ex;
-      } else {
-        ops.qmu[r] = mu;
-        ops.qe[r] = ex;
-        ops.qn[r] = nrm;
-      }
-    }
-    const uint64_t km = order_key(mu);
-    kmax = km > kmax ? km : kmax;
-    kmin = km < kmin ? km : kmin;
-    const uint64_t kn = order_key(nrm);
-    nmax = kn > nmax ? kn : nmax;
-  }
-  if (!keys) return;                     // whole workgroup: z is uniform
-  if (lane == 0) {
-    red[0][wave] = kmax;
-    red[1][wave] = kmin;
-    red[2][wave] = nmax;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t a = red[0][0], b = red[1][0], c = red[2][0];
-    for (int w = 1; w < 4; ++w) {
-      a = red[0][w] > a ? red[0][w] : a;
-      b = red[1][w] < b ? red[1][w] : b;
-      c = red[2][w] > c ? red[2][w] : c;
-    }
-    unsigned long long* hs = (unsigned long long*)(ops.hstat + 3 * bh);
-    atomicMax(&hs[0], (unsigned long long)a);
-    atomicMin(&hs[1], (unsigned long long)b);
-    atomicMax(&hs[2], (unsigned long long)c);
-  }
-}
-
-__global__ void __launch_bounds__(256) hstat_init_kernel(uint64_t* __restrict__ hstat, int32_t* __restrict__ nflag,
-                                                        int64_t heads) {
+__global__ void __launch_bounds__(256) screen_init_kernel(uint64_t* __restrict__ hstat, int32_t* __restrict__ nflag,
+                                                          int64_t heads) {
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x < heads) {
     hstat[3 * x] = 0ull;                 // max of mu: below every key
@@ -150,17 +61,65 @@ __global__ void __launch_bounds__(256) hstat_init_kernel(uint64_t* __restrict__ 
   if (x == 0) *nflag = 0;
 }
 
+// ---- wavefront helpers ------------------------------------------------------
+// value of lane - N inside each row of 16 lanes (0 where that is outside the row)
+template <int N>
+__device__ __forceinline__ uint64_t row_shr64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + N, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + N, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+// inclusive prefix sum over the 64 lanes (lane 0 first): shifts inside the rows of
+// 16 lanes, then the totals of the lower rows read back as scalars
+__device__ __forceinline__ uint64_t wave_prefix_u64(uint64_t v, int lane) {
+  v += row_shr64<1>(v);
+  v += row_shr64<2>(v);
+  v += row_shr64<4>(v);
+  v += row_shr64<8>(v);
+  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
+}
+// sum over each aligned group of 8 lanes (every lane of the group gets it)
+__device__ __forceinline__ double sum8(double v) {
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Screened map + cut.  grid = (ceil(S / ROWS), B * heads), 512 threads (8 waves,
-// two per SIMD): the GEMM of the workgroup's ROWS query blocks against the S key
-// blocks (16 x 16 tiles of v_mfma_f32_16x16x32_f16; A[i][k] in lane 16 (k / 8) + i,
+// two per SIMD).
+//
+// Map: the GEMM of the workgroup's ROWS query blocks against the S key blocks
+// (16 x 16 tiles of v_mfma_f32_16x16x32_f16; A[i][k] in lane 16 (k / 8) + i,
 // register k % 8, B[k][j] likewise with j, C[i][j] in lane 16 (i / 4) + j,
-// register i % 4; wave w takes tiles w, w + 8, ...) writes the offsets
-// zt_ij = z_ij - ub_i (float32, ub_i an upper bound of the row's largest logit,
-// so the offsets of the heavy blocks are small numbers) to LDS; then each wave
-// cuts its rows (ROWS / 8 of them).
+// register i % 4; wave w takes tiles w, w + 8, ..., with the key operands of the
+// next two of its tiles in flight) writes the offsets zt_ij = z_ij - ub_i
+// (float32, ub_i an upper bound of the row's largest logit, so the offsets of the
+// heavy blocks are small numbers) to LDS.
+//
+// LDS layout of a row: lane l's NS blocks NS l .. NS l + NS - 1 are contiguous,
+// each lane's segment padded by 4 floats so that the cut reads them with 16-byte
+// loads free of bank conflicts, and the row pitch is 4 (mod 64) floats so that the
+// four row groups of an MFMA result land in distinct banks.  Once a wave holds
+// its row in registers, the row's LDS is that wave's scratch for the cut
+// (histogram, candidate list, bitmap).
+//
+// Cut: one wavefront per row (ROWS / 8 rows each); the kept blocks of a lane's
+// segment form that lane's bits of the bitmap row.
 // ---------------------------------------------------------------------------
-constexpr int kWaves = 8;
+template <int NS>
+struct CutShape {
+  static constexpr int kSeg = NS + 4;                        // floats per lane segment
+  static constexpr int kPitchV = 64 * kSeg + 4;              // = 4 (mod 64)
+  static constexpr int kPitch = kPitchV < 772 ? 772 : kPitchV;   // also >= the 3 KB of cut scratch
+  static constexpr int kHist = 0, kCand = 512, kBm = 640;    // scratch offsets (floats)
+};
 
 template <int D, int NS, int ROWS>
 __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, const double* __restrict__ qp,
@@ -170,11 +129,9 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
                                                                int32_t* __restrict__ counts, int words,
                                                                int32_t* __restrict__ flag_list,
                                                                int32_t* __restrict__ nflag, double inv_sqrt_d) {
-  constexpr int SP = 64 * NS + 4;        // row pitch of the offsets (floats)
-  __shared__ float vals[ROWS][SP];
-  __shared__ uint64_t hist_all[kWaves][256];    // per bin: count << 44 | mass (2^-30 units)
-  __shared__ uint32_t cand_all[kWaves][128];    // crossing candidates: block ids, then masses
-  __shared__ uint32_t bm_all[kWaves][kMaxS / 32];
+  using CS = CutShape<NS>;
+  static_assert(NS == 2 || (NS % 16 == 0 || NS == 8), "segment shape");
+  __shared__ __attribute__((aligned(16))) float vals[ROWS * CS::kPitch];
   __shared__ double rc_a[ROWS], rc_ub[ROWS], rc_eps[ROWS];
   __shared__ int rc_e[ROWS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -226,80 +183,128 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
     }
     const int ntile = (S + 15) / 16;
     const int jl = lane & 15;
-    auto load_b = [&](int c, f16x8* bhi, f16x8* blo) {
-      const int j = min(16 * c + jl, S - 1);
-      const _Float16* src = ops.ks + (size_t)(rbase + j) * 2 * D + 8 * (lane >> 4);
+    struct BTile {
+      f16x8 hi[D / 32], lo[D / 32];
+      double2 rec;                       // (nu_j, scale exponent of key block j)
+    };
+    // key operands in tile order (see the pooling pass): one contiguous 1 KB per
+    // 32-channel step and half; a tile past the end loads the last tile (kept in
+    // bounds, result unused), whose slots beyond block S - 1 are never stored
+    const int ntile_pad = (S + 15) / 16;
+    const _Float16* ksh = ops.ks + (size_t)bh * ntile_pad * (D / 32) * 1024 + 8 * lane;
+    auto load_b = [&](int c, BTile& b) {
+      const _Float16* src = ksh + (size_t)min(c, ntile_pad - 1) * (D / 32) * 1024;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        bhi[s] = *(const f16x8*)(src + 32 * s);
-        blo[s] = *(const f16x8*)(src + D + 32 * s);
+        b.hi[s] = *(const f16x8*)(src + 1024 * s);
+        b.lo[s] = *(const f16x8*)(src + 1024 * s + 512);
       }
+      b.rec = ops.krec[rbase + min(16 * c + jl, S - 1)];
     };
-    f16x8 bh0[D / 32], bl0[D / 32];
-    int c = wave;
-    if (c < ntile) load_b(c, bh0, bl0);
-    for (; c < ntile; c += kWaves) {
-      f16x8 bh1[D / 32], bl1[D / 32];
-      const bool more = c + kWaves < ntile;
-      if (more) load_b(c + kWaves, bh1, bl1);
-      const int j = 16 * c + jl;
-      const int jc = min(j, S - 1);
-      const double nu = ops.kmu[rbase + jc];
-      const int ek = ops.ke[rbase + jc];
+    auto tile = [&](int c, const BTile& b) {
+      if (c >= ntile) return;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[s], bh0[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[s], bl0[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[s], bh0[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[s], b.hi[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[s], b.lo[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[s], b.hi[s], acc, 0, 0, 0);
       }
+      const int j = 16 * c + jl;
       if (j < S) {
+        const int ek = (int)b.rec.y;
+        float* dst = vals + (j / NS) * CS::kSeg + (j % NS);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int rho = 4 * (lane >> 4) + x;
           if (rho < ROWS) {
-            const double z = fma(ra[x], nu, ldexp((double)acc[x], -(re[x] + ek)));
-            vals[rho][j] = (float)fma(z, inv_sqrt_d, -rub[x]);
+            const double z = fma(ra[x], b.rec.x, ldexp((double)acc[x], -(re[x] + ek)));
+            dst[rho * CS::kPitch] = (float)fma(z, inv_sqrt_d, -rub[x]);
           }
         }
       }
-      if (more) {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-          bh0[s] = bh1[s];
-          bl0[s] = bl1[s];
-        }
-      }
+    };
+    // the scheduling barriers keep the three load groups in ring order, so that the
+    // loads pending at the loop head are the same on entry and on the back edge and
+    // each tile waits only for its own group
+    BTile b0, b1, b2;
+    int c = wave;
+    load_b(c, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(c + kWaves, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; c < ntile; c += 3 * kWaves) {
+      load_b(c + 2 * kWaves, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      tile(c, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(c + 3 * kWaves, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      tile(c + kWaves, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(c + 4 * kWaves, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      tile(c + 2 * kWaves, b2);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
 
   // ---- the cut, one wavefront per row --------------------------------------
-  uint64_t* hist = hist_all[wave];
-  uint32_t* cand = cand_all[wave];
-  uint32_t* bm = bm_all[wave];
   auto u64add = [](uint64_t a, uint64_t b) { return a + b; };
   constexpr uint64_t kMassMask = (1ull << 44) - 1;
-  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  auto set_bit = [&](int j) { atomicOr(&bm[j >> 5], 1u << (j & 31)); };
+  const int jbase = NS * lane;           // this lane's first block
   for (int rho = wave; rho < ROWS; rho += kWaves) {
     const int i = i0 + rho;
     if (i >= S) break;
     const int64_t r = rbase + i;
+    float* row = vals + rho * CS::kPitch;
+    uint64_t* hist = (uint64_t*)(row + CS::kHist);   // bin b at hist[255 - b]
+    uint32_t* cand = (uint32_t*)(row + CS::kCand);   // crossing candidates: block ids, then masses
+    uint32_t* bm = (uint32_t*)(row + CS::kBm);
+    uint64_t bits = 0;                   // bit k: block jbase + k is kept
+    // blocks of this lane below S, opaque per row: the compiler would otherwise hoist
+    // NS loop-invariant lane masks out of the row loop and spill them
+    int nv = S - jbase;
+    asm volatile("" : "+v"(nv));
     bool flagged = false;
+    bool keep_c = false;                 // lane c < ncand: exactly ranked candidate c is kept
+    uint32_t my_j = 0;
     if (thr == 0.0) {
-      for (int x = lane; x < words; x += 64) {
-        const int left = S - 32 * x;
-        bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
-      }
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        if (k < nv) bits |= 1ull << k;
     } else {
-      for (int x = lane; x < words; x += 64) bm[x] = 0u;
       float v[NS];
+      if constexpr (NS == 2) {
+        const float2 x = *(const float2*)(row + lane * CS::kSeg);
+        v[0] = x.x;
+        v[1] = x.y;
+      } else {
+#pragma unroll
+        for (int m = 0; m < NS / 4; ++m) {
+          const float4 x = *(const float4*)(row + lane * CS::kSeg + 4 * m);
+          v[4 * m] = x.x;
+          v[4 * m + 1] = x.y;
+          v[4 * m + 2] = x.z;
+          v[4 * m + 3] = x.w;
+        }
+      }
+      asm volatile("" ::: "memory");     // the row's LDS becomes scratch below
+      // this lane's slice of the query block for the exact dots (8 lanes per candidate)
+      const int sub = lane & 7, slot = lane >> 3;
+      constexpr int kQV = D / 16;        // double2 per slice
+      double2 qv[kQV];
+      auto load_q = [&]() {
+        const double2* qrow = (const double2*)(qp + (size_t)r * D + sub * (D / 8));
+#pragma unroll
+        for (int e = 0; e < kQV; ++e) qv[e] = qrow[e];
+      };
+      if constexpr (NS <= 32) load_q();   // early, in flight during the cut (registers allowing)
       float mt = -FLT_MAX;
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const int j = lane + 64 * k;
-        v[k] = j < S ? vals[rho][j] : -FLT_MAX;
+        v[k] = k < nv ? v[k] : -FLT_MAX;
         mt = fmaxf(mt, v[k]);
       }
       mt = wave_reduce(mt, lane, [](float a, float b) { return fmaxf(a, b); });
@@ -317,59 +322,58 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const float d = v[k] - mt;
-            const bool cand_k = (lane + 64 * k < S) && d >= (float)-lambda;
+            const bool cand_k = d >= (float)-lambda;   // blocks past S hold -FLT_MAX
             v[k] = d;
             const float e = cand_k ? __builtin_amdgcn_exp2f(d * 1.44269504088896341f) : 0.f;
             w[k] = (uint32_t)(e * 1073741824.0f);
             wsum += w[k];
-            if (w[k] != 0u) dmin = fminf(dmin, d);
+            dmin = fminf(dmin, w[k] != 0u ? d : 0.f);
           }
           total = wave_reduce(wsum, lane, u64add);
           dmin = wave_reduce(dmin, lane, [](float a, float b) { return fminf(a, b); });
           tscale = dmin < 0.f ? 16777215.0f / (-dmin) : 0.f;
+          // non-candidates get key 2^31: no radix prefix matches it, it is negative as an
+          // int, and above every margin unsigned (no per-block predicate stays live)
 #pragma unroll
           for (int k = 0; k < NS; ++k)
-            t[k] = w[k] != 0u ? (uint32_t)fminf((v[k] - dmin) * tscale, 16777215.0f) : 0u;
+            t[k] = w[k] != 0u ? (uint32_t)fminf((v[k] - dmin) * tscale, 16777215.0f) : 0x80000000u;
         }
         const double target = (1.0 - thr) * (double)total;
         // (count, mass) histogram of the candidates with bin(k) >= 0 in one 64-bit
         // word per bin, and the bin where the mass from the top first reaches the
         // target; false when no bin does
         auto crossing = [&](auto bin, uint64_t above_in, int& b_out, uint64_t& above_out, uint32_t& cnt_out) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) hist[4 * lane + x] = 0ull;
+          *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+          *(uint4*)(hist + 4 * lane + 2) = make_uint4(0u, 0u, 0u, 0u);
           __builtin_amdgcn_wave_barrier();
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
-            const int b = w[k] != 0u ? bin(k) : -1;
-            if (b >= 0) atomicAdd((unsigned long long*)&hist[b], (1ull << 44) | (unsigned long long)w[k]);
+            const int b = bin(k);
+            if (b >= 0) atomicAdd((unsigned long long*)&hist[255 - b], (1ull << 44) | (unsigned long long)w[k]);
           }
           __builtin_amdgcn_wave_barrier();
+          // lane l holds bins 255 - 4l .. 252 - 4l, highest first
+          const uint4 h01 = *(const uint4*)(hist + 4 * lane), h23 = *(const uint4*)(hist + 4 * lane + 2);
+          const uint64_t hv[4] = {((uint64_t)h01.y << 32) | h01.x, ((uint64_t)h01.w << 32) | h01.z,
+                                  ((uint64_t)h23.y << 32) | h23.x, ((uint64_t)h23.w << 32) | h23.z};
           uint64_t mb[4];
           uint32_t cb[4];
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            const uint64_t hv = hist[4 * lane + x];
-            mb[x] = hv & kMassMask;
-            cb[x] = (uint32_t)(hv >> 44);
+            mb[x] = hv[x] & kMassMask;
+            cb[x] = (uint32_t)(hv[x] >> 44);
           }
           const uint64_t lane_tot = mb[0] + mb[1] + mb[2] + mb[3];
-          uint64_t suf = lane_tot;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t lo = __shfl_down((uint32_t)suf, d, 64), hi = __shfl_down((uint32_t)(suf >> 32), d, 64);
-            if (lane + d < 64) suf += ((uint64_t)hi << 32) | lo;
-          }
-          uint64_t run = suf - lane_tot;
+          uint64_t run = wave_prefix_u64(lane_tot, lane) - lane_tot;   // mass of the higher bins
           int found = -1;
           uint64_t f_above = 0;
           uint32_t f_cnt = 0;
 #pragma unroll
-          for (int x = 3; x >= 0; --x) {
+          for (int x = 0; x < 4; ++x) {
             const uint64_t excl = run;
             run += mb[x];
             if (cb[x] != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + run)) {
-              found = 4 * lane + x;
+              found = 255 - 4 * lane - x;
               f_above = above_in + excl;
               f_cnt = cb[x];
             }
@@ -408,7 +412,7 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
         if (!reach) {
 #pragma unroll
           for (int k = 0; k < NS; ++k)
-            if (w[k] != 0u) set_bit(lane + 64 * k);
+            if ((int)t[k] >= 0) bits |= 1ull << k;
         } else {
           // candidates: the crossing bin widened by the error margin in key units;
           // blocks above it are kept, below it dropped
@@ -416,66 +420,69 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
           const uint32_t lo_t = tpre << tsh, hi_t = lo_t + ((1u << tsh) - 1u);
           const uint32_t lo_m = lo_t > mt_keys ? lo_t - mt_keys : 0u;
           const uint32_t hi_m = hi_t + mt_keys;           // < 2^25: no wrap
-          uint64_t sure = 0;
-          uint32_t base = 0;
+          uint64_t sure = 0, inbits = 0;
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
-            const bool in = w[k] != 0u && t[k] >= lo_m && t[k] <= hi_m;
-            if (w[k] != 0u && t[k] > hi_m) {
-              set_bit(lane + 64 * k);
+            if ((int)t[k] > (int)hi_m) {
+              bits |= 1ull << k;
               sure += w[k];
             }
-            const uint64_t ball = __ballot(in);
-            const uint32_t rank = base + (uint32_t)__popcll(ball & lt_mask);
-            if (in && rank < 64u) {
-              cand[rank] = (uint32_t)(lane + 64 * k);
-              cand[64 + rank] = w[k];
-            }
-            base += (uint32_t)__popcll(ball);
+            if (t[k] >= lo_m && t[k] <= hi_m) inbits |= 1ull << k;
           }
-          above = wave_reduce(sure, lane, u64add);
-          const uint32_t ncand = base;
-          if (ncand > 64u) {
-            flagged = true;
-          } else {
-            __builtin_amdgcn_wave_barrier();
-            // exact float64 logits of the candidates, eight lanes per candidate (each
-            // 16 channels), eight candidates per pass
-            const int sub = lane & 7, slot = lane >> 3;
-            double zc[8];
-            const double* qrow = qp + (size_t)r * D + sub * (D / 8);
+          // candidate slots: this lane's come after those of the lower lanes
+          const uint32_t nin = (uint32_t)__popcll(inbits);
+          const uint64_t incl = wave_prefix_u64(nin, lane);
+          const uint32_t ncand = (uint32_t)readlane_u64(incl, 63);
+          if (ncand <= 64u && inbits != 0ull) {
+            uint32_t slot_c = (uint32_t)incl - nin;
 #pragma unroll
-            for (int pass = 0; pass < 8; ++pass) {
-              zc[pass] = 0.0;
-              const uint32_t cidx = 8u * pass + slot;
-              if (8u * pass < ncand) {
-                const uint32_t j = cidx < ncand ? cand[cidx] : cand[0];
-                const double* krow = kp + (size_t)(rbase + j) * D + sub * (D / 8);
-                double zz = 0.0;
-#pragma unroll
-                for (int d = 0; d < D / 8; d += 2) {
-                  const double2 qv = *(const double2*)(qrow + d);
-                  const double2 kv = *(const double2*)(krow + d);
-                  zz = fma(qv.x, kv.x, zz);
-                  zz = fma(qv.y, kv.y, zz);
-                }
-                zc[pass] = zz;
+            for (int k = 0; k < NS; ++k) {
+              if ((inbits >> k) & 1ull) {
+                cand[slot_c] = (uint32_t)(jbase + k);
+                cand[64 + slot_c] = w[k];
+                ++slot_c;
               }
             }
-            // sum the eight partial dots of each candidate (lanes 8s .. 8s+7) and hand
-            // candidate c to lane c
-            double z = 0.0;
+          }
+          above = wave_reduce(sure, lane, u64add);
+          if (ncand > 64u) {
+            flagged = true;
+          } else if (ncand > 0u) {
+            __builtin_amdgcn_wave_barrier();
+            // exact float64 logits of the candidates: eight lanes per candidate (each
+            // D / 8 channels), eight candidates per pass, the next pass's key slices
+            // in flight while the current one is summed
+            const int np = (int)((ncand + 7u) / 8u);
+            auto load_k = [&](int p, double2* kv) {
+              const uint32_t cidx = min(8u * (uint32_t)p + (uint32_t)slot, ncand - 1u);
+              const double2* krow = (const double2*)(kp + (size_t)(rbase + cand[cidx]) * D + sub * (D / 8));
 #pragma unroll
-            for (int pass = 0; pass < 8; ++pass) {
-              double part = zc[pass];
-              part += __shfl_xor(part, 1, 8);
-              part += __shfl_xor(part, 2, 8);
-              part += __shfl_xor(part, 4, 8);
-              const double mine = __shfl(part, 8 * (lane & 7), 64);   // candidate 8 pass + lane % 8 -> lane
-              if ((lane >> 3) == pass) z = mine;
+              for (int e = 0; e < kQV; ++e) kv[e] = krow[e];
+            };
+            double z = 0.0;
+            auto pass = [&](int p, const double2* kv) {
+              double part = 0.0;
+#pragma unroll
+              for (int e = 0; e < kQV; ++e) {
+                part = fma(qv[e].x, kv[e].x, part);
+                part = fma(qv[e].y, kv[e].y, part);
+              }
+              part = sum8(part);
+              const double mine = __shfl(part, 8 * (lane & 7), 64);   // candidate 8 p + lane % 8 -> lane
+              if ((lane >> 3) == p) z = mine;
+            };
+            if constexpr (NS > 32) load_q();
+            double2 ka[kQV], kb[kQV];
+            load_k(0, ka);
+            for (int p = 0; p < np; p += 2) {
+              load_k(min(p + 1, np - 1), kb);
+              pass(p, ka);
+              if (p + 1 >= np) break;
+              load_k(min(p + 2, np - 1), ka);
+              pass(p + 1, kb);
             }
             const bool have = (uint32_t)lane < ncand;
-            const uint32_t my_j = have ? cand[lane] : 0u;
+            my_j = have ? cand[lane] : 0u;
             const uint32_t my_w = have ? cand[64 + lane] : 0u;
             const uint64_t my_key = have ? order_key(z * inv_sqrt_d) : 0ull;   // as the float64 path scales
             uint64_t before = 0;
@@ -485,7 +492,7 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
               const uint32_t wy = (uint32_t)__builtin_amdgcn_readlane((int)my_w, (int)y);
               if (ky > my_key || (ky == my_key && jy < my_j)) before += wy;
             }
-            if (have && (double)(above + before) < target) set_bit((int)my_j);
+            keep_c = have && (double)(above + before) < target;
           }
         }
       }
@@ -494,6 +501,22 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
       if (lane == 0) flag_list[atomicAdd(nflag, 1)] = (int32_t)r;
       continue;
     }
+    // this lane's bits into the bitmap row, then the exactly ranked candidates and
+    // the window on top
+    if constexpr (NS == 64) {
+      *(uint64_t*)(bm + 2 * lane) = bits;
+    } else if constexpr (NS == 32) {
+      bm[lane] = (uint32_t)bits;
+    } else {
+      constexpr int G = 32 / NS;         // lanes per bitmap word
+      uint32_t x = (uint32_t)bits << ((lane % G) * NS);
+#pragma unroll
+      for (int s = 1; s < G; s <<= 1) x |= (uint32_t)__shfl_xor((int)x, s, 64);
+      if (lane % G == 0) bm[lane / G] = x;
+    }
+    __builtin_amdgcn_wave_barrier();
+    auto set_bit = [&](int j) { atomicOr(&bm[j >> 5], 1u << (j & 31)); };
+    if (keep_c) set_bit((int)my_j);
     if (win_t >= 0) for_each_window_block(g, i, win_t, win_h, win_w, lane, 64, set_bit);
     __builtin_amdgcn_wave_barrier();
     uint32_t pc = 0;
@@ -504,21 +527,14 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
     }
     pc = wave_reduce(pc, lane, [](uint32_t a, uint32_t b2) { return a + b2; });
     if (lane == 0) counts[r] = (int32_t)pc;
-    __builtin_amdgcn_wave_barrier();     // bm is reused by the next row
   }
 }
 
 }  // namespace scr
 
-hipError_t launch_screen_ops(const Geom& g, const double* qp, const double* kp, const ScreenOps& ops, int32_t* nflag,
-                             hipStream_t s) {
+hipError_t launch_screen_init(const Geom& g, const ScreenOps& ops, int32_t* nflag, hipStream_t s) {
   const int64_t heads = (int64_t)g.B * g.nh;
-  scr::hstat_init_kernel<<<(unsigned)((heads + 255) / 256), 256, 0, s>>>(ops.hstat, nflag, heads);
-  dim3 grid((unsigned)((g.S + 31) / 32), (unsigned)heads, 2);
-  if (g.D == 64)
-    scr::screen_ops_kernel<64><<<grid, 256, 0, s>>>(qp, kp, ops, g);
-  else
-    scr::screen_ops_kernel<128><<<grid, 256, 0, s>>>(qp, kp, ops, g);
+  scr::screen_init_kernel<<<(unsigned)((heads + 255) / 256), 256, 0, s>>>(ops.hstat, nflag, heads);
   return hipGetLastError();
 }
 

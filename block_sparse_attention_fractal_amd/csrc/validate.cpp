@@ -82,12 +82,11 @@ MaskWs mask_ws_layout(const Geom& g) {
   w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);
   w.rowstat = off; off = align256(off + g.rows * 4 * 8);
   w.qs = off; off = align256(off + g.rows * 2 * g.D * 2);
-  w.ks = off; off = align256(off + g.rows * 2 * g.D * 2);
+  w.ks = off; off = align256(off + (int64_t)g.B * g.nh * ((g.S + 15) / 16) * 16 * 2 * g.D * 2);   // whole 16-block tiles
   w.qmu = off; off = align256(off + g.rows * 8);
-  w.kmu = off; off = align256(off + g.rows * 8);
+  w.krec = off; off = align256(off + g.rows * 16);
   w.qn = off; off = align256(off + g.rows * 8);
   w.qe = off; off = align256(off + g.rows * 4);
-  w.ke = off; off = align256(off + g.rows * 4);
   w.hstat = off; off = align256(off + (int64_t)g.B * g.nh * 3 * 8);
   w.flags = off; off = align256(off + g.rows * 4);
   w.nflag = off; off = align256(off + 4);

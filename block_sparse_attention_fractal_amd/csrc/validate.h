@@ -16,7 +16,7 @@ struct MaskWs {       // byte offsets into the mask workspace
   int64_t qp, kp, z, counts, bitmap, chunk_sums, rowstat, total;   // rowstat: SIP (max, sum, c, top) per row
   // screened cut: fp16 operands, means, norms, exponents, per-head stats, the list of
   // rows left to the float64 path and its length
-  int64_t qs, ks, qmu, kmu, qn, qe, ke, hstat, flags, nflag;
+  int64_t qs, ks, qmu, krec, qn, qe, hstat, flags, nflag;
   int32_t words;      // 32-bit words per bitmap row
 };
 struct FwdWs {         // work counters and XCD bounds, per-item costs and order (bf16), prepared V (bf16)

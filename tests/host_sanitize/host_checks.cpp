@@ -62,8 +62,8 @@ static void valid_problems() {
       CHECK(g.S * 64 == g.L);
       CHECK(g.rows == (int64_t)s[0] * s[1] * g.S);
       const MaskWs m = mask_ws_layout(g);
-      check_offsets({m.qp, m.kp, m.z, m.counts, m.bitmap, m.chunk_sums, m.rowstat, m.qs, m.ks, m.qmu, m.kmu, m.qn,
-                     m.qe, m.ke, m.hstat, m.flags, m.nflag},
+      check_offsets({m.qp, m.kp, m.z, m.counts, m.bitmap, m.chunk_sums, m.rowstat, m.qs, m.ks, m.qmu, m.krec, m.qn,
+                     m.qe, m.hstat, m.flags, m.nflag},
                     m.total);
       CHECK(m.words == (g.S + 31) / 32);
       const FwdWs f = fwd_ws_layout(g);

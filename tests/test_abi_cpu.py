@@ -62,12 +62,13 @@ def test_query_sizes(lib, B, nh, T, H, W):
     assert rows == B * nh * S and max_nnz == rows * S
     # mask workspace: qp, kp (float64), logits (float64, SIP mode), counts, bitmap, scan chunk
     # sums, SIP row statistics (4 float64 per row); the screened cut's fp16 hi/lo operands of
-    # queries and keys, their means, query norms, scale exponents, per-head statistics
-    # (3 x 8 bytes), the list of rows for the float64 path and its length; each 256-aligned
+    # queries and keys, query means, key (mean, exponent) pairs, query norms and exponents,
+    # per-head statistics (3 x 8 bytes), the list of rows for the float64 path and its
+    # length; each 256-aligned
     a = lambda x: (x + 255) // 256 * 256
     assert mws == (a(rows * D * 8) * 2 + a(rows * S * 8) + a(rows * 4) + a(rows * ((S + 31) // 32) * 4)
                    + a((rows + 1023) // 1024 * 4) + a(rows * 32)
-                   + 2 * a(rows * 2 * D * 2) + 3 * a(rows * 8) + 2 * a(rows * 4) + a(B * nh * 24)
+                   + a(rows * 2 * D * 2) + a(B * nh * ((S + 15) // 16) * 16 * 2 * D * 2) + a(rows * 8) + a(rows * 16) + a(rows * 8) + a(rows * 4) + a(B * nh * 24)
                    + a(rows * 4) + a(4))
     # forward workspace: work counters and XCD bounds, per-item cost and order (one int32 each
     # per query-block pair), prepared V
