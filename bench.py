@@ -30,6 +30,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_hunyuan_hybrid_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", "attn_bf16.hip")
+MASK_SRCS = [os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", f)
+             for f in ("pool.hip", "mask_screen.hip", "mask.hip", "mask_util.h")]
+MASK_TRAFFIC = {4: os.path.join(ROOT, "profiles", "mask_hunyuan_hybrid_traffic.json"),
+                2: os.path.join(ROOT, "profiles", "mask_wan21_traffic.json")}
 
 
 def kernel_sha() -> str:
@@ -54,6 +58,31 @@ def traffic_for_current_kernel(cfg_idx: int):
     if t.get("kernel_sha") != kernel_sha() or t.get("config") != cfg_idx:
         return None
     return t.get("bytes_per_launch")
+
+
+def mask_sha() -> str:
+    """Fingerprint of the mask-stage kernels: their sources plus their build flags."""
+    from block_sparse_attention_fractal_amd import build as _b
+    h = hashlib.sha256()
+    for p in MASK_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    h.update(repr(_b._flags()[:-4] + _b.EXTRA.get("mask_screen.hip", [])).encode())
+    return h.hexdigest()[:16]
+
+
+def mask_traffic(cfg_idx: int):
+    """HBM bytes of one build_mask call from the committed PMC summary (scaled
+    FETCH_SIZE + WRITE_SIZE over every kernel of the stage), or None when the mask
+    kernels changed since the counters were taken or none were taken here."""
+    try:
+        with open(MASK_TRAFFIC[cfg_idx]) as f:
+            t = json.load(f)
+    except (KeyError, OSError, ValueError):
+        return None
+    if t.get("mask_sha") != mask_sha() or t.get("config") != cfg_idx:
+        return None
+    return t.get("bytes_per_call")
 
 
 def density_by_class(cfg, mask):
@@ -340,6 +369,7 @@ def main():
     elt = 2
     mask_bytes = 2.0 * cfg.batch * cfg.heads * cfg.L * cfg.head_dim * elt + 4.0 * (rows + 1) + 4.0 * nnz
     mask_gbs = mask_bytes / (mask_ms * 1e-3) / 1e9
+    mask_tr = mask_traffic(cfg.idx)       # counter-based HBM bytes per call (committed profile), or None
     prep_bytes = 2.0 * cfg.batch * cfg.heads * cfg.L * cfg.head_dim * elt
     prep_gbs = prep_bytes / (prep_ms * 1e-3) / 1e9
     value = cfg.dense_flops / (ms_step * 1e-3) / 1e12
@@ -382,7 +412,9 @@ def main():
                       "timing": f"HIP events over {args.steps} steps, {args.scratch_mb} MB scratch written "
                                 f"between steps (outside the events, inside ms_per_step)"},
         "mask_stage": {"algorithmic_bytes": mask_bytes, "gbs": round(mask_gbs, 1),
-                       "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4), "from": "median build_mask time"},
+                       "hbm_frac": round(mask_gbs / HBM_PEAK_GBS, 4), "from": "median build_mask time",
+                       "traffic": mask_tr,
+                       "counter_gbs": None if mask_tr is None else round(mask_tr / (mask_ms * 1e-3) / 1e9, 1)},
         "prepare_v": {"gbs": round(prep_gbs, 1), "hbm_frac": round(prep_gbs / HBM_PEAK_GBS, 4)},
         "mask_mode": "cdf" if args.sip_seed is None else f"sip(seed={args.sip_seed})",
         "density": round(density, 5),

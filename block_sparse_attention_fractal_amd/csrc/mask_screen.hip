@@ -117,8 +117,8 @@ template <int NS>
 struct CutShape {
   static constexpr int kSeg = NS + 4;                        // floats per lane segment
   static constexpr int kPitchV = 64 * kSeg + 4;              // = 4 (mod 64)
-  static constexpr int kPitch = kPitchV < 772 ? 772 : kPitchV;   // also >= the 3 KB of cut scratch
-  static constexpr int kHist = 0, kCand = 512, kBm = 640;    // scratch offsets (floats)
+  static constexpr int kPitch = kPitchV < 900 ? 900 : kPitchV;   // also >= the 3.5 KB of cut scratch
+  static constexpr int kHist = 0, kCand = 512, kBm = 640, kSink = 768;   // scratch offsets (floats)
 };
 
 template <int D, int NS, int ROWS>
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
   static_assert(NS == 2 || (NS % 16 == 0 || NS == 8), "segment shape");
   __shared__ __attribute__((aligned(16))) float vals[ROWS * CS::kPitch];
   __shared__ double rc_a[ROWS], rc_ub[ROWS], rc_eps[ROWS];
-  __shared__ int rc_e[ROWS];
+  __shared__ int rc_e[ROWS], rc_t[ROWS], rc_y[ROWS], rc_x[ROWS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = g.S;
@@ -154,6 +154,9 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
       rc_ub[tid] = (a * (a >= 0.0 ? bmax : bmin) + nq * cmax) * inv_sqrt_d;
       rc_eps[tid] = kScreenErr * nq * cmax * inv_sqrt_d;
       rc_e[tid] = ops.qe[r];
+      rc_x[tid] = i % g.Wp;                 // the block's tile coordinates (window)
+      rc_y[tid] = (i / g.Wp) % g.Hp;
+      rc_t[tid] = i / (g.Wp * g.Hp);
     }
   }
 
@@ -433,15 +436,19 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
           const uint32_t nin = (uint32_t)__popcll(inbits);
           const uint64_t incl = wave_prefix_u64(nin, lane);
           const uint32_t ncand = (uint32_t)readlane_u64(incl, 63);
-          if (ncand <= 64u && inbits != 0ull) {
+          if (ncand <= 64u) {
+            // branch-free: a block that is no candidate is written to this lane's own
+            // sink slot (distinct per lane, so the stores never collide)
             uint32_t slot_c = (uint32_t)incl - nin;
+            uint32_t* sink = (uint32_t*)(row + CS::kSink) + lane;
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
-              if ((inbits >> k) & 1ull) {
-                cand[slot_c] = (uint32_t)(jbase + k);
-                cand[64 + slot_c] = w[k];
-                ++slot_c;
-              }
+              const bool in = (inbits >> k) & 1ull;
+              uint32_t* dj = in ? cand + slot_c : sink;
+              uint32_t* dw = in ? cand + 64 + slot_c : sink + 64;
+              *dj = (uint32_t)(jbase + k);
+              *dw = w[k];
+              slot_c += in ? 1u : 0u;
             }
           }
           above = wave_reduce(sure, lane, u64add);
@@ -515,9 +522,17 @@ __global__ void __launch_bounds__(512, 1) screen_select_kernel(ScreenOps ops, co
       if (lane % G == 0) bm[lane / G] = x;
     }
     __builtin_amdgcn_wave_barrier();
-    auto set_bit = [&](int j) { atomicOr(&bm[j >> 5], 1u << (j & 31)); };
-    if (keep_c) set_bit((int)my_j);
-    if (win_t >= 0) for_each_window_block(g, i, win_t, win_h, win_w, lane, 64, set_bit);
+    if (keep_c) atomicOr(&bm[my_j >> 5], 1u << (my_j & 31));
+    if (win_t >= 0) {
+      // the window's runs of consecutive blocks, as word masks
+      for_each_window_run(g, rc_t[rho], rc_y[rho], rc_x[rho], win_t, win_h, win_w, lane, 64, [&](int a, int b) {
+        for (int wd = a >> 5; wd <= (b >> 5); ++wd) {
+          const int lo = max(a - 32 * wd, 0), hi = min(b - 32 * wd, 31);
+          const uint32_t m = hi - lo == 31 ? 0xffffffffu : ((1u << (hi - lo + 1)) - 1u) << lo;
+          atomicOr(&bm[wd], m);
+        }
+      });
+    }
     __builtin_amdgcn_wave_barrier();
     uint32_t pc = 0;
     for (int x = lane; x < words; x += 64) {

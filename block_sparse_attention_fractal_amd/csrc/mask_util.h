@@ -101,4 +101,23 @@ __device__ __forceinline__ void for_each_window_block(const Geom& g, int i, int 
   }
 }
 
+// The same window as runs of consecutive block ids: f(a, b) for blocks a .. b, one
+// run per (frame, patch row) of the clipped box around block (ti, yi, xi); thread
+// `first` of `stride` takes runs first, first + stride, ...
+template <typename F>
+__device__ __forceinline__ void for_each_window_run(const Geom& g, int ti, int yi, int xi, int win_t, int win_h,
+                                                    int win_w, int first, int stride, F f) {
+  const int T = g.S / (g.Hp * g.Wp);
+  const int wt = min(win_t, T), wh = min(win_h, g.Hp), ww = min(win_w, g.Wp);   // no overflow below
+  const int t0 = max(ti - wt, 0), t1 = min(ti + wt, T - 1);
+  const int y0 = max(yi - wh, 0), y1 = min(yi + wh, g.Hp - 1);
+  const int x0 = max(xi - ww, 0), x1 = min(xi + ww, g.Wp - 1);
+  const int ny = y1 - y0 + 1, n = (t1 - t0 + 1) * ny;
+  for (int e = first; e < n; e += stride) {
+    const int dt = e / ny, dy = e - dt * ny;
+    const int base = ((t0 + dt) * g.Hp + y0 + dy) * g.Wp;
+    f(base + x0, base + x1);
+  }
+}
+
 }  // namespace bsa

@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < kPoolBlocks; b += 2) {
-      const bool has1 = i0 + b + 1 < g.S, has2 = i0 + b + 2 < g.S && b + 2 < kPoolBlocks;
+      const bool has1 = b + 1 < kPoolBlocks && i0 + b + 1 < g.S, has2 = b + 2 < kPoolBlocks && i0 + b + 2 < g.S;
       if (has1) load(b + 1, bb);
       __builtin_amdgcn_sched_barrier(0);
       process(i0 + b, ba);
