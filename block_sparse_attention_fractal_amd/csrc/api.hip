@@ -254,7 +254,7 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
     int32_t* cost = reinterpret_cast<int32_t*>(ws + w.cost);
     int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
     e = launch_zero_i32(counter, 8, stream);   // one work counter per XCD
-    if (e == hipSuccess) e = launch_attn_schedule(g, mask->row_ptr, mask->col_idx, cost, order, bounds, stream);
+    if (e == hipSuccess) e = launch_attn_schedule(g, mask->row_ptr, mask->col_idx, cost, order, bounds, stream, 2);
     if (e == hipSuccess)
       e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, order, bounds,
                            ncu, stream);

@@ -396,6 +396,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
           l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
         }
+        // raised wave priority for the PV products: when the other wave of the SIMD is
+        // in its softmax, this wave's MFMAs go first and the VALU work fills in
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -404,6 +407,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       j = j1; m0 = m1; shl = shl1;
       j1 = j2; m1 = m2; shl1 = shl2;
@@ -487,18 +491,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 constexpr int kItemOverhead = 4;   // per-item cost in tile steps (Q load, ring prologue, output)
 constexpr int kMaxBitmapWords = 128;   // S <= 4096 blocks
 
-// cost[it] for every item: the pair's two key lists marked in an LDS bitmap and counted
+// cost[it] for every item: the key lists of its nb query blocks marked in an LDS
+// bitmap and counted
 __global__ void __launch_bounds__(256) item_cost_kernel(const int32_t* __restrict__ row_ptr,
-                                                        const int32_t* __restrict__ col_idx, int S, int pairs,
-                                                        int items, int32_t* __restrict__ cost) {
+                                                        const int32_t* __restrict__ col_idx, int S, int groups,
+                                                        int nb, int items, int32_t* __restrict__ cost) {
   __shared__ uint32_t bits[kMaxBitmapWords];
   __shared__ int part[4];
   const int tid = threadIdx.x;
   const int words = (S + 31) >> 5;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int bh = it / pairs, p = it - bh * pairs;
-    const int64_t r0 = (int64_t)bh * S + 2 * p;
-    const int64_t e = row_ptr[r0 + (2 * p + 1 < S ? 2 : 1)];   // the two rows' entries are contiguous
+    const int bh = it / groups, p = it - bh * groups;
+    const int64_t r0 = (int64_t)bh * S + nb * p;
+    const int64_t e = row_ptr[r0 + min(nb, S - nb * p)];   // the rows' entries are contiguous
     for (int w = tid; w < words; w += 256) bits[w] = 0u;
     __syncthreads();
     for (int64_t x = row_ptr[r0] + tid; x < e; x += 256) {
@@ -614,10 +619,10 @@ __global__ void __launch_bounds__(1024) schedule_kernel(const int32_t* __restric
 }
 
 hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, int32_t* cost,
-                                int32_t* order, int32_t* bounds, hipStream_t s) {
-  const int pairs = (g.S + 1) / 2;
-  const int items = (int)((int64_t)g.B * g.nh * pairs);
-  item_cost_kernel<<<std::min(items, 4096), 256, 0, s>>>(row_ptr, col_idx, g.S, pairs, items, cost);
+                                int32_t* order, int32_t* bounds, hipStream_t s, int nb) {
+  const int groups = (g.S + nb - 1) / nb;
+  const int items = (int)((int64_t)g.B * g.nh * groups);
+  item_cost_kernel<<<std::min(items, 4096), 256, 0, s>>>(row_ptr, col_idx, g.S, groups, nb, items, cost);
   schedule_kernel<<<1, 1024, 0, s>>>(cost, items, order, bounds);
   return hipGetLastError();
 }

@@ -783,7 +783,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   const int grid = ((num_cu + 7) / 8) * 8;        // one workgroup per CU (LDS-limited), a multiple of 8 XCDs
   // work orders as for the forward (pairs of query blocks over the CSR, pairs of
   // key blocks over the transposed one); the cost scratch is reused in stream order
-  hipError_t e = launch_attn_schedule(g, row_ptr, col_idx, cost, order_q, bounds, s);
+  hipError_t e = launch_attn_schedule(g, row_ptr, col_idx, cost, order_q, bounds, s, 2);
   if (e != hipSuccess) return e;
   a.ptr = row_ptr;
   a.idx = col_idx;
@@ -794,7 +794,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   bwd::dq_bf16_kernel<true><<<grid2, 256, 0, s>>>(a);    // Delta
   a.counters = counters;
   bwd::dq_bf16_kernel<false><<<grid2, 256, 0, s>>>(a);   // dQ
-  e = launch_attn_schedule(g, tcolptr, trowidx, cost, order_k, bounds + 16, s);
+  e = launch_attn_schedule(g, tcolptr, trowidx, cost, order_k, bounds + 16, s, 2);
   if (e != hipSuccess) return e;
   a.ptr = tcolptr;
   a.idx = trowidx;

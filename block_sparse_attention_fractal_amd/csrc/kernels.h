@@ -69,10 +69,11 @@ hipError_t launch_compact_sip(const Geom& g, const uint32_t* bitmap, int words, 
                               int32_t* col_idx, float* shift, const double* z, const double* rowstat, double thr,
                               int win_t, int win_h, int win_w, hipStream_t s);
 // Block-sparse attention forward (shift: per-CSR-entry natural-log logit shift, or null).
-// Work order of the bf16 attention kernel: per-item costs (cost: one int per
-// item), the item order and the 9 XCD bounds (order: one int per item).
+// Work order over items of nb adjacent query blocks (2 for the bf16 forward and
+// the backward): per-item costs (cost: one int per item), the item order and the 9
+// XCD bounds (order: one int per item).
 hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, int32_t* cost,
-                                int32_t* order, int32_t* bounds, hipStream_t s);
+                                int32_t* order, int32_t* bounds, hipStream_t s, int nb);
 // The same order from given per-item costs (each >= 1).
 hipError_t launch_schedule_costs(const int32_t* cost, int items, int32_t* order, int32_t* bounds, hipStream_t s);
 hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
