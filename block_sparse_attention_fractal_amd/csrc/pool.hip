@@ -73,7 +73,7 @@ __device__ __forceinline__ double group_reduce(double v, int lane, Op op) {
   return v;
 }
 
-constexpr int kPoolBlocks = 4;          // consecutive blocks per wavefront
+constexpr int kPoolBlocks = 2;          // consecutive blocks per wavefront (150 VGPRs, three waves per SIMD)
 
 // grid = (ceil(S / (4 kPoolBlocks)), B * heads, 2): z = 0 pools Q, z = 1 pools K;
 // wave w of workgroup x takes blocks (4x + w) kPoolBlocks + b of head y, with the
