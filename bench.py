@@ -233,7 +233,9 @@ def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
     transposes, the Delta walk, the dQ kernel and the dK/dV kernel) on the bench's mask,
     with a seeded N(0,1) dout.  Executed FLOPs count the 7 tile products of 64 x 64 x D
     (dQ: S, dP, dQ; dK/dV: S, dP, dV, dK) per kept tile; the Delta walk's two products
-    (S, dP again) and the dQ kernel's second (low-part) dZ product are extra work on top."""
+    (S, dP again) and the dQ kernel's second (low-part) dZ product are extra work on top.
+    For bf16 head_dim 128 the training pair is timed as well (attend_train, then
+    backward_train without the Delta walk)."""
     import torch
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     o = torch.empty_like(q)
@@ -259,9 +261,37 @@ def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
     D = q.shape[-1]
     flops = 7.0 * 2 * g.block * g.block * D * mask.nnz()
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms_per_call": round(ms, 4), "executed_tflop": round(flops / 1e12, 3),
-            "executed_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "dout": "seeded N(0,1), bf16"}
+    res = {"ms_per_call": round(ms, 4), "executed_tflop": round(flops / 1e12, 3),
+           "executed_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "dout": "seeded N(0,1), bf16"}
+    if q.dtype == torch.bfloat16 and D == 128:
+        # the training pair: attend_train (P as a bf16 pair in the PV product, o + o_lo)
+        # and backward_train (row term from o + o_lo, no walk over the kept tiles)
+        vt = bsa.prepare_v(v, g)
+        pair = (torch.empty_like(q), torch.empty_like(q))
+        for _ in range(max(1, warmup)):
+            o_t, olo_t, lse_t = bsa.attend_train(q, k, vt, mask, g, workspace=fwd_ws, out=pair)
+            bsa.backward_train(q, k, v, mask, g, o_t, olo_t, lse_t, dout, workspace=ws, out=grads)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            o_t, olo_t, lse_t = bsa.attend_train(q, k, vt, mask, g, workspace=fwd_ws, out=pair)
+        ev[1].record(stream)
+        for _ in range(steps):
+            bsa.backward_train(q, k, v, mask, g, o_t, olo_t, lse_t, dout, workspace=ws, out=grads)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        fms = ev[0].elapsed_time(ev[1]) / steps
+        bms = ev[1].elapsed_time(ev[2]) / steps
+        btf = flops / (bms * 1e-3) / 1e12
+        res["train_pair"] = {"attend_train_ms": round(fms, 4), "backward_train_ms": round(bms, 4),
+                             "backward_train_tflops": round(btf, 2),
+                             "backward_train_mfma_frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "what": "attend_train (o, o_lo, lse) then backward_train (row term dO.(o+o_lo)); "
+                                     "FLOPs as above (7 tile products), the forward's lo PV product on top"}
+        del vt, pair
+    return res
 
 
 def main():

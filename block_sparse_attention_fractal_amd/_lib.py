@@ -19,7 +19,8 @@ BSA_ORDER_FRACTAL, BSA_ORDER_TILE_MAJOR, BSA_ORDER_HILBERT = 0, 1, 2
 # every symbol declared in include/bsa.h
 EXPORTED = ["bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
             "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_query_attend_ws", "bsa_attend",
-            "bsa_attend_static", "bsa_query_backward_ws", "bsa_backward", "bsa_query_group_sizes", "bsa_build_group_mask",
+            "bsa_attend_static", "bsa_query_backward_ws", "bsa_backward", "bsa_attend_train", "bsa_backward_train",
+            "bsa_query_group_sizes", "bsa_build_group_mask",
             "bsa_forward_groups", "bsa_prepare_v_groups", "bsa_query_attend_groups_ws", "bsa_attend_groups", "bsa_status_str", "bsa_last_error",
             "bsa_version"]
 
@@ -78,6 +79,8 @@ def lib():
     l.bsa_attend_static.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp]
     l.bsa_query_backward_ws.argtypes = [P(Problem), P(i64)]
     l.bsa_backward.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, i64, vp]
+    l.bsa_attend_train.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, i64, vp]
+    l.bsa_backward_train.argtypes = [P(Problem), vp, vp, vp, P(CSR), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
     l.bsa_query_group_sizes.argtypes = [P(Problem), ctypes.c_int, P(i64), P(i64), P(i64)]
     l.bsa_build_group_mask.argtypes = [P(Problem), ctypes.c_int, P(MaskParams), vp, vp, P(CSR), vp, i64, vp]
     l.bsa_forward_groups.argtypes = [P(Problem), ctypes.c_int, vp, vp, vp, P(CSR), vp, vp, vp, i64, vp]
@@ -91,7 +94,8 @@ def lib():
     l.bsa_version.argtypes = []
     for name in ("bsa_query_sizes", "bsa_permute", "bsa_order_table", "bsa_permute_table", "bsa_pool",
                  "bsa_block_map", "bsa_build_mask", "bsa_forward", "bsa_prepare_v", "bsa_query_attend_ws",
-                 "bsa_attend", "bsa_attend_static", "bsa_query_backward_ws", "bsa_backward", "bsa_version"):
+                 "bsa_attend", "bsa_attend_static", "bsa_query_backward_ws", "bsa_backward", "bsa_attend_train",
+                 "bsa_backward_train", "bsa_version"):
         getattr(l, name).restype = ctypes.c_int
     _lib = l
     return l

@@ -278,6 +278,27 @@ def attend(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, 
     return (o, lse) if return_lse else o
 
 
+def attend_train(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+                 layout: str = "original", workspace: Optional[torch.Tensor] = None, out=None):
+    """bf16 training forward (bsa_attend_train): returns (o, o_lo, lse), with o + o_lo
+    holding O to ~2^-16 for backward_train.  `vp` = prepare_v(v); `out` = (o, o_lo)."""
+    _check_qkv(q, k)
+    prob = make_problem(q, grid, layout)
+    sz = query_sizes(prob)
+    if mask.rows != sz["rows"]:
+        raise ValueError(f"mask has {mask.rows} rows, the problem needs {sz['rows']}")
+    if vp.numel() != q.numel() or vp.dtype != q.dtype or not vp.is_contiguous():
+        raise ValueError("vp must be a contiguous tensor with q's dtype and size")
+    o, o_lo = (torch.empty_like(q), torch.empty_like(q)) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws = _workspace(attend_workspace_bytes(prob), q.device, workspace)
+    csr = mask.as_struct()
+    check(lib().bsa_attend_train(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), vp.data_ptr(), ctypes.byref(csr),
+                                 o.data_ptr(), o_lo.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 _stream(q.device)))
+    return o, o_lo, lse
+
+
 def attend_static(q: torch.Tensor, k: torch.Tensor, vp: torch.Tensor, mask: BlockMask, grid: VideoGrid,
                   layout: str = "original", return_lse: bool = False, out: Optional[torch.Tensor] = None):
     """attend() through bsa_attend_static: no workspace argument (the library's static
@@ -322,6 +343,29 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask,
     check(lib().bsa_backward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                              ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def backward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, grid: VideoGrid,
+                   o: torch.Tensor, o_lo: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                   layout: str = "original", workspace: Optional[torch.Tensor] = None, out=None):
+    """Gradients (dq, dk, dv) from attend_train's (o, o_lo, lse): the row term is
+    dO . (o + o_lo) (bsa_backward_train), so the walk over the kept tiles that
+    backward() runs for it is skipped.  bf16, head_dim 128."""
+    _check_qkv(q, k, v, dout, o, o_lo)
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [batch, heads, L] as attend_train gives it")
+    prob = make_problem(q, grid, layout)
+    ws = _workspace(backward_workspace_bytes(prob), q.device, workspace)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _check_qkv(q, dq, dk, dv)
+    csr = mask.as_struct()
+    check(lib().bsa_backward_train(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(csr),
+                                   o.data_ptr(), o_lo.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

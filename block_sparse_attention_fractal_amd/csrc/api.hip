@@ -57,7 +57,7 @@ int geom_or_fail(const bsa_problem* p, Geom* g) {
 
 extern "C" {
 
-int bsa_version(void) { return 510; }
+int bsa_version(void) { return 520; }
 
 const char* bsa_status_str(int s) {
   switch (s) {
@@ -242,7 +242,7 @@ static int check_attend_args(const bsa_problem* p, Geom* g, const void* q, const
 }
 
 static int enqueue_attend(const Geom& g, const void* q, const void* k, const void* vp, const bsa_csr* mask, void* o,
-                          float* lse, char* ws, hipStream_t stream) {
+                          float* lse, char* ws, hipStream_t stream, void* o_lo = nullptr) {
   const FwdWs w = fwd_ws_layout(g);
   hipError_t e;
   if (g.dtype == BSA_BF16) {
@@ -256,8 +256,8 @@ static int enqueue_attend(const Geom& g, const void* q, const void* k, const voi
     e = launch_zero_i32(counter, 8, stream);   // one work counter per XCD
     if (e == hipSuccess) e = launch_attn_schedule(g, mask->row_ptr, mask->col_idx, cost, order, bounds, stream, 2);
     if (e == hipSuccess)
-      e = launch_attn_bf16(g, q, k, vp, o, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, order, bounds,
-                           ncu, stream);
+      e = launch_attn_bf16(g, q, k, vp, o, o_lo, lse, mask->row_ptr, mask->col_idx, mask->shift, counter, order,
+                           bounds, ncu, stream);
   } else {
     e = launch_attn_f32(g, (const float*)q, (const float*)k, (const float*)vp, (float*)o, lse, mask->row_ptr,
                         mask->col_idx, mask->shift, stream);
@@ -284,26 +284,33 @@ int bsa_query_backward_ws(const bsa_problem* p, int64_t* bwd_ws) {
   return BSA_OK;
 }
 
-int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
-                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, int64_t ws_bytes,
-                 hipStream_t stream) {
+// Shared by bsa_backward (o == NULL: the Delta walk) and bsa_backward_train
+// (Delta = dO . (o + o_lo) from the training forward's output pair).
+static int backward_impl(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                         const void* o, const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+                         void* dv, void* ws, int64_t ws_bytes, hipStream_t stream, const char* who) {
   Geom g;
   int st = geom_or_fail(p, &g);
   if (st != BSA_OK) return st;
+  const std::string name(who);
   if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !mask || !mask->row_ptr || !mask->col_idx)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: null pointer");
-  const void* t16[] = {q, k, v, dout, dq, dk, dv};
+    return fail(BSA_ERR_INVALID_ARG, name + ": null pointer");
+  const bool from_output = o != nullptr;
+  if (from_output && !o_lo) return fail(BSA_ERR_INVALID_ARG, name + ": null pointer");
+  const void* t16[] = {q, k, v, dout, dq, dk, dv, from_output ? o : q, from_output ? o_lo : q};
   for (const void* t : t16)
-    if (!aligned(t, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: tensors must be 16-byte aligned");
-  if (!aligned(lse, 4)) return fail(BSA_ERR_INVALID_ARG, "bsa_backward: misaligned lse");
-  if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: masks with logit shifts are not supported");
+    if (!aligned(t, 16)) return fail(BSA_ERR_INVALID_ARG, name + ": tensors must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(BSA_ERR_INVALID_ARG, name + ": misaligned lse");
+  if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, name + ": masks with logit shifts are not supported");
+  if (from_output && g.dtype != BSA_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, name + ": the training pair is bf16 only (float32 uses bsa_backward)");
   if (g.dtype == BSA_BF16 && g.D != 128)
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: bf16 head_dim " + std::to_string(g.D) +
+    return fail(BSA_ERR_UNSUPPORTED, name + ": bf16 head_dim " + std::to_string(g.D) +
                                          " (only 128 is implemented; float32 supports 64 and 128)");
   const BwdWs w = bwd_ws_layout(g);
   if (!ws || ws_bytes < w.total)
-    return fail(BSA_ERR_WORKSPACE, "bsa_backward: workspace needs " + std::to_string(w.total) + " bytes");
-  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, "bsa_backward: workspace must be 256-byte aligned");
+    return fail(BSA_ERR_WORKSPACE, name + ": workspace needs " + std::to_string(w.total) + " bytes");
+  if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, name + ": workspace must be 256-byte aligned");
   int ncu = 0;
   if (g.dtype == BSA_BF16) {
     st = current_cu_count(&ncu);
@@ -317,6 +324,7 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
   int32_t* tcolptr = reinterpret_cast<int32_t*>(base + w.tcolptr);
   int32_t* trowidx = reinterpret_cast<int32_t*>(base + w.trowidx);
   hipError_t e = launch_backward_prep(g, lse, ld, mask->row_ptr, mask->col_idx, tbits, w.words, tcounts, stream);
+  if (e == hipSuccess && from_output) e = launch_delta_from_output(g, o, o_lo, dout, ld, stream);
   if (e == hipSuccess)
     e = launch_scan(g, tcounts, tcolptr, reinterpret_cast<int32_t*>(base + w.tchunks), nullptr, stream);
   if (e == hipSuccess) e = launch_compact(g, tbits, w.words, tcolptr, trowidx, stream);
@@ -329,9 +337,24 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
     e = launch_backward(g, q, k, v, dout, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
                         mask->col_idx, tcolptr, trowidx, counters, reinterpret_cast<int32_t*>(base + w.cost),
                         reinterpret_cast<int32_t*>(base + w.order_q), reinterpret_cast<int32_t*>(base + w.order_k),
-                        reinterpret_cast<int32_t*>(base + w.bounds), ncu, stream);
+                        reinterpret_cast<int32_t*>(base + w.bounds), ncu, !from_output, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return BSA_OK;
+}
+
+int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, int64_t ws_bytes,
+                 hipStream_t stream) {
+  return backward_impl(p, q, k, v, mask, nullptr, nullptr, lse, dout, dq, dk, dv, ws, ws_bytes, stream,
+                       "bsa_backward");
+}
+
+int bsa_backward_train(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                       const void* o, const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+                       void* dv, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  if (!o) return fail(BSA_ERR_INVALID_ARG, "bsa_backward_train: null pointer");
+  return backward_impl(p, q, k, v, mask, o, o_lo, lse, dout, dq, dk, dv, ws, ws_bytes, stream,
+                       "bsa_backward_train");
 }
 
 int bsa_prepare_v(const bsa_problem* p, const void* v, void* vt, hipStream_t stream) {
@@ -353,6 +376,19 @@ int bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v
   int st = check_attend_args(p, &g, q, k, vp, mask, o, lse, ws, ws_bytes, false, "bsa_attend");
   if (st != BSA_OK) return st;
   return enqueue_attend(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream);
+}
+
+int bsa_attend_train(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
+                     void* o, void* o_lo, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  int st = check_attend_args(p, &g, q, k, vp, mask, o, lse, ws, ws_bytes, false, "bsa_attend_train");
+  if (st != BSA_OK) return st;
+  if (!o_lo || !lse) return fail(BSA_ERR_INVALID_ARG, "bsa_attend_train: null pointer");
+  if (!aligned(o_lo, 16)) return fail(BSA_ERR_INVALID_ARG, "bsa_attend_train: misaligned pointer");
+  if (g.dtype != BSA_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_train: bf16 only (the float32 path is float64-accurate already)");
+  if (mask->shift) return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_train: masks with logit shifts are not supported");
+  return enqueue_attend(g, q, k, vp, mask, o, lse, static_cast<char*>(ws), stream, o_lo);
 }
 
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask, void* o,

@@ -63,6 +63,7 @@ struct AttnBf16Args {
   const uint16_t* k;
   const uint16_t* vt;
   uint16_t* o;
+  uint16_t* o_lo;      // training variant: O - bf16(O) in bf16 (null otherwise)
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
@@ -140,7 +141,11 @@ __device__ __forceinline__ void opaque_vgpr(uint32_t& x) { asm volatile("" : "+v
 // The body is compiled for the device only: instantiated in the host pass, its
 // LDS address-space casts and VGPR asm operands (dependent on D) would make the
 // instantiation invalid there and drop the launch stub.
-template <int D, bool kShift>   // head dim; whether the CSR carries per-entry logit shifts
+// kTrain: the PV product takes P as a pair of bf16 terms (hi and the rounding
+// residual lo), O is normalised by the float32 sum of P and written as a bf16
+// pair (o and o_lo), so that o + o_lo carries O = sum P v / sum P to ~2^-16 and
+// the backward can form its row term dO . O from it.
+template <int D, bool kShift, bool kTrain>   // head dim; per-entry logit shifts; training variant
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using Sh = Shape<D>;
@@ -344,7 +349,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       wait_barrier4();                                        // K(j) and V(j) resident everywhere
       issue_v(j1, std::integral_constant<int, VS ^ 1>{});     // into the slot V(j-1) used
       issue_k(j2, std::integral_constant<int, (KS + 2) % 3>{});   // into the slot K(j-1) used
-      bf16x8 pbv[4];
+      bf16x8 pbv[4], pbl[4];
       if (m0) {
         f32x16 sacc[2];
 #pragma unroll
@@ -386,15 +391,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int e = 0; e < 16; ++e) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
             l_run += p;
-            pbv[2 * t + (e >> 3)][e & 7] = (__bf16)p;
+            const __bf16 ph = (__bf16)p;
+            pbv[2 * t + (e >> 3)][e & 7] = ph;
+            if constexpr (kTrain) pbl[2 * t + (e >> 3)][e & 7] = (__bf16)(p - (float)ph);
           }
         }
+        if constexpr (!kTrain) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
-          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
-          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
-          l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
+          for (int s = 0; s < 4; ++s) {
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
+            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
+          }
         }
         // raised wave priority for the PV products: when the other wave of the SIMD is
         // in its softmax, this wave's MFMAs go first and the VALU work fills in
@@ -405,6 +414,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int u = 0; u < kOU; ++u) {
             const bf16x8 av = *(lds_bf16x8*)(uintptr_t)(vaddr[s] + VS * kTile + u * 4096);
             oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+            if constexpr (kTrain) oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbl[s], oacc[u], 0, 0, 0);
           }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -436,17 +446,26 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     if (has_q) {
       l_run = pair_sum(l_run);
       l_pv = pair_sum(l_pv);
-      const float inv = l_pv > 0.f ? 1.f / l_pv : 0.f;   // an empty row yields zeros
+      const float lnorm = kTrain ? l_run : l_pv;
+      const float inv = lnorm > 0.f ? 1.f / lnorm : 0.f;   // an empty row yields zeros
       uint8_t* ob = smem + qb * (kTile);       // block qb's 64 x 2D bytes of O
+      uint8_t* obl = smem + (2 + qb) * kTile;  // training variant: block qb's O - bf16(O)
 #pragma unroll
       for (int u = 0; u < kOU; ++u) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int unit = 8 * u + 2 * rq + h;
-          uint2 w;
-          w.x = pack_bf16x2(oacc[u][4 * rq + 0] * inv, oacc[u][4 * rq + 1] * inv);
-          w.y = pack_bf16x2(oacc[u][4 * rq + 2] * inv, oacc[u][4 * rq + 3] * inv);
-          *(uint2*)(ob + qrow * (2 * D) + ((unit ^ (qrow & (D / 4 - 1))) << 3)) = w;
+          const int off = qrow * (2 * D) + ((unit ^ (qrow & (D / 4 - 1))) << 3);
+          float ov[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) ov[x] = oacc[u][4 * rq + x] * inv;
+          *(uint2*)(ob + off) = make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
+          if constexpr (kTrain) {
+            float lo[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) lo[x] = ov[x] - (float)(__bf16)ov[x];
+            *(uint2*)(obl + off) = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+          }
         }
       }
       if (a.lse && h == 0) {
@@ -463,15 +482,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
         const int t7 = tid & 127;
         const int lchunk = t7 % kCh;
         const int base = block_base_row(a, i0 + sb);
-        uint16_t* oh = a.o + (size_t)bh * g.L * D;
-        const uint8_t* ob = smem + sb * kTile;
 #pragma unroll
-        for (int u = 0; u < 64 / kRowsPer; ++u) {
-          const int row = t7 / kCh + kRowsPer * u;
-          const uint2 lo = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk) ^ (row & (D / 4 - 1))) << 3));
-          const uint2 hi = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk + 1) ^ (row & (D / 4 - 1))) << 3));
-          const int tok = base + (row >> 3) * rs + (row & 7);
-          *(uint4*)(oh + (size_t)tok * D + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int part = 0; part < (kTrain ? 2 : 1); ++part) {
+          uint16_t* oh = (part ? a.o_lo : a.o) + (size_t)bh * g.L * D;
+          const uint8_t* ob = smem + (2 * part + sb) * kTile;
+#pragma unroll
+          for (int u = 0; u < 64 / kRowsPer; ++u) {
+            const int row = t7 / kCh + kRowsPer * u;
+            const uint2 lo = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk) ^ (row & (D / 4 - 1))) << 3));
+            const uint2 hi = *(const uint2*)(ob + row * (2 * D) + (((2 * lchunk + 1) ^ (row & (D / 4 - 1))) << 3));
+            const int tok = base + (row >> 3) * rs + (row & 7);
+            *(uint4*)(oh + (size_t)tok * D + lchunk * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
         }
       }
     }
@@ -632,14 +654,15 @@ hipError_t launch_schedule_costs(const int32_t* cost, int items, int32_t* order,
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
-                            const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s) {
+hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, void* o_lo,
+                            float* lse, const int32_t* row_ptr, const int32_t* col_idx, const float* shift,
+                            int32_t* counters, const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s) {
   AttnBf16Args a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.vt = (const uint16_t*)vt;
   a.o = (uint16_t*)o;
+  a.o_lo = (uint16_t*)o_lo;
   a.lse = lse;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -655,16 +678,21 @@ hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const v
   a.pairs = (g.S + 1) / 2;
   a.items = (int32_t)((int64_t)g.B * g.nh * a.pairs);
   const int grid = ((num_cu * 2 + 7) / 8) * 8;   // two resident workgroups per CU, a multiple of 8 XCDs
+  if (o_lo && shift) return hipErrorInvalidValue;   // the training variant takes unshifted masks only
   if (g.D == 64) {
-    if (shift)
-      attn_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    if (o_lo)
+      attn_bf16_kernel<64, false, true><<<grid, 256, 0, s>>>(a);
+    else if (shift)
+      attn_bf16_kernel<64, true, false><<<grid, 256, 0, s>>>(a);
     else
-      attn_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
+      attn_bf16_kernel<64, false, false><<<grid, 256, 0, s>>>(a);
   } else {
-    if (shift)
-      attn_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    if (o_lo)
+      attn_bf16_kernel<128, false, true><<<grid, 256, 0, s>>>(a);
+    else if (shift)
+      attn_bf16_kernel<128, true, false><<<grid, 256, 0, s>>>(a);
     else
-      attn_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
+      attn_bf16_kernel<128, false, false><<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

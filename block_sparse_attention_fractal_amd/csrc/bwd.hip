@@ -16,7 +16,11 @@
 //
 // Three passes, no atomics on the gradients (deterministic):
 //   * Delta: query-major over the CSR, the dQ pass's walk and products without
-//     the dQ product (S^T = K Q^T and dP^T = V dO^T), sums per query;
+//     the dQ product (S^T = K Q^T and dP^T = V dO^T), sums per query -- or, for
+//     the training pair, Delta = dO . (o + o_lo) from the training forward's
+//     output pair (O to ~2^-16 with P fed to its PV product as a bf16 pair), whose
+//     error against sum P dP / sum P is far below what the dQ cancellation
+//     amplifies into a visible error;
 //   * dQ: query-major over the CSR, a pair of query blocks per workgroup (the
 //     forward kernel's schedule): S^T = K Q^T and dP^T = V dO^T with the
 //     32x32x16 bf16 MFMA (each lane holds 32 keys of one query), dZ^T in
@@ -727,7 +731,40 @@ __global__ void __launch_bounds__(256) popcount_rows_kernel(const uint32_t* __re
   if (lane == 0) counts[r] = c;
 }
 
+// Delta = dO . (o + o_lo) per token (float32; products of bf16 values are exact),
+// 16 threads per token, eight channels each.
+__global__ void __launch_bounds__(256) delta_from_output_kernel(const uint16_t* __restrict__ o,
+                                                                const uint16_t* __restrict__ olo,
+                                                                const uint16_t* __restrict__ dout,
+                                                                float2* __restrict__ ld, int64_t ntok) {
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c8 = threadIdx.x & 15;
+  float sum = 0.f;
+  if (tok < ntok) {
+    const size_t off = (size_t)tok * kD + 8 * c8;
+    const uint4 a = *(const uint4*)(o + off), b = *(const uint4*)(olo + off), d = *(const uint4*)(dout + off);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w}, dv[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      sum = fmaf(__uint_as_float(dv[m] << 16), __uint_as_float(av[m] << 16) + __uint_as_float(bv[m] << 16), sum);
+      sum = fmaf(__uint_as_float(dv[m] & 0xFFFF0000u),
+                 __uint_as_float(av[m] & 0xFFFF0000u) + __uint_as_float(bv[m] & 0xFFFF0000u), sum);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 16);
+  if (tok < ntok && c8 == 0) ld[tok].y = sum;
+}
+
 }  // namespace bwd
+
+hipError_t launch_delta_from_output(const Geom& g, const void* o, const void* o_lo, const void* dout, float2* ld,
+                                   hipStream_t s) {
+  const int64_t ntok = (int64_t)g.B * g.nh * g.L;
+  bwd::delta_from_output_kernel<<<(unsigned)((ntok + 15) / 16), 256, 0, s>>>(
+      (const uint16_t*)o, (const uint16_t*)o_lo, (const uint16_t*)dout, ld, ntok);
+  return hipGetLastError();
+}
 
 hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, const int32_t* row_ptr,
                                 const int32_t* col_idx, uint32_t* tbits, int words, int32_t* tcounts, hipStream_t s) {
@@ -745,7 +782,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
                            const void* qt, const void* dot, float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
-                           int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s) {
+                           int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s) {
   const double scale = 1.0 / sqrt((double)g.D);
   if (g.dtype == BSA_F32) {
     const unsigned grid = (unsigned)g.rows;
@@ -791,7 +828,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.order = order_q;
   a.bounds = bounds;
   const int grid2 = ((num_cu * 2 + 7) / 8) * 8;   // two workgroups per CU
-  bwd::dq_bf16_kernel<true><<<grid2, 256, 0, s>>>(a);    // Delta
+  if (delta_walk) bwd::dq_bf16_kernel<true><<<grid2, 256, 0, s>>>(a);    // Delta
   a.counters = counters;
   bwd::dq_bf16_kernel<false><<<grid2, 256, 0, s>>>(a);   // dQ
   e = launch_attn_schedule(g, tcolptr, trowidx, cost, order_k, bounds + 16, s, 2);

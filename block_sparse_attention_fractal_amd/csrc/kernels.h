@@ -76,9 +76,11 @@ hipError_t launch_attn_schedule(const Geom& g, const int32_t* row_ptr, const int
                                 int32_t* order, int32_t* bounds, hipStream_t s, int nb);
 // The same order from given per-item costs (each >= 1).
 hipError_t launch_schedule_costs(const int32_t* cost, int items, int32_t* order, int32_t* bounds, hipStream_t s);
-hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, float* lse,
-                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, int32_t* counters,
-                            const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s);
+// o_lo non-null: the training variant (P as a bf16 pair in the PV product, O
+// normalised by the float32 sum of P, O - bf16(O) written to o_lo; shift must be null).
+hipError_t launch_attn_bf16(const Geom& g, const void* q, const void* k, const void* vt, void* o, void* o_lo,
+                            float* lse, const int32_t* row_ptr, const int32_t* col_idx, const float* shift,
+                            int32_t* counters, const int32_t* order, const int32_t* bounds, int num_cu, hipStream_t s);
 hipError_t launch_attn_f32(const Geom& g, const float* q, const float* k, const float* v, float* o, float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* shift, hipStream_t s);
 // Backward: per-token lse*log2e into ld (.x), and the transposed mask's bitmap
@@ -88,11 +90,15 @@ hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, con
 // Backward: the row term Delta (into ld .y) and dQ over the CSR, dK/dV over the
 // transposed CSR (qt, dot: prepared transposes of Q, dO for bf16; counters: 24
 // ints, zeroed).
+// Backward of the training pair: the row term from the forward's output instead
+// of the Delta walk, Delta = dO . (o + o_lo) per token (into ld .y; bf16, D = 128).
+hipError_t launch_delta_from_output(const Geom& g, const void* o, const void* o_lo, const void* dout, float2* ld,
+                                   hipStream_t s);
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
                            const void* qt, const void* dot, float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
-                           int32_t* order_k, int32_t* bounds, int num_cu, hipStream_t s);
+                           int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s);
 // Logits of query-block means against Sk key columns (blocks or 4-token groups)
 // for heads h0 .. h0+nheads-1; z holds those heads' rows only.
 hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,

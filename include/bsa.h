@@ -266,6 +266,31 @@ int bsa_backward(const bsa_problem* p, const void* q, const void* k, const void*
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, int64_t ws_bytes,
                  hipStream_t stream);
 
+/* The training pair (bf16, head_dim 128 for the backward; NABLA page,
+ * Metodologia item 2 "Expansion", the method trained with the mask): a forward
+ * that also returns the low part of its output, and a backward that takes the
+ * row term from that output instead of recomputing it over the kept tiles.
+ * bsa_attend_train: bsa_attend's arguments and work order, plus o_lo (same
+ * shape and order as o, 16-byte aligned, required) and lse (required).  The PV
+ * product takes P as a pair of bf16 terms (the rounded value and its rounding
+ * residual), O = sum P v / sum P is normalised by the float32 sum of P, and
+ * o = bf16(O), o_lo = bf16(O - o): o + o_lo holds O to ~2^-16 relative.  The
+ * lse equals bsa_attend's; o differs from bsa_attend's in the last bf16 place
+ * (bsa_attend divides by the sum of the rounded weights).  float32 problems and
+ * masks with shifts -> BSA_ERR_UNSUPPORTED.
+ * bsa_backward_train: bsa_backward's arguments, contract and workspace
+ * (bsa_query_backward_ws), plus o and o_lo from bsa_attend_train on the same
+ * mask (required, 16-byte aligned); Delta_n = dO_n . (o_n + o_lo_n).  Its error
+ * against sum P dP / sum P is ~2^-16 of |dO||O|, far below what the dQ sum
+ * amplifies into a visible error even when all keys share a large common
+ * component; bsa_backward's walk over the kept tiles is skipped.  float32
+ * problems -> BSA_ERR_UNSUPPORTED. */
+int bsa_attend_train(const bsa_problem* p, const void* q, const void* k, const void* vp, const bsa_csr* mask,
+                     void* o, void* o_lo, float* lse, void* ws, int64_t ws_bytes, hipStream_t stream);
+int bsa_backward_train(const bsa_problem* p, const void* q, const void* k, const void* v, const bsa_csr* mask,
+                       const void* o, const void* o_lo, const float* lse, const void* dout, void* dq, void* dk,
+                       void* dv, void* ws, int64_t ws_bytes, hipStream_t stream);
+
 /* ---- 4-token key groups ---------------------------------------------
  * Fine-grained key selection gathered into full tiles (AB-Attention page,
  * news.hamidun.com/es/news/14960, "Los tres recursos de AB-Attention", third
@@ -327,7 +352,7 @@ const char* bsa_last_error(void);
  * token-order tables and the backward pass; 300 adds the 4-token key-group path; 400 adds
  * bsa_query_attend_ws and bsa_query_attend_groups_ws (the attention workspaces hold the work
  * order); 500 drops the forward output from bsa_backward (the row term is recomputed); 510
- * adds bsa_attend_static. */
+ * adds bsa_attend_static; 520 adds the training pair bsa_attend_train / bsa_backward_train. */
 int bsa_version(void);
 
 #ifdef __cplusplus

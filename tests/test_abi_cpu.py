@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_version() == 510
+    assert lib.bsa_version() == 520
     for code, name in [(0, "BSA_OK"), (1, "BSA_ERR_INVALID_ARG"), (2, "BSA_ERR_SHAPE"), (3, "BSA_ERR_DTYPE"),
                        (4, "BSA_ERR_UNSUPPORTED"), (5, "BSA_ERR_CAPACITY"), (6, "BSA_ERR_WORKSPACE"),
                        (7, "BSA_ERR_HIP")]:
@@ -197,6 +197,36 @@ def test_attend_static_rejects_before_touching_the_gpu(lib):
     assert aws.value > 4 << 20
     assert f(ctypes.byref(big), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, None) == 6
     assert "static scratch" in lib.bsa_last_error().decode()
+
+
+def test_training_pair_rejects_before_launch(lib):
+    """bsa_attend_train / bsa_backward_train: missing output pair, float32 problems,
+    shifted masks and the bf16 backward's head_dim limit are refused on the host."""
+    p = P()
+    st, (rows, max_nnz, mws, fws) = sizes(lib, p)
+    aws, bws = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.bsa_query_attend_ws(ctypes.byref(p), ctypes.byref(aws)) == 0
+    assert lib.bsa_query_backward_ws(ctypes.byref(p), ctypes.byref(bws)) == 0
+    csr = _lib.CSR(FAKE, FAKE, max_nnz, None, None)
+    shifted = _lib.CSR(FAKE, FAKE, max_nnz, None, FAKE)
+    fa, fb = lib.bsa_attend_train, lib.bsa_backward_train
+    assert fa(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, FAKE, FAKE, aws.value, None) == 1
+    assert fa(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE, None, FAKE, aws.value, None) == 1
+    assert fa(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE + 8, FAKE, FAKE, aws.value, None) == 1
+    assert fa(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(shifted), FAKE, FAKE, FAKE, FAKE, aws.value, None) == 4
+    pf = P(dtype=0)
+    assert lib.bsa_query_attend_ws(ctypes.byref(pf), ctypes.byref(aws)) == 0
+    assert fa(ctypes.byref(pf), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, FAKE, FAKE, FAKE, aws.value, None) == 4
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)   # o, o_lo, lse, dout, dq, dk, dv, ws
+    assert fb(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), None, *args[1:], bws.value, None) == 1
+    assert fb(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(csr), FAKE, None, *args[2:], bws.value, None) == 1
+    assert fb(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(shifted), *args, bws.value, None) == 4
+    assert lib.bsa_query_backward_ws(ctypes.byref(pf), ctypes.byref(bws)) == 0
+    assert fb(ctypes.byref(pf), FAKE, FAKE, FAKE, ctypes.byref(csr), *args, bws.value, None) == 4
+    p64 = P(D=64)
+    assert lib.bsa_query_backward_ws(ctypes.byref(p64), ctypes.byref(bws)) == 0
+    assert fb(ctypes.byref(p64), FAKE, FAKE, FAKE, ctypes.byref(csr), *args, bws.value, None) == 4
+    assert "head_dim" in lib.bsa_last_error().decode()
 
 
 def test_struct_layouts_match_the_header():

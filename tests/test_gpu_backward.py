@@ -11,7 +11,15 @@ tensors take the forward's bar (mean-relative 5e-3, max-abs 2e-2) relative to
 the gradient's scale (max |reference|): dV and dK round P and dZ to bf16 once
 (2^-9 per term, no cancellation, ~2e-3 measured on the CPU by rounding the
 oracle's own P and dZ), and dQ, whose dZ terms of one query sum to zero,
-carries dZ as a hi + lo pair of bf16 values."""
+carries dZ as a hi + lo pair of bf16 values.
+
+The training pair (attend_train + backward_train, mode "train") takes the row
+term from the forward's output pair o + o_lo instead; its error against the
+kernels' own sum P dP / sum P is ~2^-16 |dO||O|, so the same bars apply.  The
+pair's output is checked on its own: o within the forward's bf16 bar, o + o_lo
+ten times tighter (mean-relative 5e-4, max-abs 2e-3: P enters the PV product as a
+bf16 pair, 2^-17, so what remains is the float32 rounding of the logits), and
+lse bit-identical to attend's (same float32 sum in the same order)."""
 import numpy as np
 import pytest
 import torch
@@ -66,7 +74,7 @@ def grad_errors(got, ref, dtype, name, lse_max=0.0):
     return mean_rel <= 5e-3 and err.max() <= 2e-2 * scale, msg
 
 
-def run_case(cfg, inputs, row_ptr=None, col_idx=None, thr=None):
+def run_case(cfg, inputs, row_ptr=None, col_idx=None, thr=None, mode="walk"):
     q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
     g = grid_of(cfg)
     if row_ptr is None:
@@ -74,9 +82,13 @@ def run_case(cfg, inputs, row_ptr=None, col_idx=None, thr=None):
     else:
         mask = bsa.mask_from_csr(torch.from_numpy(row_ptr.astype(np.int32)).cuda(),
                                  torch.from_numpy(col_idx.astype(np.int32)).cuda(), cfg.S)
-    _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
     do_np = dout_for(cfg)
-    dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
+    if mode == "train":
+        o, o_lo, lse = bsa.attend_train(q, k, bsa.prepare_v(v, g), mask, g)
+        dq, dk, dv = bsa.backward_train(q, k, v, mask, g, o, o_lo, lse, to_dev(do_np, cfg.dtype))
+    else:
+        _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+        dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
     torch.cuda.synchronize()
     rp = mask.row_ptr.cpu().numpy().astype(np.int64)
     ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
@@ -95,14 +107,14 @@ def run_case(cfg, inputs, row_ptr=None, col_idx=None, thr=None):
     return msg
 
 
-@pytest.mark.parametrize("ci", [0, 1])
-def test_backward_matches_oracle(ci):
+@pytest.mark.parametrize("ci,mode", [(0, "walk"), (1, "walk"), (1, "train")])
+def test_backward_matches_oracle(ci, mode):
     cfg = get_config(ci)
-    run_case(cfg, make_inputs(cfg))
+    run_case(cfg, make_inputs(cfg), mode=mode)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
-def test_backward_odd_blocks_and_unused_keys(dtype, D):
+@pytest.mark.parametrize("dtype,D,mode", [("bf16", 128, "walk"), ("bf16", 128, "train"), ("f32", 64, "walk")])
+def test_backward_odd_blocks_and_unused_keys(dtype, D, mode):
     """S = 15 (the last pair of query and key blocks is half empty) and a hand-made
     CSR in which key blocks 3 and 11 are kept by no row: their dK, dV must be 0."""
     cfg = small_cfg(dtype=dtype, D=D, T=1, H=24, W=40, seed=9)
@@ -113,24 +125,62 @@ def test_backward_odd_blocks_and_unused_keys(dtype, D):
     for r in range(cfg.rows):
         keep[r, rng.choice(allowed, size=rng.integers(1, 6), replace=False)] = True
     rp, ci = oracle.csr_from_keep(keep)
-    run_case(cfg, make_inputs(cfg), rp, ci)
+    run_case(cfg, make_inputs(cfg), rp, ci, mode=mode)
 
 
-def test_backward_dense_mask_bf16():
+@pytest.mark.parametrize("mode", ["walk", "train"])
+def test_backward_dense_mask_bf16(mode):
     cfg = small_cfg(nh=2, T=2, H=16, W=32, thr=0.0, seed=31)
-    run_case(cfg, make_inputs(cfg), thr=0.0)
+    run_case(cfg, make_inputs(cfg), thr=0.0, mode=mode)
 
 
-def test_backward_strong_common_key_component():
+@pytest.mark.parametrize("mode", ["walk", "train"])
+def test_backward_strong_common_key_component(mode):
     """Local heads with the HunyuanVideo-scale positional amplitude (4): every key
     carries a large common component, the case in which a row term that does not
     match the kernel's own P would leak into dQ."""
     cfg = Config(98, "edge", "bf16", 1, 2, 4, 48, 80, 128, 8, 64, 0.05, None, 4.0, seed=17)
-    run_case(cfg, make_inputs(cfg))
+    run_case(cfg, make_inputs(cfg), mode=mode)
 
 
-@pytest.mark.parametrize("ci,dq_heads,dkv_heads", [(2, (0, 17, 39), (0, 17, 39)), (4, (0, 20), (0, 16))])
-def test_backward_fullsize_sampled(ci, dq_heads, dkv_heads):
+@pytest.mark.parametrize("name,cfg", [("small-bf16", get_config(1)),
+                                      ("ragged-S15", small_cfg(T=1, H=24, W=40, seed=9)),
+                                      ("common-key", Config(98, "edge", "bf16", 1, 2, 4, 48, 80, 128, 8, 64, 0.05,
+                                                            None, 4.0, seed=17))],
+                         ids=["small-bf16", "ragged-S15", "common-key"])
+def test_attend_train_output_pair(name, cfg):
+    """attend_train: o within the forward's bf16 bar, o + o_lo ten times tighter,
+    lse bit-identical to attend's on the same mask."""
+    inputs = make_inputs(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    g = grid_of(cfg)
+    mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window)
+    vt = bsa.prepare_v(v, g)
+    o, o_lo, lse = bsa.attend_train(q, k, vt, mask, g)
+    _, lse_ref = bsa.attend(q, k, vt, mask, g, return_lse=True)
+    torch.cuda.synchronize()
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    src = oracle.fractal_positions(cfg.T, cfg.H, cfg.W, cfg.patch)
+    qf, kf, vf = (inputs[n][:, :, src] for n in "qkv")
+    O, _ = oracle.block_sparse_attention(qf, kf, vf, rp, ci, cfg.block)
+    ref = np.empty_like(O)
+    ref[:, :, src] = O
+    hi = to_host_f64(o)
+    pair = hi + to_host_f64(o_lo)
+    e_hi, e_pair = np.abs(hi - ref), np.abs(pair - ref)
+    mr_hi = e_hi.mean() / np.abs(ref).mean()
+    mr_pair = e_pair.mean() / np.abs(ref).mean()
+    print(f"{name}: o max_abs {e_hi.max():.3e} mean_rel {mr_hi:.3e}; o+o_lo max_abs {e_pair.max():.3e} "
+          f"mean_rel {mr_pair:.3e}")
+    assert np.array_equal(lse.cpu().numpy(), lse_ref.cpu().numpy())
+    assert e_hi.max() <= 2e-2 and mr_hi <= 5e-3
+    assert e_pair.max() <= 2e-3 and mr_pair <= 5e-4
+
+
+@pytest.mark.parametrize("ci,dq_heads,dkv_heads,mode", [(2, (0, 17, 39), (0, 17, 39), "walk"),
+                                                        (4, (0, 20), (0, 16), "walk"), (4, (0, 20), (0, 16), "train")])
+def test_backward_fullsize_sampled(ci, dq_heads, dkv_heads, mode):
     """Full-size workloads as the benchmark's backward leg runs them: the Wan2.1-scale
     one (40 heads, 21 x 32 x 48 tokens) and one batch item of the HunyuanVideo-scale
     hybrid one (24 heads, 33 x 48 x 80 tokens, sliding-tile window; local heads 0-16,
@@ -147,9 +197,14 @@ def test_backward_fullsize_sampled(ci, dq_heads, dkv_heads):
     for n in ("q_bits", "k_bits", "v_bits"):
         inputs.pop(n)
     mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window)
-    _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
     do_np = dout_for(cfg, batch=1)
-    dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
+    if mode == "train":
+        o, o_lo, lse = bsa.attend_train(q, k, bsa.prepare_v(v, g), mask, g)
+        dq, dk, dv = bsa.backward_train(q, k, v, mask, g, o, o_lo, lse, to_dev(do_np, cfg.dtype))
+        del o, o_lo
+    else:
+        _, lse = bsa.forward(q, k, v, mask, g, return_lse=True)
+        dq, dk, dv = bsa.backward(q, k, v, mask, g, lse, to_dev(do_np, cfg.dtype))
     torch.cuda.synchronize()
     del q, k, v, lse
     S = cfg.S
