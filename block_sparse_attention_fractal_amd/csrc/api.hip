@@ -328,13 +328,9 @@ static int backward_impl(const bsa_problem* p, const void* q, const void* k, con
   if (e == hipSuccess)
     e = launch_scan(g, tcounts, tcolptr, reinterpret_cast<int32_t*>(base + w.tchunks), nullptr, stream);
   if (e == hipSuccess) e = launch_compact(g, tbits, w.words, tcolptr, trowidx, stream);
-  if (e == hipSuccess && g.dtype == BSA_BF16) {
-    e = launch_prep_vt(g, q, base + w.qt, stream);
-    if (e == hipSuccess) e = launch_prep_vt(g, dout, base + w.dot, stream);
-  }
   if (e == hipSuccess) e = launch_zero_i32(counters, 24, stream);
   if (e == hipSuccess)
-    e = launch_backward(g, q, k, v, dout, base + w.qt, base + w.dot, ld, dq, dk, dv, mask->row_ptr,
+    e = launch_backward(g, q, k, v, dout, ld, dq, dk, dv, mask->row_ptr,
                         mask->col_idx, tcolptr, trowidx, counters, reinterpret_cast<int32_t*>(base + w.cost),
                         reinterpret_cast<int32_t*>(base + w.order_q), reinterpret_cast<int32_t*>(base + w.order_k),
                         reinterpret_cast<int32_t*>(base + w.bounds), ncu, !from_output, stream);

@@ -28,9 +28,10 @@
 //     transposing LDS reads;
 //   * dK, dV: key-major over the transposed mask (built here: a bitmap per key
 //     block, counted, scanned and compacted), a pair of key blocks per
-//     workgroup: S = Q K^T and dP = dO V^T with the key fragments in registers
-//     (each lane holds 32 queries of one key), then dV^T += dO^T P and
-//     dK^T += Q^T dZ with Q^T and dO^T pre-transposed.
+//     workgroup of producer and consumer waves: S = Q K^T and dP = dO V^T with
+//     the key fragments in registers (each lane holds 32 queries of one key),
+//     then dV^T += dO^T P and dK^T += Q^T dZ with Q^T and dO^T read from the
+//     natural tiles by transposing LDS reads.
 // float32 tensors take two plain kernels with float64 arithmetic (accuracy
 // rather than speed, as in the forward's float32 path); their dQ kernel forms
 // Delta the same way in a first walk over the row.
@@ -70,8 +71,6 @@ struct Args {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const uint16_t* qt;      // prepared transposes [B*nh, S, D, 64]
-  const uint16_t* dot;
   float2* ld;              // per token: (lse * log2 e, Delta); Delta written by the Delta pass
   uint16_t* dq;
   uint16_t* dk;
@@ -130,10 +129,14 @@ struct PairWalk {
   }
 };
 
-// Stores a pair of 64 x 128 bf16 blocks from the transposed accumulators of the
+// Stores a pair of 64 x 128 bf16 blocks from the transposed accumulators of
 // four waves (wave w: block w >> 1, columns 32 (w & 1) .. +31), through LDS.
+// Every thread of the workgroup calls it (two barriers); `valid` threads stage
+// their accumulators, and the 256 threads with `stores` (index tid among them)
+// write the blocks out.
 __device__ __forceinline__ void store_pair(uint8_t* stage, const f32x16 (&acc)[4], float mul, bool valid, int wave,
-                                           int lane, int tid, const Geom& g, int i0, bool two, uint16_t* out_head) {
+                                           int lane, int tid, const Geom& g, int i0, bool two, uint16_t* out_head,
+                                           bool stores = true) {
   const int h = lane >> 5, l32 = lane & 31;
   const int blk = wave >> 1, col = 32 * (wave & 1) + l32;   // col = token of the block
   __syncthreads();
@@ -153,7 +156,7 @@ __device__ __forceinline__ void store_pair(uint8_t* stage, const f32x16 (&acc)[4
   }
   __syncthreads();
   const int sb = tid >> 7;
-  if (sb == 0 || two) {
+  if (stores && (sb == 0 || two)) {
     const int rs = g.layout == 1 ? 8 : g.W;
     const int t7 = tid & 127;
     const int lchunk = t7 & 15;
@@ -358,116 +361,125 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV pass (bf16), key-major over the transposed mask.  Stage: natural Q |
-// natural dO | transposed Q | transposed dO | (lse2, Delta) of the 64 queries:
-// 64.5 KB; two stages.
+// dK/dV pass (bf16), producer / consumer form: 512 threads, waves 0-3 produce
+// and waves 4-7 consume; waves w and w + 4 own the same 32 keys (key block
+// (w & 3) >> 1 of the pair, keys 32 (w & 1) .. +31).  In phase n the producers
+// compute S = Q K^T, dP = dO V^T (K, V fragments in registers), P and dZ of
+// tile n+1 while the consumers accumulate dV^T += dO^T P and dK^T += Q^T dZ of
+// tile n, with P and dZ handed over through LDS in the consumers' operand
+// layout and Q^T, dO^T read from the natural tiles by transposing LDS reads.
+// Two waves per SIMD (one of each role) where the four-wave kernel had one, so
+// one wave's exponentials overlap the other's matrix products.  LDS: three
+// stages of natural Q | natural dO | (lse2, Delta) (tile n for the consumers,
+// n+1 for the producers, n+2 in flight) and the 32 KB hand-over buffer.  The
+// roles run separate loops (so the compiler never keeps both roles' registers
+// live) with the same barriers: two per phase.
 // ---------------------------------------------------------------------------
-constexpr int kLdOff = 4 * kTile;
-constexpr int kStageB = 4 * kTile + 512;
+constexpr int kStagePC = 2 * kTile + 512;
+constexpr int kLdOffPC = 2 * kTile;
+constexpr int kHandOff = 3 * kStagePC;             // 4 producers x 8 KB
+constexpr int kLdsPC = kHandOff + 4 * 8192;
 
-__global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageB];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageB];
+__global__ void __launch_bounds__(512, 1) dkdv_pc_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem_pc[kLdsPC];
   __shared__ int s_item;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w4 = wave & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int kbk = wave >> 1, wkk = wave & 1;     // key block of the pair, which 32 keys of it
+  const int kbk = w4 >> 1, wkk = w4 & 1;     // key block of the pair, which 32 keys of it
   const Geom g = a.g;
   const int rs = g.layout == 1 ? 8 : g.W;
   const float c_log2 = a.c_log2;
-
-  int noff[4], toff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = (4 * wave + u) * 64 + lane;
-    const int m = c >> 4;
-    const int lc = (lane & 15) ^ (m & 15);
-    noff[u] = (((m >> 3) * rs + (m & 7)) * kD + lc * 8) * 2;
-    const int d = c >> 3;
-    const int lv = (lane & 7) ^ ((d >> 1) & 7);
-    toff[u] = d * 128 + lv * 16;
-  }
-  // (lse2, Delta) of the 64 queries: 32 chunks of 16 bytes = 2 tokens each, wave 0
-  const int ldm = 2 * (lane & 31);
-  const int ldoff = (((ldm >> 3) * rs + (ldm & 7))) * 8;
   const int xcd = blockIdx.x & 7;
   const int lo_t = a.bounds[xcd], hi_t = a.bounds[xcd + 1];   // this XCD's stretch of the work order
 
-  for (;;) {
+  int noff[2];                       // this thread's two 16-byte chunks of each natural tile
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = (2 * wave + u) * 64 + lane;
+    const int m = c >> 4;
+    noff[u] = (((m >> 3) * rs + (m & 7)) * kD + (((lane & 15) ^ (m & 15)) * 8)) * 2;
+  }
+  const int ldm = 2 * (lane & 31);   // (lse2, Delta) of the 64 queries: 32 chunks of 2 tokens, wave 0
+  const int ldoff = (((ldm >> 3) * rs + (ldm & 7))) * 8;
+  // transposing reads (as in the dQ pass, rows = queries here): byte offset in the
+  // natural tile of this lane's read for query step s, channel tile u, read r2
+  int trp[4];
+  {
+    const int trj = lane & 15, trg = lane >> 4, hh = trg >> 1;
+    const int c0 = 2 * (trg & 1) + ((trj & 3) >> 1);
+    const int b0 = (4 * hh + (trj >> 2)) * 256 + 16 * (c0 ^ (trj >> 2)) + 8 * (trj & 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) trp[x] = b0 + 64 * (x ^ hh);
+  }
+  auto tr_off = [&](int u, int s, int r2) { return trp[u ^ (2 * r2)] + 2048 * r2 + 4096 * s; };
+  uint8_t* const hand = smem_pc + kHandOff + w4 * 8192;   // this key slice's P / dZ hand-over
+  auto hand_off = [&](int s, int which) { return ((2 * s + which) * 64 + lane) * 16; };
+
+  // item prologue shared by both roles: claim, walk, resources
+  struct Item {
+    int64_t bh;
+    int j0;
+    bool two;
+  };
+  auto claim = [&](Item& it) -> bool {
     if (tid == 0) s_item = lo_t + atomicAdd(&a.counters[xcd], 1);
     __syncthreads();
     const int idx = __builtin_amdgcn_readfirstlane(s_item);
-    if (idx >= hi_t) break;
+    if (idx >= hi_t) return false;
     const int64_t item = a.order[idx];
-    const int64_t bh = item / a.pairs;
-    const int j0 = 2 * (int)(item - bh * a.pairs);
-    const int64_t r0 = bh * g.S + j0;
-    const bool two = j0 + 1 < g.S;
-    const bool has_k = kbk == 0 || two;
-    PairWalk wk;
-    wk.init(a, r0, two, lane);
-
-    const size_t hoff = (size_t)bh * g.L * kD;
+    it.bh = item / a.pairs;
+    it.j0 = 2 * (int)(item - it.bh * a.pairs);
+    it.two = it.j0 + 1 < g.S;
+    return true;
+  };
+  auto issue = [&](const Item& it, int i, int slot) {
+    const size_t hoff = (size_t)it.bh * g.L * kD;
     const __amdgpu_buffer_rsrc_t qrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hoff), (short)0, g.L * kD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t drs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hoff), (short)0, g.L * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t qtrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.qt + hoff), (short)0, g.L * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t dtrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.dot + hoff), (short)0, g.L * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t lrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + (size_t)bh * g.L), (short)0, g.L * 8, 0x00020000);
-    auto issue = [&](int i, uint8_t* st) {
-      const int ic = min(max(i, 0), g.S - 1);
-      const int base = block_base_row(g, ic);
-      const int ns = base * kD * 2;
-      const int ts = ic * kD * 64 * 2;
+    uint8_t* st = smem_pc + slot * kStagePC;
+    const int ic = min(max(i, 0), g.S - 1);
+    const int base = block_base_row(g, ic);
+    const int ns = base * kD * 2;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int slot = (4 * wave + u) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + slot), 16, noff[u], ns, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + kTile + slot), 16, noff[u], ns, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qtrs, (lds_void*)(st + 2 * kTile + slot), 16, toff[u], ts, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(dtrs, (lds_void*)(st + 3 * kTile + slot), 16, toff[u], ts, 0, 0);
-      }
-      if (wave == 0 && lane < 32)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(st + kLdOff), 16, ldoff, base * 8, 0, 0);
-    };
-
-    bf16x8 kreg[8], vreg[8];
-    if (has_k) {
-      const int ktok = block_base_row(g, j0 + kbk) + ((32 * wkk + l32) >> 3) * rs + (l32 & 7);
-      const uint16_t* krow = a.k + ((size_t)bh * g.L + ktok) * kD + 8 * h;
-      const uint16_t* vrow = a.v + ((size_t)bh * g.L + ktok) * kD + 8 * h;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        kreg[s] = *(const bf16x8*)(krow + 16 * s);
-        vreg[s] = *(const bf16x8*)(vrow + 16 * s);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int sl = (2 * wave + u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + sl), 16, noff[u], ns, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + kTile + sl), 16, noff[u], ns, 0, 0);
     }
-    f32x16 dka[4], dva[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        dka[u][e] = 0.f;
-        dva[u][e] = 0.f;
-      }
+    if (wave == 0 && lane < 32) {
+      const __amdgpu_buffer_rsrc_t lrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + (size_t)it.bh * g.L), (short)0, g.L * 8, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(st + kLdOffPC), 16, ldoff, base * 8, 0, 0);
+    }
+  };
 
-    int i;
-    bool ka, kb;
-    wk.next(a, lane, i, ka, kb);
-    if (i != 0x7fffffff) issue(i, stage0);
-    auto step = [&](uint8_t* st, uint8_t* other) {
-      int in_;
-      bool kan, kbn;
-      wk.next(a, lane, in_, kan, kbn);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (in_ != 0x7fffffff) issue(in_, other);
-      const bool mine = kbk == 0 ? ka : kb;
-      if (mine) {
+  if (wave < 4) {
+    // ---- producers ----
+    Item it;
+    while (claim(it)) {
+      const int64_t r0 = it.bh * g.S + it.j0;
+      const bool has_k = kbk == 0 || it.two;
+      PairWalk wk;
+      wk.init(a, r0, it.two, lane);
+      bf16x8 kreg[8], vreg[8];
+      if (has_k) {
+        const int ktok = block_base_row(g, it.j0 + kbk) + ((32 * wkk + l32) >> 3) * rs + (l32 & 7);
+        const uint16_t* krow = a.k + ((size_t)it.bh * g.L + ktok) * kD + 8 * h;
+        const uint16_t* vrow = a.v + ((size_t)it.bh * g.L + ktok) * kD + 8 * h;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          kreg[s] = *(const bf16x8*)(krow + 16 * s);
+          vreg[s] = *(const bf16x8*)(vrow + 16 * s);
+        }
+      }
+      bf16x8 pb[4], db[4];
+      // P and dZ of the tile in `slot` (this wave's 32 keys x 64 queries) into pb, db
+      auto produce = [&](int slot) {
+        const uint8_t* st = smem_pc + slot * kStagePC;
         f32x16 sacc[2], pacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -485,8 +497,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Args a) {
           }
         }
         // accumulator register e of tile t holds query 32t + 8(e/4) + 4h + e%4
-        bf16x8 pb[4], db[4];
-        const float2* ldt = (const float2*)(st + kLdOff);
+        const float2* ldt = (const float2*)(st + kLdOffPC);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -497,28 +508,125 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(Args a) {
             db[2 * t + (e >> 3)][e & 7] = (__bf16)(p * (pacc[t][e] - ld.y));
           }
         }
+      };
+      auto hand_over = [&]() {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+          *(bf16x8*)(hand + hand_off(s, 0)) = pb[s];
+          *(bf16x8*)(hand + hand_off(s, 1)) = db[s];
+        }
+      };
+      int i0t, i1t;
+      bool ka0, kb0, ka1, kb1;
+      wk.next(a, lane, i0t, ka0, kb0);
+      wk.next(a, lane, i1t, ka1, kb1);
+      if (i0t != 0x7fffffff) issue(it, i0t, 0);
+      if (i1t != 0x7fffffff) issue(it, i1t, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const bool mine0 = kbk == 0 ? ka0 : kb0;
+      if (i0t != 0x7fffffff && mine0) {
+        produce(0);
+        hand_over();
+      }
+      __syncthreads();
+      // phase loop: the consumers take tile `cur` (slot cs), the producers tile `nxt`
+      int cur = i0t, nxt = i1t;
+      bool kan = ka1, kbn = kb1;
+      int cs = 0;
+      while (cur != 0x7fffffff) {
+        int i2t;
+        bool ka2, kb2;
+        wk.next(a, lane, i2t, ka2, kb2);
+        const int ns = cs == 2 ? 0 : cs + 1, ns2 = ns == 2 ? 0 : ns + 1;
+        if (i2t != 0x7fffffff) issue(it, i2t, ns2);
+        const bool mine = nxt != 0x7fffffff && (kbk == 0 ? kan : kbn);
+        if (mine) produce(ns);
+        __syncthreads();                 // the consumers have read tile cur's hand-over
+        if (mine) hand_over();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile i2t landed
+        __syncthreads();
+        cur = nxt;
+        nxt = i2t;
+        kan = ka2;
+        kbn = kb2;
+        cs = ns;
+      }
+      f32x16 none[4];
+      store_pair(smem_pc, none, 1.f, false, w4, lane, tid, g, it.j0, it.two, a.dv + (size_t)it.bh * g.L * kD, false);
+      store_pair(smem_pc, none, 1.f, false, w4, lane, tid, g, it.j0, it.two, a.dk + (size_t)it.bh * g.L * kD, false);
+    }
+  } else {
+    // ---- consumers ----
+    Item it;
+    while (claim(it)) {
+      const int64_t r0 = it.bh * g.S + it.j0;
+      const bool has_k = kbk == 0 || it.two;
+      PairWalk wk;
+      wk.init(a, r0, it.two, lane);
+      f32x16 dka[4], dva[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bf16x8 adt = *(const bf16x8*)(st + 3 * kTile + tr_lds(32 * u + l32, 2 * s + h));
-            dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt, pb[s], dva[u], 0, 0, 0);
-            const bf16x8 aqt = *(const bf16x8*)(st + 2 * kTile + tr_lds(32 * u + l32, 2 * s + h));
-            dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, db[s], dka[u], 0, 0, 0);
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          dka[u][e] = 0.f;
+          dva[u][e] = 0.f;
+        }
+      int i0t, i1t;
+      bool ka0, kb0, ka1, kb1;
+      wk.next(a, lane, i0t, ka0, kb0);
+      wk.next(a, lane, i1t, ka1, kb1);
+      if (i0t != 0x7fffffff) issue(it, i0t, 0);
+      if (i1t != 0x7fffffff) issue(it, i1t, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      __syncthreads();                   // the producers hand over tile i0t
+      int cur = i0t, nxt = i1t;
+      bool kac = ka0, kbc = kb0, kan = ka1, kbn = kb1;
+      int cs = 0;
+      while (cur != 0x7fffffff) {
+        int i2t;
+        bool ka2, kb2;
+        wk.next(a, lane, i2t, ka2, kb2);
+        const int ns = cs == 2 ? 0 : cs + 1, ns2 = ns == 2 ? 0 : ns + 1;
+        if (i2t != 0x7fffffff) issue(it, i2t, ns2);
+        if (kbk == 0 ? kac : kbc) {
+          const uint8_t* st = smem_pc + cs * kStagePC;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 pbs = *(const bf16x8*)(hand + hand_off(s, 0));
+            const bf16x8 dbs = *(const bf16x8*)(hand + hand_off(s, 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const v4i16 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + kTile + tr_off(u, s, 0)));
+              const v4i16 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + kTile + tr_off(u, s, 1)));
+              const bf16x8 adt = __builtin_bit_cast(
+                  bf16x8, (v8i16){dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]});
+              dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt, pbs, dva[u], 0, 0, 0);
+              const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 0)));
+              const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 1)));
+              const bf16x8 aqt = __builtin_bit_cast(
+                  bf16x8, (v8i16){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]});
+              dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, dbs, dka[u], 0, 0, 0);
+            }
           }
         }
+        __syncthreads();                 // tile cur's hand-over read
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile i2t landed
+        __syncthreads();                 // tile nxt handed over
+        cur = nxt;
+        nxt = i2t;
+        kac = kan;
+        kbc = kbn;
+        kan = ka2;
+        kbn = kb2;
+        cs = ns;
       }
-      i = in_;
-      ka = kan;
-      kb = kbn;
-    };
-    while (i != 0x7fffffff) {
-      step(stage0, stage1);
-      if (i == 0x7fffffff) break;
-      step(stage1, stage0);
+      (void)nxt;
+      store_pair(smem_pc, dva, 1.f, has_k, w4, lane, tid - 256, g, it.j0, it.two, a.dv + (size_t)it.bh * g.L * kD);
+      store_pair(smem_pc, dka, a.inv_sqrt_d, has_k, w4, lane, tid - 256, g, it.j0, it.two,
+                 a.dk + (size_t)it.bh * g.L * kD);
     }
-    store_pair(stage0, dva, 1.f, has_k, wave, lane, tid, g, j0, two, a.dv + hoff);
-    store_pair(stage0, dka, a.inv_sqrt_d, has_k, wave, lane, tid, g, j0, two, a.dk + hoff);
   }
 }
 
@@ -779,7 +887,7 @@ hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, con
 }
 
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* qt, const void* dot, float2* ld, void* dq, void* dk,
+                           float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s) {
@@ -806,8 +914,6 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout;
-  a.qt = (const uint16_t*)qt;
-  a.dot = (const uint16_t*)dot;
   a.ld = ld;
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
@@ -838,7 +944,7 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
   a.counters = counters + 8;
   a.order = order_k;
   a.bounds = bounds + 16;
-  bwd::dkdv_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  bwd::dkdv_pc_kernel<<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

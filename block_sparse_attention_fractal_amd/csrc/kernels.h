@@ -95,7 +95,7 @@ hipError_t launch_backward_prep(const Geom& g, const float* lse, float2* ld, con
 hipError_t launch_delta_from_output(const Geom& g, const void* o, const void* o_lo, const void* dout, float2* ld,
                                    hipStream_t s);
 hipError_t launch_backward(const Geom& g, const void* q, const void* k, const void* v, const void* dout,
-                           const void* qt, const void* dot, float2* ld, void* dq, void* dk,
+                           float2* ld, void* dq, void* dk,
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s);

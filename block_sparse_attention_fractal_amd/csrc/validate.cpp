@@ -126,11 +126,6 @@ BwdWs bwd_ws_layout(const Geom& g) {
   w.tbitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
   w.tcolptr = off; off = align256(off + (g.rows + 1) * 4);
   w.trowidx = off; off = align256(off + g.rows * (int64_t)g.S * 4);
-  w.qt = w.dot = off;
-  if (g.dtype == BSA_BF16) {
-    w.qt = off; off = align256(off + tok * g.D * 2);
-    w.dot = off; off = align256(off + tok * g.D * 2);
-  }
   w.total = off;
   return w;
 }

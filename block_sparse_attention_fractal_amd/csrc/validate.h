@@ -22,8 +22,8 @@ struct MaskWs {       // byte offsets into the mask workspace
 struct FwdWs {         // work counters and XCD bounds, per-item costs and order (bf16), prepared V (bf16)
   int64_t counter, bounds, cost, order, vt, total;
 };
-struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work counters and orders, prepared transposes (bf16)
-  int64_t delta, counter, bounds, cost, order_q, order_k, tcounts, tchunks, tbitmap, tcolptr, trowidx, qt, dot, total;
+struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work counters and orders
+  int64_t delta, counter, bounds, cost, order_q, order_k, tcounts, tchunks, tbitmap, tcolptr, trowidx, total;
   int32_t words;
 };
 struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits, bits

@@ -70,7 +70,7 @@ static void valid_problems() {
       check_offsets({f.counter, f.cost, f.order, f.vt}, f.total);
       const BwdWs b = bwd_ws_layout(g);
       check_offsets({b.delta, b.counter, b.bounds, b.cost, b.order_q, b.order_k, b.tcounts, b.tchunks, b.tbitmap,
-                     b.tcolptr, b.trowidx, b.qt, b.dot}, b.total);
+                     b.tcolptr, b.trowidx}, b.total);
       CHECK(b.counter + 24 * 4 <= b.bounds);
       std::string msg;
       if (check_group(g, BSA_KEY_GROUP, &msg) == BSA_OK) {
