@@ -2,7 +2,7 @@
 """Benchmark of the block-sparse video attention hot path on one MI355X.
 
 One step = the whole path over one batch already resident in HBM:
-  build_mask(q, k)  (block pooling, float64 block logits, CDF cut + window, CSR)
+  build_mask(q, k)  (block pooling, screened reduced map kept on chip, CDF cut + window, CSR)
   prepare_v(v)      (V to fractal block order, per-block transposed)
   attend(q, k, v')  (block-sparse attention over the kept 64 x 64 tiles)
 The fractal permutation of Q, K and O is fused into the loads/stores of these
@@ -12,7 +12,9 @@ Prints ONE JSON line.  `value` is dense-equivalent TFLOP/s of a whole step
 (4*B*heads*L^2*D / step time); `roofline` covers the attention kernel
 (executed FLOPs / its own event-timed duration vs the bf16 MFMA peak);
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
-workload and extrapolates it to one full call.
+workload and extrapolates it to one full call.  The default invocation (no
+--config) also times the Wan2.1-scale workload (config 2, short rows) and
+reports it under `short_rows`.
 """
 import argparse
 import hashlib
@@ -294,6 +296,55 @@ def time_backward(bsa, q, k, v, mask, g, fwd_ws, steps, warmup, stream):
     return res
 
 
+def time_short_rows(bsa, steps, warmup, stream, scratch):
+    """The Wan2.1-scale workload (config 2: 2.8 % of the tiles kept, ~14 per row): the
+    short-row regime, timed like the main line (events per stage, scratch written
+    between steps) and reported beside it."""
+    import torch
+    from workloads import get_config, make_inputs
+    cfg = get_config(2)
+    dev = torch.device("cuda:0")
+    inputs = make_inputs(cfg)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(inputs[n + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+               for n in "qkv")
+    del inputs
+    g = bsa.VideoGrid(cfg.T, cfg.H, cfg.W, cfg.patch, cfg.block)
+    sz = bsa.query_sizes(bsa.make_problem(q, g))
+    mask_ws = torch.empty(sz["mask_ws"], dtype=torch.uint8, device=dev)
+    fwd_ws = torch.empty(max(sz["fwd_ws"], 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(warmup + steps):
+        if scratch.numel():
+            scratch.fill_(s & 0xFF)
+        ev = events[s - warmup] if s >= warmup else None
+        if ev is not None:
+            ev[0].record(stream)
+        mask = bsa.build_mask(q, k, g, cfg.thr, cfg.window, workspace=mask_ws)
+        if ev is not None:
+            ev[1].record(stream)
+        vt = bsa.prepare_v(v, g)
+        if ev is not None:
+            ev[2].record(stream)
+        bsa.attend(q, k, vt, mask, g, workspace=fwd_ws, out=o)
+        if ev is not None:
+            ev[3].record(stream)
+    torch.cuda.synchronize()
+    st = [np.array([e[i].elapsed_time(e[i + 1]) for e in events]) for i in range(3)]
+    nnz = mask.nnz()
+    flops = 4.0 * cfg.block * cfg.block * cfg.head_dim * nnz
+    att = float(np.median(st[2]))
+    return {"workload": f"config 2 {cfg.name}: B={cfg.batch}, heads={cfg.heads}, T x H x W = {cfg.T}x{cfg.H}x{cfg.W}, "
+                        f"thr={cfg.thr}",
+            "build_mask_ms": {"median": round(float(np.median(st[0])), 4), "min": round(float(st[0].min()), 4)},
+            "prepare_v_ms": {"median": round(float(np.median(st[1])), 4), "min": round(float(st[1].min()), 4)},
+            "attend_ms": {"median": round(att, 4), "min": round(float(st[2].min()), 4)},
+            "density": round(nnz / float(mask.rows * mask.S), 5),
+            "attend_tflops": round(flops / (att * 1e-3) / 1e12, 2),
+            "attend_frac": round(flops / (att * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "dense_equiv_tflops": round(cfg.dense_flops / (float(np.median(st[0] + st[1] + st[2])) * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,7 +353,9 @@ def main():
     ap.add_argument("--scratch-mb", type=int, default=512,
                     help="MB of scratch written between timed steps so that the 256 MB MALL holds none of the "
                          "inputs when a step starts (0 disables)")
-    ap.add_argument("--config", type=int, default=4, help="workload index (default 4: HunyuanVideo-scale hybrid)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload index (default 4: HunyuanVideo-scale hybrid; the default run also reports the "
+                         "Wan2.1-scale config 2 figures under short_rows)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also print per-stage details on stderr")
@@ -313,6 +366,9 @@ def main():
     ap.add_argument("--sip-seed", type=int, default=None,
                     help="build the mask by SIP sampling with this Philox seed instead of the CDF cut")
     args = ap.parse_args()
+    short_rows = args.config is None and args.sip_seed is None
+    if args.config is None:
+        args.config = 4
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path shards by (batch, head) "
                                    "without communication, so a multi-GPU figure is N independent copies of it",
@@ -461,6 +517,10 @@ def main():
         rp = mask.row_ptr.cpu().numpy().astype(np.int64)
         ci = mask.col_idx[:nnz].cpu().numpy()
         line["cpu_baseline"], line["mask_check"] = cpu_baseline(cfg, inputs, rp, ci, exec_flops, args.cpu_seconds)
+    if short_rows:
+        del inputs, q, k, v, o, mask_ws, fwd_ws, mask
+        torch.cuda.empty_cache()
+        line["short_rows"] = time_short_rows(bsa, args.steps, args.warmup, stream, scratch)
     print(json.dumps(line), flush=True)
 
 
