@@ -488,12 +488,17 @@ __global__ void __launch_bounds__(512, 1) dkdv_pc_kernel(Args a) {
             sacc[t][e] = 0.f;
             pacc[t][e] = 0.f;
           }
+          bf16x8 aq[8], ad[8];
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const bf16x8 aq = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
-            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc[t], 0, 0, 0);
-            const bf16x8 ad = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
-            pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[s], pacc[t], 0, 0, 0);
+            aq[s] = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
+            ad[s] = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[s], kreg[s], sacc[t], 0, 0, 0);
+            pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[s], vreg[s], pacc[t], 0, 0, 0);
           }
         }
         // accumulator register e of tile t holds query 32t + 8(e/4) + 4h + e%4
@@ -596,18 +601,21 @@ __global__ void __launch_bounds__(512, 1) dkdv_pc_kernel(Args a) {
           for (int s = 0; s < 4; ++s) {
             const bf16x8 pbs = *(const bf16x8*)(hand + hand_off(s, 0));
             const bf16x8 dbs = *(const bf16x8*)(hand + hand_off(s, 1));
+            bf16x8 adt[4], aqt[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const v4i16 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + kTile + tr_off(u, s, 0)));
               const v4i16 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + kTile + tr_off(u, s, 1)));
-              const bf16x8 adt = __builtin_bit_cast(
-                  bf16x8, (v8i16){dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]});
-              dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt, pbs, dva[u], 0, 0, 0);
+              adt[u] = __builtin_bit_cast(bf16x8, (v8i16){dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]});
               const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 0)));
               const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + tr_off(u, s, 1)));
-              const bf16x8 aqt = __builtin_bit_cast(
-                  bf16x8, (v8i16){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]});
-              dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, dbs, dka[u], 0, 0, 0);
+              aqt[u] = __builtin_bit_cast(bf16x8, (v8i16){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt[u], pbs, dva[u], 0, 0, 0);
+              dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt[u], dbs, dka[u], 0, 0, 0);
             }
           }
         }
