@@ -143,6 +143,39 @@ def test_backward_strong_common_key_component(mode):
     run_case(cfg, make_inputs(cfg), mode=mode)
 
 
+@pytest.mark.parametrize("dtype,D,mode", [("bf16", 128, "walk"), ("bf16", 128, "train"), ("f32", 64, "walk")])
+def test_backward_fractal_layout_matches_original(dtype, D, mode):
+    """The whole path in fractal token order (inputs permuted, layout="fractal",
+    gradients permuted back) gives gradients bit-identical to the original order's:
+    the kernels change only their addressing with the layout."""
+    cfg = small_cfg(dtype=dtype, nh=2, T=3, H=16, W=24, D=D, thr=0.2, seed=21)
+    inputs = make_inputs(cfg)
+    g = grid_of(cfg)
+    q, k, v = (to_device(inputs, n, cfg.dtype) for n in "qkv")
+    dout = to_dev(dout_for(cfg), cfg.dtype)
+
+    def grads(layout):
+        x = [q, k, v, dout]
+        if layout == "fractal":
+            x = [bsa.permute(t, g) for t in x]
+        qq, kk, vv, dd = x
+        mask = bsa.build_mask(qq, kk, g, cfg.thr, layout=layout)
+        if mode == "train":
+            o, o_lo, lse = bsa.attend_train(qq, kk, bsa.prepare_v(vv, g, layout=layout), mask, g, layout=layout)
+            out = bsa.backward_train(qq, kk, vv, mask, g, o, o_lo, lse, dd, layout=layout)
+        else:
+            _, lse = bsa.forward(qq, kk, vv, mask, g, layout=layout, return_lse=True)
+            out = bsa.backward(qq, kk, vv, mask, g, lse, dd, layout=layout)
+        if layout == "fractal":
+            out = [bsa.permute(t, g, inverse=True) for t in out]
+        torch.cuda.synchronize()
+        return [t.cpu() for t in out]
+
+    a, b = grads("original"), grads("fractal")
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), name
+
+
 @pytest.mark.parametrize("name,cfg", [("small-bf16", get_config(1)),
                                       ("ragged-S15", small_cfg(T=1, H=24, W=40, seed=9)),
                                       ("common-key", Config(98, "edge", "bf16", 1, 2, 4, 48, 80, 128, 8, 64, 0.05,
