@@ -294,11 +294,19 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(Args a) {
             pacc[e] = 0.f;
           }
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const bf16x8 ak = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * s + h));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc, 0, 0, 0);
-            const bf16x8 av = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * s + h));
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc, 0, 0, 0);
+          for (int s0 = 0; s0 < 8; s0 += 4) {
+            bf16x8 ak[4], av[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              ak[s] = *(const bf16x8*)(st + nat_lds(32 * t + l32, 2 * (s0 + s) + h));
+              av[s] = *(const bf16x8*)(st + kTile + nat_lds(32 * t + l32, 2 * (s0 + s) + h));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[s], qreg[s0 + s], sacc, 0, 0, 0);
+              pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s], doreg[s0 + s], pacc, 0, 0, 0);
+            }
           }
           if constexpr (kDelta) {
 #pragma unroll
