@@ -247,12 +247,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: BlockMask, 
     return (o, lse) if return_lse else o
 
 
-def prepare_v(v: torch.Tensor, grid: VideoGrid, layout: str = "original") -> torch.Tensor:
+def prepare_v(v: torch.Tensor, grid: VideoGrid, layout: str = "original",
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 only: V in the attention kernel's layout (fractal block order, per-block
-    transposed).  Returned as a flat bf16 tensor of V's size."""
+    transposed).  Returned as a flat bf16 tensor of V's size (written into `out` when given)."""
     _check_qkv(v)
     prob = make_problem(v, grid, layout)
-    vt = torch.empty(v.numel(), dtype=v.dtype, device=v.device)
+    if out is not None and (out.numel() != v.numel() or out.dtype != v.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor with v's dtype and size")
+    vt = torch.empty(v.numel(), dtype=v.dtype, device=v.device) if out is None else out
     check(lib().bsa_prepare_v(ctypes.byref(prob), v.data_ptr(), vt.data_ptr(), _stream(v.device)))
     return vt
 
