@@ -582,8 +582,9 @@ hipError_t launch_select(const Geom& g, const double* z, double thr, double lamb
 //   p_j  = exp(z_j - max) / sum                       (the reduced map, float64)
 //   pi_top = 1 for the row's top block (largest p, lowest id on ties), and for
 //   the others pi_j = min(1, c p_j),  sum_j pi_j = k  (k = the row's CDF-cut count)
-//   take j iff u_rj < pi_j,  u_rj from Philox4x64-10 at counter (r, j, 0, 0),
-//   key (seed, 0): u = (word0 >> 11) * 2^-53
+//   take j iff u_rj < pi_j,  u_rj from Philox4x64-10 at counter (r, floor(j/4), 0, 0),
+//   key (seed, 0): u = (word_(j mod 4) >> 11) * 2^-53 (one generator block serves
+//   four consecutive blocks of the row)
 //
 // c is found by capping: c = (k - t) / (mass of the uncapped blocks), then every
 // uncapped block with c p_j >= 1 is capped (pi = 1) and c recomputed, until none
@@ -596,9 +597,9 @@ __device__ __forceinline__ double block_prob(double z, double m, double sum) { r
 __device__ __forceinline__ double incl_prob(double p, double c) { return p > 0.0 ? fmin(1.0, c * p) : 0.0; }
 
 // Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw: "Parallel random numbers:
-// as easy as 1, 2, 3", SC 2011): word 0 of the block at counter (c0, c1, 0, 0),
-// key (k0, 0).
-__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t k0) {
+// as easy as 1, 2, 3", SC 2011): the four words of the block at counter
+// (c0, c1, 0, 0), key (k0, 0).
+__device__ __forceinline__ void philox4x64(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t (&w)[4]) {
   uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0, key0 = k0, key1 = 0;
 #pragma unroll
   for (int rnd = 0; rnd < 10; ++rnd) {
@@ -611,7 +612,10 @@ __device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint
     key0 += 0x9E3779B97F4A7C15ull;
     key1 += 0xBB67AE8584CAA73Bull;
   }
-  return x0;
+  w[0] = x0;
+  w[1] = x1;
+  w[2] = x2;
+  w[3] = x3;
 }
 
 template <int NS>
@@ -644,11 +648,14 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     }
   } else {
     for (int x = lane; x < words; x += 64) bm[x] = 0u;
+    // slot k of this lane holds block jk(k): lane groups of four consecutive blocks,
+    // so that one generator block serves a lane's four draws
+    auto jk = [&](int k) { return 4 * (lane + 64 * (k >> 2)) + (k & 3); };
     double p[NS];
     m = -DBL_MAX;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int j = lane + 64 * k;
+      const int j = jk(k);
       const double v = zr[min(j, S - 1)];
       p[k] = j < S ? v : -DBL_MAX;
       m = fmax(m, p[k]);
@@ -657,7 +664,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     double part = 0.0;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      p[k] = lane + 64 * k < S ? exp(p[k] - m) : 0.0;
+      p[k] = jk(k) < S ? exp(p[k] - m) : 0.0;
       part += p[k];
     }
     sum = dsum(part);
@@ -665,7 +672,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     double pmax = 0.0;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      p[k] = lane + 64 * k < S ? block_prob(zr[lane + 64 * k], m, sum) : 0.0;
+      p[k] = p[k] / sum;                       // = block_prob(z_j, m, sum), the same operations
       pos += p[k] > 0.0;
       pmax = fmax(pmax, p[k]);
     }
@@ -675,7 +682,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
     int tj = S;
 #pragma unroll
     for (int k = 0; k < NS; ++k)
-      if (p[k] == pmax) tj = min(tj, lane + 64 * k);
+      if (p[k] == pmax) tj = min(tj, jk(k));
     top = (int)wave_reduce((uint32_t)tj, lane, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
     // the others share budget - 1: min(1, c p_j), capped blocks found by iteration
     const int kk = budget - 1;
@@ -685,7 +692,7 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
       uint64_t capped = 0;                     // bit k: slot k of this lane is capped (or the top block)
 #pragma unroll
       for (int k = 0; k < NS; ++k)
-        if (lane + 64 * k == top) capped |= 1ull << k;
+        if (jk(k) == top) capped |= 1ull << k;
       int t = 0;
       for (int it = 0; it <= S; ++it) {        // every pass caps at least one block
         double rest = 0.0;
@@ -709,18 +716,25 @@ __global__ void __launch_bounds__(256) sip_kernel(const double* __restrict__ z, 
       }
     }                                          // else c stays +inf: every positive block is taken
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const int j = lane + 64 * k;
-      if (j < S) {
-        // u in [0, 1): pi >= 1 is always taken and pi == 0 never, so the draw is
-        // only made where it can decide
-        const double pi = j == top ? 1.0 : incl_prob(p[k], c);
-        if (pi >= 1.0) {
-          set_bit(j);
-        } else if (pi > 0.0) {
-          const double u = (double)(philox4x64_w0((uint64_t)r, (uint64_t)j, seed) >> 11) * 0x1p-53;
-          if (u < pi) set_bit(j);
-        }
+    for (int kq = 0; kq < NS / 4; ++kq) {
+      // u in [0, 1): pi >= 1 is always taken and pi == 0 never, so the generator
+      // runs only where one of the four blocks needs a draw
+      const int q = lane + 64 * kq;            // blocks 4q .. 4q+3, generator counter (r, q)
+      double pi[4];
+      bool draw = false;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int j = 4 * q + w;
+        pi[w] = j >= S ? 0.0 : (j == top ? 1.0 : incl_prob(p[4 * kq + w], c));
+        if (pi[w] >= 1.0) set_bit(j);
+        draw |= pi[w] > 0.0 && pi[w] < 1.0;
+      }
+      if (draw) {
+        uint64_t u64[4];
+        philox4x64((uint64_t)r, (uint64_t)q, seed, u64);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (pi[w] > 0.0 && pi[w] < 1.0 && (double)(u64[w] >> 11) * 0x1p-53 < pi[w]) set_bit(4 * q + w);
       }
     }
   }
@@ -747,7 +761,7 @@ hipError_t launch_sip(const Geom& g, const double* z, double thr, uint64_t seed,
   const unsigned grid = (unsigned)((g.rows + 3) / 4);
 #define BSA_SIP(NS_) \
   sip_kernel<NS_><<<grid, 256, 0, s>>>(z, g, thr, seed, win_t, win_h, win_w, bitmap, counts, rowstat, words)
-  if (g.S <= 128) BSA_SIP(2);
+  if (g.S <= 256) BSA_SIP(4);
   else if (g.S <= 512) BSA_SIP(8);
   else if (g.S <= 1024) BSA_SIP(16);
   else if (g.S <= 2048) BSA_SIP(32);

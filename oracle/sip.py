@@ -27,9 +27,10 @@ Readings taken where the page is silent (also listed with the design notes):
   S4  the draw is one independent Bernoulli trial per (row, block) -- Poisson
       sampling, for which the Horvitz-Thompson weights 1 / pi are exactly the
       unbiasing ones -- with the uniform variate of Philox4x64-10 (Salmon et al.,
-      "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter
-      (row, block, 0, 0) and key (seed, 0): u = (word0 >> 11) * 2^-53, and the
-      block is taken iff u < pi.
+      "Parallel random numbers: as easy as 1, 2, 3", SC 2011): the block at
+      counter (row, floor(block / 4), 0, 0) and key (seed, 0) gives four words,
+      one per block of four consecutive blocks, u = (word_(block mod 4) >> 11)
+      * 2^-53, and the block is taken iff u < pi.
   S5  blocks of the sliding-tile window are always present and carry no weight
       (pi = 1); the window is unioned after the sampling.
   S6  the weight enters attention as the additive logit shift log(1 / pi) on
@@ -76,13 +77,15 @@ def philox4x64_10(ctr: np.ndarray, key) -> np.ndarray:
 
 
 def uniforms(rows: np.ndarray, S: int, seed: int) -> np.ndarray:
-    """u[r, j] in [0, 1) for the given CSR rows and every block j (reading S4)."""
+    """u[r, j] in [0, 1) for the given CSR rows and every block j (reading S4):
+    word j mod 4 of the generator block at counter (r, floor(j / 4))."""
     rows = np.asarray(rows, np.uint64)
-    ctr = np.zeros((len(rows), S, 4), np.uint64)
+    nq = (S + 3) // 4
+    ctr = np.zeros((len(rows), nq, 4), np.uint64)
     ctr[..., 0] = rows[:, None]
-    ctr[..., 1] = np.arange(S, dtype=np.uint64)[None, :]
-    w0 = philox4x64_10(ctr, (seed, 0))[..., 0]
-    return (w0 >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    ctr[..., 1] = np.arange(nq, dtype=np.uint64)[None, :]
+    words = philox4x64_10(ctr, (seed, 0)).reshape(len(rows), 4 * nq)[:, :S]
+    return (words >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
 
 
 def inclusion_probabilities(a: np.ndarray, k: int) -> np.ndarray:

@@ -34,6 +34,24 @@ def test_philox_matches_numpy(key, state):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("row,seed", [(1, 7), (5, 123456789), (300, 2**63 + 5)])
+def test_uniforms_are_numpys_philox_words(row, seed):
+    """Reading S4: u[r, j] is word j mod 4 of the Philox4x64-10 block at counter
+    (r, floor(j / 4), 0, 0), key (seed, 0) -- checked against numpy's own Philox
+    (numpy advances its counter before producing a block, so its state is set
+    one below the wanted counter)."""
+    S = 37
+    u = sip.uniforms(np.array([row]), S, seed)[0]
+    for q in range((S + 3) // 4):
+        gen = np.random.Philox(key=np.array([seed, 0], dtype=np.uint64),
+                               counter=np.array([row - 1, q, 0, 0], dtype=np.uint64))
+        words = gen.random_raw(4)
+        for w in range(4):
+            j = 4 * q + w
+            if j < S:
+                assert u[j] == float(int(words[w]) >> 11) * 2.0 ** -53
+
+
 def test_uniforms_range_and_mean():
     u = sip.uniforms(np.arange(300), 400, seed=99)
     assert u.min() >= 0.0 and u.max() < 1.0
