@@ -451,6 +451,7 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
   double* qp = reinterpret_cast<double*>(base + w.qp);
   double* kg = reinterpret_cast<double*>(base + w.kg);
   double* z = reinterpret_cast<double*>(base + w.z);
+  double* partmax = reinterpret_cast<double*>(base + w.partmax);
   int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
   const bool win = mp->win_t >= 0;
@@ -464,9 +465,10 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
   const int64_t bh = (int64_t)g.B * g.nh;
   for (int64_t h0 = 0; h0 < bh && e == hipSuccess; h0 += w.chunk_heads) {
     const int64_t nh = std::min<int64_t>(w.chunk_heads, bh - h0);
-    e = launch_logits(g, qp, kg, z, (int)SG, h0, nh, stream);
+    e = launch_logits(g, qp, kg, z, (int)SG, h0, nh, stream, partmax);
     if (e == hipSuccess)
-      e = launch_group_select(g, z, h0 * g.S, nh * g.S, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words, stream);
+      e = launch_group_select(g, z, h0 * g.S, nh * g.S, partmax, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words,
+                              stream);
   }
   if (e == hipSuccess)
     e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);

@@ -9,9 +9,10 @@
 //     over a chunk of heads at a time so the workspace stays bounded;
 //   * group_select_kernel: the CDF cut of one row per 1024-thread workgroup.
 //     A row has L/4 entries (31 680 at 33 x 48 x 80 tokens), too many to hold
-//     in registers as the block select does, so the row is read twice from
-//     the logits (max, then the float32 offsets z - max into LDS, 4 B per
-//     entry) and every radix pass runs over LDS (the float32 exponential of an
+//     in registers as the block select does, so the row is read once from the
+//     logits (the float32 offsets z - max into LDS, 4 B per entry; the row max
+//     comes from the maxima of its 64-column parts, written by the logit GEMM's
+//     epilogue) and every radix pass runs over LDS (the float32 exponential of an
 //     entry is only recomputed where its mass enters a histogram or the exact
 //     ranking; the keys are a subtraction and a scale).  The numerics are those of the
 //     block select: the ORDER is decided on the float64 logits, the masses are
@@ -90,11 +91,13 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   const uint32_t lo = __shfl_xor((uint32_t)v, d, 64), hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
   return ((unsigned long long)hi << 32) | lo;
 }
+
 __device__ __forceinline__ double shfl_xor_f64(double v, int d) {
   return __longlong_as_double((long long)shfl_xor_u64((unsigned long long)__double_as_longlong(v), d));
 }
 
-__global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restrict__ z, int64_t row0, int SG,
+__global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restrict__ z,
+                                                           const double* __restrict__ partmax, int64_t row0, int SG,
                                                            Geom g, double thr, double lambda, int win_t, int win_h,
                                                            int win_w, uint32_t* __restrict__ bitmap,
                                                            int32_t* __restrict__ counts, int words) {
@@ -179,16 +182,12 @@ __global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restr
       sm.bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
     }
   } else {
-    // pass 1 over the logits: row max; pass 2: candidates, masses, offsets into
-    // LDS (four independent loads in flight per thread in both passes)
+    // the row max from the maxima of its 64-column parts (the GEMM's epilogue);
+    // one pass over the logits: candidates, masses, offsets into LDS (four loads
+    // in flight per thread)
+    const int nparts = 2 * ((SG + 127) / 128);
     double m = -DBL_MAX;
-    for (int j0 = tid; j0 < SG; j0 += 4 * kNT) {
-      double v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = zr[min(j0 + u * kNT, SG - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) m = fmax(m, v[u]);
-    }
+    for (int x = tid; x < nparts; x += kNT) m = fmax(m, partmax[(size_t)blockIdx.x * nparts + x]);
     m = max_f64(m);
     unsigned long long wsum = 0;
     float dmin = 0.f;
@@ -407,11 +406,12 @@ hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, double thr,
+hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, const double* partmax,
+                               double thr,
                                double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
                                int words, hipStream_t s) {
-  gmask::group_select_kernel<<<(unsigned)nrows, gmask::kNT, 0, s>>>(z, row0, g.L / 4, g, thr, lambda, win_t, win_h, win_w,
-                                                             bitmap, counts, words);
+  gmask::group_select_kernel<<<(unsigned)nrows, gmask::kNT, 0, s>>>(z, partmax, row0, g.L / 4, g, thr, lambda, win_t,
+                                                                    win_h, win_w, bitmap, counts, words);
   return hipGetLastError();
 }
 

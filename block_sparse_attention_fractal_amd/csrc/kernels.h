@@ -100,15 +100,18 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s);
 // Logits of query-block means against Sk key columns (blocks or 4-token groups)
-// for heads h0 .. h0+nheads-1; z holds those heads' rows only.
+// for heads h0 .. h0+nheads-1; z holds those heads' rows only.  partmax (or null):
+// per row of those heads, the largest logit of each 64-column part of the row
+// (2 * ceil(Sk / 128) values per row).
 hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
-                         int64_t nheads, hipStream_t s);
+                         int64_t nheads, hipStream_t s, double* partmax = nullptr);
 // 4-token key groups: float64 group means of k -> kg [B*nh, L/4, D].
 hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStream_t s);
 // CDF cut + window union over the L/4 group logits of rows row0 .. row0+nrows-1
 // (z: those rows, L/4 entries each) -> bitmap rows and kept counts.
-hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, double thr,
-                               double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+// partmax: the rows' per-part maxima from launch_logits (2 * ceil(L/4 / 128) per row).
+hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, const double* partmax,
+                               double thr, double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
                                int words, hipStream_t s);
 int group_select_max_groups();
 // V -> [B*nh, L/4, D, 4] bf16 (each group channel-major) for the gathered attention.

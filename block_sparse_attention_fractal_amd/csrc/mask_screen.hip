@@ -45,10 +45,6 @@ constexpr double kScreenErr = 0x1p-15;   // relative error of the screened centr
 constexpr float kTrust = 4e-5f;          // largest offset error (logit units) a screened row may carry
 constexpr int kWaves = 8;
 
-__device__ __forceinline__ double key_to_double(uint64_t k) {
-  const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
-  return __longlong_as_double((long long)b);
-}
 
 __global__ void __launch_bounds__(256) screen_init_kernel(uint64_t* __restrict__ hstat, int32_t* __restrict__ nflag,
                                                           int64_t heads) {

@@ -14,6 +14,12 @@ __device__ __forceinline__ uint64_t order_key(double z) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
+// inverse of order_key
+__device__ __forceinline__ double key_to_double(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
 // Wavefront-wide reduction with DPP moves inside each row of 16 lanes and lane
 // swaps across rows and halves; every lane ends with the result.
 __device__ __forceinline__ uint32_t dpp_step(uint32_t v, int step) {

@@ -154,6 +154,7 @@ GrpMaskWs grp_mask_ws_layout(const Geom& g) {
   w.qp = off; off = align256(off + g.rows * g.D * 8);
   w.kg = off; off = align256(off + bh * SG * g.D * 8);
   w.z = off; off = align256(off + w.chunk_heads * per_head);
+  w.partmax = off; off = align256(off + w.chunk_heads * g.S * 2 * ((SG + 127) / 128) * 8);   // per 64-column part
   w.counts = off; off = align256(off + g.rows * 4);
   w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
   w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);

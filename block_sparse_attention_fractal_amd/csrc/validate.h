@@ -26,8 +26,8 @@ struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work cou
   int64_t delta, counter, bounds, cost, order_q, order_k, tcounts, tchunks, tbitmap, tcolptr, trowidx, total;
   int32_t words;
 };
-struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits, bits
-  int64_t qp, kg, z, counts, bitmap, chunk_sums, total;
+struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits and their rows' part maxima, bits
+  int64_t qp, kg, z, partmax, counts, bitmap, chunk_sums, total;
   int64_t chunk_heads;  // heads whose group logits are computed together
   int32_t words;        // 32-bit words per bitmap row (L/4 bits)
 };

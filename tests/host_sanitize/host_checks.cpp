@@ -75,7 +75,7 @@ static void valid_problems() {
       std::string msg;
       if (check_group(g, BSA_KEY_GROUP, &msg) == BSA_OK) {
         const GrpMaskWs gm = grp_mask_ws_layout(g);
-        check_offsets({gm.qp, gm.kg, gm.z, gm.counts, gm.bitmap, gm.chunk_sums}, gm.total);
+        check_offsets({gm.qp, gm.kg, gm.z, gm.partmax, gm.counts, gm.bitmap, gm.chunk_sums}, gm.total);
         CHECK(gm.chunk_heads >= 1);
         const GrpFwdWs gf = grp_fwd_ws_layout(g);
         check_offsets({gf.counter, gf.cost, gf.order, gf.vg}, gf.total);

@@ -259,11 +259,12 @@ def test_query_group_sizes(lib, B, nh, T, H, W):
     rows = B * nh * S
     assert max_nnz == rows * SG
     # workspace: query-block means, group means, a chunk of heads of group logits
-    # (as many heads as fit 2 GiB, at least one), counts, bitmap, scan chunk sums
+    # (as many heads as fit 2 GiB, at least one) and their rows' maxima per 64-column part, counts,
+    # bitmap, scan chunk sums
     a = lambda x: (x + 255) // 256 * 256
     per_head = S * SG * 8
     chunk = max(1, min(B * nh, (1 << 31) // per_head))
-    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(rows * 4)
+    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(chunk * S * 2 * ((SG + 127) // 128) * 8) + a(rows * 4)
                    + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
     assert fws == 256 + 2 * a(rows * 4) + a(B * nh * L * D * 2)
     aws = ctypes.c_int64()
