@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "mask_screen.hip", "group_mask.hip", "attn_bf16.hip", "attn_f32.hip",
+SOURCES = ["api.hip", "permute.hip", "pool.hip", "mask.hip", "mask_screen.hip", "group_mask.hip", "group_screen.hip", "attn_bf16.hip", "attn_f32.hip",
            "attn_groups.hip", "bwd.hip", "validate.cpp", "order.cpp"]
 
 
@@ -41,6 +41,7 @@ def _flags():
 # reductions (finite inputs), which lets the compiler drop the NaN-quieting
 # v_max x,x before every fmax
 EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"], "mask.hip": ["-fno-honor-nans"], "mask_screen.hip": ["-fno-honor-nans"], "group_mask.hip": ["-fno-honor-nans"],
+         "group_screen.hip": ["-fno-honor-nans"],
          "attn_groups.hip": ["-fno-honor-nans"]}
 
 

@@ -450,26 +450,39 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
   char* base = static_cast<char*>(ws);
   double* qp = reinterpret_cast<double*>(base + w.qp);
   double* kg = reinterpret_cast<double*>(base + w.kg);
-  double* z = reinterpret_cast<double*>(base + w.z);
-  double* partmax = reinterpret_cast<double*>(base + w.partmax);
+  float* zt = reinterpret_cast<float*>(base + w.zt);
   int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
+  int32_t* flags = reinterpret_cast<int32_t*>(base + w.flags);
+  int32_t* nflag = reinterpret_cast<int32_t*>(base + w.nflag);
+  ScreenOps ops{reinterpret_cast<_Float16*>(base + w.qs), reinterpret_cast<_Float16*>(base + w.ks),
+                reinterpret_cast<double*>(base + w.qmu),  reinterpret_cast<double2*>(base + w.krec),
+                reinterpret_cast<double*>(base + w.qn),   reinterpret_cast<int32_t*>(base + w.qe),
+                reinterpret_cast<uint64_t*>(base + w.hstat)};
+  const GroupRankBufs rb{reinterpret_cast<int32_t*>(base + w.cn), reinterpret_cast<double2*>(base + w.cab),
+                         reinterpret_cast<uint2*>(base + w.cjw)};
   const bool win = mp->win_t >= 0;
   // candidates: groups within lambda of the row's max logit (as in the block cut)
   const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)SG) - std::log(mp->thr) : 0.0;
   const int wt = win ? mp->win_t : -1, wh = win ? mp->win_h : -1, ww = win ? mp->win_w : -1;
-  // query-block means from the block pooling kernel (its key output lands in kg
-  // and is overwritten by the group means right after)
-  hipError_t e = launch_pool(g, q, k, qp, kg, stream);
-  if (e == hipSuccess) e = launch_pool_groups(g, k, kg, stream);
+  // query-block means and their screen operands, group means and theirs; then per
+  // chunk of heads the screened map and the cut; the exact ranking of the entries
+  // inside the cuts' margins, and the float64 cut of the rows the screen left
+  hipError_t e = launch_screen_init(g, ops, nflag, stream);
+  if (e == hipSuccess) e = launch_pool_queries_screen(g, q, qp, ops, stream);
+  if (e == hipSuccess) e = launch_pool_groups_screen(g, k, kg, ops, stream);
   const int64_t bh = (int64_t)g.B * g.nh;
   for (int64_t h0 = 0; h0 < bh && e == hipSuccess; h0 += w.chunk_heads) {
     const int64_t nh = std::min<int64_t>(w.chunk_heads, bh - h0);
-    e = launch_logits(g, qp, kg, z, (int)SG, h0, nh, stream, partmax);
+    if (mp->thr > 0.0) e = launch_group_logits_screen(g, ops, zt, h0, nh, w.pitch, stream);
     if (e == hipSuccess)
-      e = launch_group_select(g, z, h0 * g.S, nh * g.S, partmax, mp->thr, lambda, wt, wh, ww, bitmap, counts, w.words,
-                              stream);
+      e = launch_group_screen_select(g, zt, w.pitch, ops, qp, kg, h0 * g.S, nh * g.S, mp->thr, lambda, wt, wh, ww,
+                                     bitmap, counts, w.words, flags, nflag, rb, stream);
   }
+  if (e == hipSuccess && mp->thr > 0.0) e = launch_group_rank(g, rb, qp, kg, bitmap, counts, w.words, stream);
+  if (e == hipSuccess && mp->thr > 0.0)
+    e = launch_group_fallback(g, qp, kg, reinterpret_cast<double*>(base + w.zfb), mp->thr, lambda, wt, wh, ww, bitmap,
+                              counts, w.words, flags, nflag, stream);
   if (e == hipSuccess)
     e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
   if (e == hipSuccess) {

@@ -1,30 +1,24 @@
-// Key-group mask (AB-Attention page, news.hamidun.com/es/news/14960, "Los tres
-// recursos de AB-Attention", third resource: 4-token key/value blocks), selected
-// with the NABLA reduced map and CDF cut taken at group granularity (NABLA page,
-// gist.science/es/paper/2507.13546, Metodologia item 2, "Atencion Reducida" and
-// "Umbralizacion CDF"; item 3 for the window union).
+// Key-group mask, the float64 path (AB-Attention page, news.hamidun.com/es/news/14960,
+// "Los tres recursos de AB-Attention", third resource: 4-token key/value blocks),
+// cut with the NABLA reduced map and CDF cut taken at group granularity (NABLA
+// page, gist.science/es/paper/2507.13546, Metodologia item 2, "Atencion Reducida"
+// and "Umbralizacion CDF"; item 3 for the window union).
 //
-//   * pool_groups_kernel: float64 means of 4 consecutive fractal-order keys;
-//   * the logits reuse the float64 block-logit GEMM with L/4 key columns, run
-//     over a chunk of heads at a time so the workspace stays bounded;
-//   * group_select_kernel: the CDF cut of one row per 1024-thread workgroup.
-//     A row has L/4 entries (31 680 at 33 x 48 x 80 tokens), too many to hold
-//     in registers as the block select does, so the row is read once from the
-//     logits (the float32 offsets z - max into LDS, 4 B per entry; the row max
-//     comes from the maxima of its 64-column parts, written by the logit GEMM's
-//     epilogue) and every radix pass runs over LDS (the float32 exponential of an
-//     entry is only recomputed where its mass enters a histogram or the exact
-//     ranking; the keys are a subtraction and a scale).  The numerics are those of the
-//     block select: the ORDER is decided on the float64 logits, the masses are
-//     float32 exponentials in fixed point (2^-30 of the row max) summed exactly,
-//     the 24-bit monotone key is radix-selected 8 bits per pass until the
-//     crossing bin holds <= 256 entries, which are then ranked exactly on their
-//     float64 logits (ties by index); more than 256 entries with one 24-bit key
-//     fall back to passes over the exact 64-bit order keys, then index order.
+// The rows the screened cut (group_screen.hip) cannot decide are cut here from
+// float64 logits: group_fallback_kernel walks the list of such rows with a
+// persistent grid, computes each row's L/4 logits qp_i . kg_j / sqrt(D) into its
+// own float64 scratch row, and cuts it with select_row: the float32 offsets
+// z - max in LDS (4 B per entry), the masses float32 exponentials in fixed point
+// (2^-30 of the row max) summed exactly, the 24-bit monotone key radix-selected
+// 8 bits per pass until the crossing bin holds <= 256 entries, which are then
+// ranked exactly on their float64 logits (ties by index); more than 256 entries
+// with one 24-bit key fall back to passes over the exact 64-bit order keys, then
+// index order.
 #include <float.h>
 
 #include "kernels.h"
 #include "mask_util.h"
+#include "validate.h"
 
 namespace bsa {
 namespace gmask {
@@ -32,40 +26,7 @@ namespace gmask {
 constexpr int kMaxSG = 32768;     // groups per head the LDS row buffer holds
 constexpr int kNT = 1024;         // threads per row: the LDS row buffer allows one workgroup
 constexpr int kNW = kNT / 64;     // per CU, so the row gets 16 waves to hide its loads
-
-// float64 means of every 4 consecutive fractal-order rows of k -> kg [B*nh, L/4, D].
-// Thread = (group, 4 channels); the group's 4 rows are consecutive in memory.
-template <typename T>
-__global__ void __launch_bounds__(256) pool_groups_kernel(const T* __restrict__ k, double* __restrict__ kg, Geom g) {
-  const int per = g.D / 4;                          // threads per group
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t SG = g.L / 4;
-  const int64_t ngroups = (int64_t)g.B * g.nh * SG;
-  if (idx >= ngroups * per) return;
-  const int c = (int)(idx % per);
-  const int64_t gg = idx / per;
-  const int64_t bh = gg / SG;
-  const int gid = (int)(gg - bh * SG);
-  const int blk = gid / (g.N / 4), m0 = (gid % (g.N / 4)) * 4;
-  const T* src = k + ((size_t)bh * g.L + block_token_row(g, blk, m0)) * g.D + 4 * c;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float x;
-      if constexpr (sizeof(T) == 2) {
-        x = __uint_as_float((uint32_t)((const uint16_t*)src)[(size_t)t * g.D + d] << 16);
-      } else {
-        x = ((const float*)src)[(size_t)t * g.D + d];
-      }
-      acc[d] += (double)x;                          // sums of 4 bf16/f32 values are exact in float64
-    }
-  }
-  double* dst = kg + (size_t)gg * g.D + 4 * c;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) dst[d] = acc[d] * 0.25;
-}
+constexpr int kFallbackWGs = kGroupFallbackRows;   // persistent grid, one float64 scratch row each
 
 struct SelectSmem {
   float dv[kMaxSG];                   // (float)(z - max) of candidates, -inf otherwise
@@ -96,16 +57,14 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int d) {
   return __longlong_as_double((long long)shfl_xor_u64((unsigned long long)__double_as_longlong(v), d));
 }
 
-__global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restrict__ z,
-                                                           const double* __restrict__ partmax, int64_t row0, int SG,
-                                                           Geom g, double thr, double lambda, int win_t, int win_h,
-                                                           int win_w, uint32_t* __restrict__ bitmap,
-                                                           int32_t* __restrict__ counts, int words) {
-  __shared__ SelectSmem sm;
+// The cut of row r from its float64 logits zr (global memory, L/4 entries); m_part:
+// this thread's share of the row max.  Called by all kNT threads of the workgroup.
+__device__ __forceinline__ void select_row(const double* __restrict__ zr, double m_part, int64_t r, int SG,
+                                           const Geom& g, double thr, double lambda, int win_t, int win_h,
+                                           int win_w, uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts,
+                                           int words, SelectSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t r = row0 + blockIdx.x;
   const int i = (int)(r % g.S);
-  const double* zr = z + (int64_t)blockIdx.x * SG;
   const int gpb = g.N / 4;
   for (int x = tid; x < words; x += kNT) sm.bm[x] = 0u;
 
@@ -182,13 +141,9 @@ __global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restr
       sm.bm[x] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
     }
   } else {
-    // the row max from the maxima of its 64-column parts (the GEMM's epilogue);
     // one pass over the logits: candidates, masses, offsets into LDS (four loads
     // in flight per thread)
-    const int nparts = 2 * ((SG + 127) / 128);
-    double m = -DBL_MAX;
-    for (int x = tid; x < nparts; x += kNT) m = fmax(m, partmax[(size_t)blockIdx.x * nparts + x]);
-    m = max_f64(m);
+    const double m = max_f64(m_part);
     unsigned long long wsum = 0;
     float dmin = 0.f;
     for (int j0 = tid; j0 < SG; j0 += 4 * kNT) {
@@ -394,24 +349,53 @@ __global__ void __launch_bounds__(kNT) group_select_kernel(const double* __restr
   if (tid == 0) counts[r] = (int32_t)pc;
 }
 
-}  // namespace gmask
-
-hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStream_t s) {
-  const int64_t n = (int64_t)g.B * g.nh * (g.L / 4) * (g.D / 4);
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  if (g.dtype == 1)
-    gmask::pool_groups_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)k, kg, g);
-  else
-    gmask::pool_groups_kernel<float><<<grid, 256, 0, s>>>((const float*)k, kg, g);
-  return hipGetLastError();
+// Rows left by the screened cut: a persistent grid of kFallbackWGs workgroups, each
+// with its own float64 scratch row (zscr: kFallbackWGs * L/4 doubles).
+__global__ void __launch_bounds__(kNT) group_fallback_kernel(const double* __restrict__ qp,
+                                                             const double* __restrict__ kg, double* __restrict__ zscr,
+                                                             Geom g, double thr, double lambda, int win_t, int win_h,
+                                                             int win_w, uint32_t* __restrict__ bitmap,
+                                                             int32_t* __restrict__ counts, int words,
+                                                             const int32_t* __restrict__ flag_list,
+                                                             const int32_t* __restrict__ nflag, double inv_sqrt_d) {
+  __shared__ SelectSmem sm;
+  __shared__ double qrow[128];
+  const int SG = g.L / 4;
+  double* zr = zscr + (size_t)blockIdx.x * SG;
+  const int n = *nflag;
+  for (int x = blockIdx.x; x < n; x += gridDim.x) {
+    const int64_t r = flag_list[x];
+    const int64_t bh = r / g.S;
+    __syncthreads();                     // the previous row is done with qrow, zr and sm
+    if ((int)threadIdx.x < g.D) qrow[threadIdx.x] = qp[(size_t)r * g.D + threadIdx.x];
+    __syncthreads();
+    double m = -DBL_MAX;
+    for (int j = threadIdx.x; j < SG; j += kNT) {
+      const double2* kr = (const double2*)(kg + ((size_t)bh * SG + j) * g.D);
+      double z = 0.0;
+      for (int d = 0; d < g.D / 2; ++d) {
+        const double2 kv = kr[d];
+        z = fma(qrow[2 * d], kv.x, z);
+        z = fma(qrow[2 * d + 1], kv.y, z);
+      }
+      z *= inv_sqrt_d;
+      zr[j] = z;
+      m = fmax(m, z);
+    }
+    // (the row max's barriers make zr visible to the whole workgroup)
+    select_row(zr, m, r, SG, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, words, sm);
+  }
 }
 
-hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, const double* partmax,
-                               double thr,
-                               double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
-                               int words, hipStream_t s) {
-  gmask::group_select_kernel<<<(unsigned)nrows, gmask::kNT, 0, s>>>(z, partmax, row0, g.L / 4, g, thr, lambda, win_t,
-                                                                    win_h, win_w, bitmap, counts, words);
+}  // namespace gmask
+
+hipError_t launch_group_fallback(const Geom& g, const double* qp, const double* kg, double* zscr, double thr,
+                                 double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+                                 int words, const int32_t* flag_list, const int32_t* nflag, hipStream_t s) {
+  const double inv = 1.0 / sqrt((double)g.D);
+  gmask::group_fallback_kernel<<<gmask::kFallbackWGs, gmask::kNT, 0, s>>>(qp, kg, zscr, g, thr, lambda, win_t, win_h,
+                                                                          win_w, bitmap, counts, words, flag_list,
+                                                                          nflag, inv);
   return hipGetLastError();
 }
 

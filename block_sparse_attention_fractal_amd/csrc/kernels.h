@@ -37,6 +37,8 @@ hipError_t launch_screen_init(const Geom& g, const ScreenOps& ops, int32_t* nfla
 // launch_pool plus the screen operands in the same pass (after launch_screen_init).
 hipError_t launch_pool_screen(const Geom& g, const void* q, const void* k, double* qp, double* kp,
                               const ScreenOps& ops, hipStream_t s);
+// The query half of launch_pool_screen only (qp and the query screen operands).
+hipError_t launch_pool_queries_screen(const Geom& g, const void* q, double* qp, const ScreenOps& ops, hipStream_t s);
 // Screened reduced map + CDF cut + window union -> bitmap rows and counts; rows it
 // cannot decide are appended to flag_list (count in nflag) for the float64 path.
 hipError_t launch_screen_select(const Geom& g, const ScreenOps& ops, const double* qp, const double* kp, double thr,
@@ -99,20 +101,38 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s);
-// Logits of query-block means against Sk key columns (blocks or 4-token groups)
-// for heads h0 .. h0+nheads-1; z holds those heads' rows only.  partmax (or null):
-// per row of those heads, the largest logit of each 64-column part of the row
-// (2 * ceil(Sk / 128) values per row).
-hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
-                         int64_t nheads, hipStream_t s, double* partmax = nullptr);
-// 4-token key groups: float64 group means of k -> kg [B*nh, L/4, D].
-hipError_t launch_pool_groups(const Geom& g, const void* k, double* kg, hipStream_t s);
-// CDF cut + window union over the L/4 group logits of rows row0 .. row0+nrows-1
-// (z: those rows, L/4 entries each) -> bitmap rows and kept counts.
-// partmax: the rows' per-part maxima from launch_logits (2 * ceil(L/4 / 128) per row).
-hipError_t launch_group_select(const Geom& g, const double* z, int64_t row0, int64_t nrows, const double* partmax,
-                               double thr, double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
-                               int words, hipStream_t s);
+// 4-token key groups (group_screen.hip): float64 group means kg [B*nh, L/4, D] and
+// their screen operands (ops.ks in 16-group MFMA tiles, ops.krec (mean, exponent)
+// per group, ops.hstat per head; after launch_screen_init).
+hipError_t launch_pool_groups_screen(const Geom& g, const void* k, double* kg, const ScreenOps& ops, hipStream_t s);
+// Screened group map of heads h0 .. h0+nheads-1 as float32 offsets from each row's
+// upper bound: zt [nheads*S, pitch] (pitch: L/4 rounded up to a multiple of 32).
+hipError_t launch_group_logits_screen(const Geom& g, const ScreenOps& ops, float* zt, int64_t h0, int64_t nheads,
+                                      int pitch, hipStream_t s);
+// CDF cut + window union of rows row0 .. row0+nrows-1 from their screened offsets
+// (zt: those rows) -> bitmap rows and counts; rows it cannot decide are appended to
+// flag_list (count in nflag) for launch_group_fallback.
+// Per row: the number of entries the screened cut left inside its error margin
+// (cn), the mass above them and the target (cab), and the entries (cjw: up to 64
+// (group id, mass) pairs per row).
+struct GroupRankBufs {
+  int32_t* cn;
+  double2* cab;
+  uint2* cjw;
+};
+hipError_t launch_group_screen_select(const Geom& g, const float* zt, int pitch, const ScreenOps& ops,
+                                      const double* qp, const double* kg, int64_t row0, int64_t nrows, double thr,
+                                      double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap,
+                                      int32_t* counts, int words, int32_t* flag_list, int32_t* nflag,
+                                      const GroupRankBufs& rb, hipStream_t s);
+// Exact ranking of the entries the screened cut handed over (every row).
+hipError_t launch_group_rank(const Geom& g, const GroupRankBufs& rb, const double* qp, const double* kg,
+                             uint32_t* bitmap, int32_t* counts, int words, hipStream_t s);
+// The float64 cut of the listed rows (group_mask.hip); zscr: kGroupFallbackRows
+// rows of L/4 doubles.
+hipError_t launch_group_fallback(const Geom& g, const double* qp, const double* kg, double* zscr, double thr,
+                                 double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
+                                 int words, const int32_t* flag_list, const int32_t* nflag, hipStream_t s);
 int group_select_max_groups();
 // V -> [B*nh, L/4, D, 4] bf16 (each group channel-major) for the gathered attention.
 hipError_t launch_prep_vg(const Geom& g, const void* v, void* vg, hipStream_t s);

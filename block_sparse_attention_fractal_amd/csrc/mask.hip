@@ -25,16 +25,15 @@ namespace bsa {
 // (4 x 4 MFMA tiles); k chunks of 16 staged in LDS k-major (so the 16 lanes of a
 // fragment read 128 contiguous bytes), double-buffered: the next chunk is read
 // into registers while the current one is multiplied.
-// The same kernel serves the key-group map: Sk key columns per head (S for
-// blocks, L/4 for 4-token groups) and heads h0 .. h0 + gridDim.z - 1, with z
-// holding only those heads' rows.
+// Sk key columns per head and heads h0 .. h0 + gridDim.z - 1 (z holds only those
+// heads' rows).
 // ---------------------------------------------------------------------------
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ void __launch_bounds__(256, 2) block_logits_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
                                                            double* __restrict__ z, int Sq, int Sk, int64_t h0,
-                                                           double inv_sqrt_d, double* __restrict__ partmax) {
+                                                           double inv_sqrt_d) {
   constexpr int TM = 128, KC = 16;
   __shared__ __attribute__((aligned(16))) double As[2][KC][TM];
   __shared__ __attribute__((aligned(16))) double Bs[2][KC][TM];
@@ -98,39 +97,24 @@ __global__ void __launch_bounds__(256, 2) block_logits_kernel(const double* __re
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int gi = i0 + wr + 16 * m + 4 * r + fk;   // the same row for the 16 lanes of one fk
-      double vmax = -DBL_MAX;
+      const int gi = i0 + wr + 16 * m + 4 * r + fk;
+      if (gi >= Sq) continue;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int gj = j0 + wc + 16 * n + fi;
-        const double v = acc[m][n][r] * inv_sqrt_d;
-        if (gi < Sq && gj < Sk) {
-          zh[(size_t)gi * Sk + gj] = v;
-          vmax = fmax(vmax, v);
-        }
-      }
-      if (partmax) {   // the largest logit of this wave's 64 columns of the row
-        // reduced over the 16 lanes of the row with DPP moves inside the row
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const uint64_t b = (uint64_t)__double_as_longlong(vmax);
-          const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
-          vmax = fmax(vmax, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
-        }
-        if (fi == 0 && gi < Sq)
-          partmax[((size_t)blockIdx.z * Sq + gi) * (2 * gridDim.x) + 2 * blockIdx.x + (wave & 1)] = vmax;
+        if (gj < Sk) zh[(size_t)gi * Sk + gj] = acc[m][n][r] * inv_sqrt_d;
       }
     }
 }
 
-hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
-                         int64_t nheads, hipStream_t s, double* partmax) {
+static hipError_t launch_logits(const Geom& g, const double* qp, const double* kp, double* z, int Sk, int64_t h0,
+                                int64_t nheads, hipStream_t s) {
   dim3 grid((Sk + 127) / 128, (g.S + 127) / 128, (unsigned)nheads);
   const double inv = 1.0 / sqrt((double)g.D);
   if (g.D == 64)
-    block_logits_kernel<64><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv, partmax);
+    block_logits_kernel<64><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv);
   else
-    block_logits_kernel<128><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv, partmax);
+    block_logits_kernel<128><<<grid, 256, 0, s>>>(qp, kp, z, g.S, Sk, h0, inv);
   return hipGetLastError();
 }
 

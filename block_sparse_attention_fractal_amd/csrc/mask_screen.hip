@@ -57,36 +57,6 @@ __global__ void __launch_bounds__(256) screen_init_kernel(uint64_t* __restrict__
   if (x == 0) *nflag = 0;
 }
 
-// ---- wavefront helpers ------------------------------------------------------
-// value of lane - N inside each row of 16 lanes (0 where that is outside the row)
-template <int N>
-__device__ __forceinline__ uint64_t row_shr64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + N, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + N, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-// inclusive prefix sum over the 64 lanes (lane 0 first): shifts inside the rows of
-// 16 lanes, then the totals of the lower rows read back as scalars
-__device__ __forceinline__ uint64_t wave_prefix_u64(uint64_t v, int lane) {
-  v += row_shr64<1>(v);
-  v += row_shr64<2>(v);
-  v += row_shr64<4>(v);
-  v += row_shr64<8>(v);
-  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
-  const int row = lane >> 4;
-  return v + (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
-}
-// sum over each aligned group of 8 lanes (every lane of the group gets it)
-__device__ __forceinline__ double sum8(double v) {
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
-    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-  }
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // Screened map + cut.  grid = (ceil(S / ROWS), B * heads), 512 threads (8 waves,
 // two per SIMD).

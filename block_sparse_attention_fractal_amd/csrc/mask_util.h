@@ -77,6 +77,92 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// ---- pooling sums and lane reductions --------------------------------------
+// add_chunk: one 16-byte chunk of a token row (8 bf16 or 4 float32 values) added
+// into float64 sums (exact for bf16 and for sums of a few float32 values).
+template <typename T>
+__device__ __forceinline__ void add_chunk(double* acc, const uint4& c);
+
+template <>
+__device__ __forceinline__ void add_chunk<uint16_t>(double* acc, const uint4& c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+    acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void add_chunk<float>(double* acc, const uint4& c) {
+  acc[0] += (double)__uint_as_float(c.x);
+  acc[1] += (double)__uint_as_float(c.y);
+  acc[2] += (double)__uint_as_float(c.z);
+  acc[3] += (double)__uint_as_float(c.w);
+}
+
+// value of lane ^ 16 / lane ^ 32 (VALU lane swaps, no LDS round trip)
+__device__ __forceinline__ double xor16(double x, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  const uint32_t l = (lane & 16) ? lo[0] : lo[1], h = (lane & 16) ? hi[0] : hi[1];
+  return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+}
+__device__ __forceinline__ double xor32(double x, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  const uint32_t l = (lane & 32) ? lo[0] : lo[1], h = (lane & 32) ? hi[0] : hi[1];
+  return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+}
+
+// Reduction over the lanes of one row group (lane bits below log2(LPR)): DPP
+// steps inside 8 / 16 lanes, then the 16-lane swap.
+template <int LPR, typename Op>
+__device__ __forceinline__ double group_reduce(double v, int lane, Op op) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if (st == 3 && LPR == 8) break;
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
+    v = op(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+  }
+  if constexpr (LPR == 32) v = op(v, xor16(v, lane));
+  return v;
+}
+
+// ---- prefix sums and row sums over lanes ----------------------------------
+// value of lane - N inside each row of 16 lanes (0 where that is outside the row)
+template <int N>
+__device__ __forceinline__ uint64_t row_shr64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + N, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + N, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+// inclusive prefix sum over the 64 lanes (lane 0 first): shifts inside the rows of
+// 16 lanes, then the totals of the lower rows read back as scalars
+__device__ __forceinline__ uint64_t wave_prefix_u64(uint64_t v, int lane) {
+  v += row_shr64<1>(v);
+  v += row_shr64<2>(v);
+  v += row_shr64<4>(v);
+  v += row_shr64<8>(v);
+  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
+}
+// sum over each aligned group of 8 lanes (every lane of the group gets it)
+__device__ __forceinline__ double sum8(double v) {
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  return v;
+}
+
 // Sliding-tile window (NABLA page, Metodologia item 3): block ids are tiles
 // (t, y, x) of Hp x Wp patches per frame; ids i and j are within the window when
 // every coordinate differs by at most the given extent.

@@ -20,62 +20,9 @@
 
 namespace bsa {
 
-template <typename T>
-__device__ __forceinline__ void add_chunk(double* acc, const uint4& c);
-
-template <>
-__device__ __forceinline__ void add_chunk<uint16_t>(double* acc, const uint4& c) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-    acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void add_chunk<float>(double* acc, const uint4& c) {
-  acc[0] += (double)__uint_as_float(c.x);
-  acc[1] += (double)__uint_as_float(c.y);
-  acc[2] += (double)__uint_as_float(c.z);
-  acc[3] += (double)__uint_as_float(c.w);
-}
-
-// value of lane ^ 16 / lane ^ 32 (VALU lane swaps, no LDS round trip)
-__device__ __forceinline__ double xor16(double x, int lane) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
-  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
-  const uint32_t l = (lane & 16) ? lo[0] : lo[1], h = (lane & 16) ? hi[0] : hi[1];
-  return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
-}
-__device__ __forceinline__ double xor32(double x, int lane) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
-  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
-  const uint32_t l = (lane & 32) ? lo[0] : lo[1], h = (lane & 32) ? hi[0] : hi[1];
-  return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
-}
-
-// Reduction over the lanes of one row group (lane bits below log2(LPR)): DPP
-// steps inside 8 / 16 lanes, then the 16-lane swap.
-template <int LPR, typename Op>
-__device__ __forceinline__ double group_reduce(double v, int lane, Op op) {
-  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    if (st == 3 && LPR == 8) break;
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = dpp_step((uint32_t)b, st), hi = dpp_step((uint32_t)(b >> 32), st);
-    v = op(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
-  }
-  if constexpr (LPR == 32) v = op(v, xor16(v, lane));
-  return v;
-}
-
 constexpr int kPoolBlocks = 2;          // consecutive blocks per wavefront (150 VGPRs, three waves per SIMD)
 
-// grid = (ceil(S / (4 kPoolBlocks)), B * heads, 2): z = 0 pools Q, z = 1 pools K;
+// grid = (ceil(S / (4 kPoolBlocks)), B * heads, 2 or 1): z = 0 pools Q, z = 1 pools K;
 // wave w of workgroup x takes blocks (4x + w) kPoolBlocks + b of head y, with the
 // loads of block b + 1 in flight while block b is summed and written.
 template <typename T, int D, bool kScreen>
@@ -257,8 +204,9 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
 
 template <bool kScreen>
 static hipError_t launch_pool_impl(const Geom& g, const void* q, const void* k, double* qp, double* kp,
-                                   const ScreenOps& ops, hipStream_t s) {
-  dim3 grid((unsigned)((g.S + 4 * kPoolBlocks - 1) / (4 * kPoolBlocks)), (unsigned)((int64_t)g.B * g.nh), 2);
+                                   const ScreenOps& ops, hipStream_t s, bool queries_only = false) {
+  dim3 grid((unsigned)((g.S + 4 * kPoolBlocks - 1) / (4 * kPoolBlocks)), (unsigned)((int64_t)g.B * g.nh),
+            queries_only ? 1u : 2u);
   if (g.dtype == 1 && g.D == 64)
     pool_kernel<uint16_t, 64, kScreen><<<grid, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, qp, kp, ops, g);
   else if (g.dtype == 1)
@@ -277,6 +225,10 @@ hipError_t launch_pool(const Geom& g, const void* q, const void* k, double* qp, 
 hipError_t launch_pool_screen(const Geom& g, const void* q, const void* k, double* qp, double* kp,
                               const ScreenOps& ops, hipStream_t s) {
   return launch_pool_impl<true>(g, q, k, qp, kp, ops, s);
+}
+
+hipError_t launch_pool_queries_screen(const Geom& g, const void* q, double* qp, const ScreenOps& ops, hipStream_t s) {
+  return launch_pool_impl<true>(g, q, q, qp, nullptr, ops, s, true);
 }
 
 }  // namespace bsa

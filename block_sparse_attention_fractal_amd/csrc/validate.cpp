@@ -146,15 +146,28 @@ GrpMaskWs grp_mask_ws_layout(const Geom& g) {
   GrpMaskWs w{};
   const int64_t SG = g.L / BSA_KEY_GROUP;
   const int64_t bh = (int64_t)g.B * g.nh;
-  const int64_t per_head = (int64_t)g.S * SG * 8;          // one head's group logits
-  const int64_t budget = int64_t(1) << 31;                 // logits of at most ~2 GiB at a time
+  w.pitch = (int32_t)((SG + 31) / 32 * 32);
+  const int64_t per_head = (int64_t)g.S * w.pitch * 4;      // one head's screened group logits
+  const int64_t budget = int64_t(1) << 31;                  // at most ~2 GiB of them at a time
   w.chunk_heads = std::max<int64_t>(1, std::min<int64_t>(bh, budget / per_head));
   w.words = (int32_t)((SG + 31) / 32);
   int64_t off = 0;
   w.qp = off; off = align256(off + g.rows * g.D * 8);
   w.kg = off; off = align256(off + bh * SG * g.D * 8);
-  w.z = off; off = align256(off + w.chunk_heads * per_head);
-  w.partmax = off; off = align256(off + w.chunk_heads * g.S * 2 * ((SG + 127) / 128) * 8);   // per 64-column part
+  w.zt = off; off = align256(off + w.chunk_heads * per_head);
+  w.qs = off; off = align256(off + g.rows * 2 * g.D * 2);
+  w.ks = off; off = align256(off + bh * ((SG + 15) / 16) * 16 * 2 * g.D * 2);   // whole 16-group tiles
+  w.qmu = off; off = align256(off + g.rows * 8);
+  w.krec = off; off = align256(off + bh * SG * 16);
+  w.qn = off; off = align256(off + g.rows * 8);
+  w.qe = off; off = align256(off + g.rows * 4);
+  w.hstat = off; off = align256(off + bh * 3 * 8);
+  w.flags = off; off = align256(off + g.rows * 4);
+  w.nflag = off; off = align256(off + 4);
+  w.zfb = off; off = align256(off + (int64_t)kGroupFallbackRows * SG * 8);
+  w.cn = off; off = align256(off + g.rows * 4);
+  w.cab = off; off = align256(off + g.rows * 16);
+  w.cjw = off; off = align256(off + g.rows * 64 * 8);
   w.counts = off; off = align256(off + g.rows * 4);
   w.bitmap = off; off = align256(off + g.rows * (int64_t)w.words * 4);
   w.chunk_sums = off; off = align256(off + ((g.rows + 1023) / 1024) * 4);

@@ -26,9 +26,14 @@ struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work cou
   int64_t delta, counter, bounds, cost, order_q, order_k, tcounts, tchunks, tbitmap, tcolptr, trowidx, total;
   int32_t words;
 };
-struct GrpMaskWs {     // key-group mask: query-block means, group means, a head chunk of logits and their rows' part maxima, bits
-  int64_t qp, kg, z, partmax, counts, bitmap, chunk_sums, total;
+// Workgroups of the key-group mask's float64 path, each with one float64 scratch row.
+constexpr int kGroupFallbackRows = 256;
+struct GrpMaskWs {     // key-group mask: query-block and group means, the screen operands, a head chunk of
+                       // screened logits, the rows left to the float64 path and its scratch rows, bits
+  int64_t qp, kg, zt, qs, ks, qmu, krec, qn, qe, hstat, flags, nflag, zfb, cn, cab, cjw, counts, bitmap,
+      chunk_sums, total;
   int64_t chunk_heads;  // heads whose group logits are computed together
+  int32_t pitch;        // floats per screened row (L/4 rounded up to 32)
   int32_t words;        // 32-bit words per bitmap row (L/4 bits)
 };
 struct GrpFwdWs {      // work counters and XCD bounds, per-row cost and order (bf16), prepared V (bf16)

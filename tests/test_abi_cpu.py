@@ -258,14 +258,22 @@ def test_query_group_sizes(lib, B, nh, T, H, W):
     S, SG = L // 64, L // 4
     rows = B * nh * S
     assert max_nnz == rows * SG
-    # workspace: query-block means, group means, a chunk of heads of group logits
-    # (as many heads as fit 2 GiB, at least one) and their rows' maxima per 64-column part, counts,
-    # bitmap, scan chunk sums
+    # workspace: query-block and group means, a chunk of heads of screened group
+    # logits (float32 rows of L/4 rounded up to 32 entries, as many heads as fit
+    # 2 GiB, at least one), the screen operands (query fp16 hi/lo, whole 16-group
+    # tiles of group fp16 hi/lo, query means, group (mean, exponent), query norms
+    # and exponents, per-head statistics), the rows left to the float64 path and
+    # their count, 256 float64 scratch rows of that path, the entries handed to the
+    # exact ranking (count, (mass above, target), 64 (id, mass) pairs per row),
+    # counts, bitmap, scan chunk sums
     a = lambda x: (x + 255) // 256 * 256
-    per_head = S * SG * 8
+    pitch = (SG + 31) // 32 * 32
+    per_head = S * pitch * 4
     chunk = max(1, min(B * nh, (1 << 31) // per_head))
-    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(chunk * S * 2 * ((SG + 127) // 128) * 8) + a(rows * 4)
-                   + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
+    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(rows * 2 * D * 2)
+                   + a(B * nh * ((SG + 15) // 16) * 16 * 2 * D * 2) + a(rows * 8) + a(B * nh * SG * 16)
+                   + a(rows * 8) + a(rows * 4) + a(B * nh * 3 * 8) + a(rows * 4) + a(4) + a(256 * SG * 8)
+                   + a(rows * 4) + a(rows * 16) + a(rows * 64 * 8) + a(rows * 4) + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
     assert fws == 256 + 2 * a(rows * 4) + a(B * nh * L * D * 2)
     aws = ctypes.c_int64()
     assert lib.bsa_query_attend_groups_ws(ctypes.byref(P(B, nh, T, H, W, D)), 4, ctypes.byref(aws)) == 0

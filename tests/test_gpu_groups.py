@@ -84,6 +84,50 @@ def test_group_mask_and_attention_match_oracle(name):
           f"max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
+def _group_mask_vs_oracle(cfg, inputs):
+    g = grid_of(cfg)
+    q, k = (to_device(inputs, n, cfg.dtype) for n in "qk")
+    mask = bsa.build_group_mask(q, k, g, cfg.thr, cfg.window)
+    torch.cuda.synchronize()
+    rp = mask.row_ptr.cpu().numpy().astype(np.int64)
+    ci = mask.col_idx[: int(rp[-1])].cpu().numpy()
+    ref = groups.build_group_mask(inputs["q"], inputs["k"], cfg.T, cfg.H, cfg.W, cfg.patch, 64, G, cfg.thr,
+                                  cfg.window, details=True)
+    return rp, compare_masks(rp, ci, ref, cfg.thr, cfg.L // G)
+
+
+def _with_bf16(inputs, name, x):
+    from workloads import bf16_bits_to_f32, bf16_round
+    bits = bf16_round(x)
+    inputs[name + "_bits"], inputs[name] = bits, bf16_bits_to_f32(bits)
+
+
+@pytest.mark.parametrize("frames", [4, 2], ids=["every-row-float64", "half-the-rows-float64"])
+def test_group_mask_rows_beyond_the_screen(frames):
+    """Queries of the first `frames` frames scaled by 96: the screened group logits of
+    their rows cannot be trusted to the band, so those rows are cut from float64
+    logits; the CSR must match the oracle's, alone and mixed with screened rows."""
+    cfg = small(T=4, H=24, W=40, thr=0.1, window=(1, 1, 1), amp=0.0, seed=52)
+    inputs = make_inputs(cfg)
+    x = inputs["q"].copy()
+    x[:, :, : frames * cfg.H * cfg.W] *= 96.0
+    _with_bf16(inputs, "q", x)
+    rp, (n_mis, n_band) = _group_mask_vs_oracle(cfg, inputs)
+    print(f"groups, frames scaled {frames}: nnz={rp[-1]} mismatches={n_mis} band={n_band}")
+
+
+def test_group_mask_exact_ties():
+    """Every key equal: all group logits of a row tie, the screen's margin holds the
+    whole row (more entries than it ranks exactly), so every row goes to the float64
+    path, which keeps the lowest group indices first."""
+    cfg = small(nh=2, T=2, H=16, W=32, thr=0.3, seed=53)
+    inputs = make_inputs(cfg)
+    _with_bf16(inputs, "k", np.repeat(inputs["k"][:, :, :1], cfg.L, axis=2))
+    rp, (n_mis, n_band) = _group_mask_vs_oracle(cfg, inputs)
+    assert n_mis == 0
+    print(f"groups, all keys equal: nnz={rp[-1]} of {cfg.rows * cfg.L // G}")
+
+
 def test_thr_zero_keeps_every_group_and_is_dense():
     cfg = small(nh=1, T=2, H=16, W=32, thr=0.0, seed=15)
     inputs = make_inputs(cfg)
