@@ -449,7 +449,6 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
   if (!aligned(ws, 256)) return fail(BSA_ERR_WORKSPACE, "bsa_build_group_mask: workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
   double* qp = reinterpret_cast<double*>(base + w.qp);
-  double* kg = reinterpret_cast<double*>(base + w.kg);
   float* zt = reinterpret_cast<float*>(base + w.zt);
   int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
@@ -465,24 +464,25 @@ int bsa_build_group_mask(const bsa_problem* p, int group, const bsa_mask_params*
   // candidates: groups within lambda of the row's max logit (as in the block cut)
   const double lambda = mp->thr > 0.0 ? 40.0 + std::log((double)SG) - std::log(mp->thr) : 0.0;
   const int wt = win ? mp->win_t : -1, wh = win ? mp->win_h : -1, ww = win ? mp->win_w : -1;
-  // query-block means and their screen operands, group means and theirs; then per
+  // query-block means and their screen operands, the groups' operands; then per
   // chunk of heads the screened map and the cut; the exact ranking of the entries
   // inside the cuts' margins, and the float64 cut of the rows the screen left
   hipError_t e = launch_screen_init(g, ops, nflag, stream);
   if (e == hipSuccess) e = launch_pool_queries_screen(g, q, qp, ops, stream);
-  if (e == hipSuccess) e = launch_pool_groups_screen(g, k, kg, ops, stream);
+  if (e == hipSuccess) e = launch_pool_groups_screen(g, k, ops, stream);
   const int64_t bh = (int64_t)g.B * g.nh;
   for (int64_t h0 = 0; h0 < bh && e == hipSuccess; h0 += w.chunk_heads) {
     const int64_t nh = std::min<int64_t>(w.chunk_heads, bh - h0);
     if (mp->thr > 0.0) e = launch_group_logits_screen(g, ops, zt, h0, nh, w.pitch, stream);
     if (e == hipSuccess)
-      e = launch_group_screen_select(g, zt, w.pitch, ops, qp, kg, h0 * g.S, nh * g.S, mp->thr, lambda, wt, wh, ww,
-                                     bitmap, counts, w.words, flags, nflag, rb, stream);
+      e = launch_group_screen_select(g, zt, w.pitch, ops, h0 * g.S, nh * g.S, mp->thr, wt, wh, ww, bitmap, w.words,
+                                     flags, nflag, rb, stream);
   }
-  if (e == hipSuccess && mp->thr > 0.0) e = launch_group_rank(g, rb, qp, kg, bitmap, counts, w.words, stream);
+  if (e == hipSuccess && mp->thr > 0.0) e = launch_group_rank(g, rb, qp, k, bitmap, w.words, stream);
   if (e == hipSuccess && mp->thr > 0.0)
-    e = launch_group_fallback(g, qp, kg, reinterpret_cast<double*>(base + w.zfb), mp->thr, lambda, wt, wh, ww, bitmap,
+    e = launch_group_fallback(g, qp, k, reinterpret_cast<double*>(base + w.zfb), mp->thr, lambda, wt, wh, ww, bitmap,
                               counts, w.words, flags, nflag, stream);
+  if (e == hipSuccess) e = launch_bitmap_counts(bitmap, w.words, g.rows, counts, stream);
   if (e == hipSuccess)
     e = launch_scan(g, counts, out->row_ptr, reinterpret_cast<int32_t*>(base + w.chunk_sums), out->nnz, stream);
   if (e == hipSuccess) {

@@ -6,8 +6,8 @@
 //
 // The rows the screened cut (group_screen.hip) cannot decide are cut here from
 // float64 logits: group_fallback_kernel walks the list of such rows with a
-// persistent grid, computes each row's L/4 logits qp_i . kg_j / sqrt(D) into its
-// own float64 scratch row, and cuts it with select_row: the float32 offsets
+// persistent grid, computes each row's L/4 logits qp_i . kg_j / sqrt(D) (kg_j the
+// float64 mean of group j's 4 keys) into its own float64 scratch row, and cuts it with select_row: the float32 offsets
 // z - max in LDS (4 B per entry), the masses float32 exponentials in fixed point
 // (2^-30 of the row max) summed exactly, the 24-bit monotone key radix-selected
 // 8 bits per pass until the crossing bin holds <= 256 entries, which are then
@@ -350,11 +350,13 @@ __device__ __forceinline__ void select_row(const double* __restrict__ zr, double
 }
 
 // Rows left by the screened cut: a persistent grid of kFallbackWGs workgroups, each
-// with its own float64 scratch row (zscr: kFallbackWGs * L/4 doubles).
-__global__ void __launch_bounds__(kNT) group_fallback_kernel(const double* __restrict__ qp,
-                                                             const double* __restrict__ kg, double* __restrict__ zscr,
-                                                             Geom g, double thr, double lambda, int win_t, int win_h,
-                                                             int win_w, uint32_t* __restrict__ bitmap,
+// with its own float64 scratch row (zscr: kFallbackWGs * L/4 doubles); the group
+// means are formed from the 4 keys of each group (exact, as in the oracle).
+template <typename T>
+__global__ void __launch_bounds__(kNT) group_fallback_kernel(const double* __restrict__ qp, const T* __restrict__ k,
+                                                             double* __restrict__ zscr, Geom g, double thr,
+                                                             double lambda, int win_t, int win_h, int win_w,
+                                                             uint32_t* __restrict__ bitmap,
                                                              int32_t* __restrict__ counts, int words,
                                                              const int32_t* __restrict__ flag_list,
                                                              const int32_t* __restrict__ nflag, double inv_sqrt_d) {
@@ -371,12 +373,12 @@ __global__ void __launch_bounds__(kNT) group_fallback_kernel(const double* __res
     __syncthreads();
     double m = -DBL_MAX;
     for (int j = threadIdx.x; j < SG; j += kNT) {
-      const double2* kr = (const double2*)(kg + ((size_t)bh * SG + j) * g.D);
       double z = 0.0;
-      for (int d = 0; d < g.D / 2; ++d) {
-        const double2 kv = kr[d];
-        z = fma(qrow[2 * d], kv.x, z);
-        z = fma(qrow[2 * d + 1], kv.y, z);
+      for (int c0 = 0; c0 < g.D; c0 += 8) {
+        double mk[8];
+        group_mean<T, 8>(k, g, bh, j, c0, mk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z = fma(qrow[c0 + e], mk[e], z);
       }
       z *= inv_sqrt_d;
       zr[j] = z;
@@ -389,13 +391,16 @@ __global__ void __launch_bounds__(kNT) group_fallback_kernel(const double* __res
 
 }  // namespace gmask
 
-hipError_t launch_group_fallback(const Geom& g, const double* qp, const double* kg, double* zscr, double thr,
+hipError_t launch_group_fallback(const Geom& g, const double* qp, const void* k, double* zscr, double thr,
                                  double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
                                  int words, const int32_t* flag_list, const int32_t* nflag, hipStream_t s) {
   const double inv = 1.0 / sqrt((double)g.D);
-  gmask::group_fallback_kernel<<<gmask::kFallbackWGs, gmask::kNT, 0, s>>>(qp, kg, zscr, g, thr, lambda, win_t, win_h,
-                                                                          win_w, bitmap, counts, words, flag_list,
-                                                                          nflag, inv);
+  if (g.dtype == 1)
+    gmask::group_fallback_kernel<uint16_t><<<gmask::kFallbackWGs, gmask::kNT, 0, s>>>(
+        qp, (const uint16_t*)k, zscr, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, words, flag_list, nflag, inv);
+  else
+    gmask::group_fallback_kernel<float><<<gmask::kFallbackWGs, gmask::kNT, 0, s>>>(
+        qp, (const float*)k, zscr, g, thr, lambda, win_t, win_h, win_w, bitmap, counts, words, flag_list, nflag, inv);
   return hipGetLastError();
 }
 

@@ -17,14 +17,16 @@
 // channels and the cross products hi*lo + lo*hi go to three float32 accumulators:
 // with at most 64 additions per accumulator (D = 128) the float32 sums are within
 // 2^-17 of the sum of |products|, the split and the dropped lo*lo term add
-// 3 * 2^-22, so every screened logit of row i is within
-//   eps_i = 1.125 * 2^-17 |c_i| max_j |e_j| / sqrt(D)
+// 3 * 2^-22 and the float32 epilogue (the accumulators summed, scaled and added to
+// the rank-one part minus the row's bound) 2^-22, so every screened logit of row i
+// is within
+//   eps_i = 1.1875 * 2^-17 |c_i| max_j |e_j| / sqrt(D)
 // of the exact one (four times tighter than the single-accumulator bound of the
 // block screen: the group means average 4 tokens instead of 64, so their centred
-// norms are about 4 times larger).
+// norms are about 4 times larger), and the stored float32 offset v adds 2^-22 |v|.
 //
-//   * pool_groups_screen_kernel: float64 means of the 4 keys of every group (kept
-//     for the exact recomputation) and their screen operands, in MFMA tile order;
+//   * pool_groups_screen_kernel: the screen operands of every group (from the
+//     float64 means of its 4 keys), in MFMA tile order;
 //   * group_logits_screen_kernel: the screened map of a chunk of heads as float32
 //     offsets z - ub_i (ub_i an upper bound of the row's largest logit), written
 //     to HBM (4 bytes per entry instead of 8);
@@ -38,8 +40,9 @@
 //     guarantee, or with more than 64 entries inside it, are listed for the exact
 //     float64 path (group_mask.hip);
 //   * group_rank_kernel: the handed-over entries get their exact float64 logits
-//     and are ranked exactly, one wavefront per row with many rows in flight (so
-//     the loads of the group means do not stall a whole workgroup).
+//     (group means formed again from the 4 keys) and are ranked exactly, one
+//     wavefront per row with many rows in flight (so their loads do not stall a
+//     whole workgroup).
 #include <float.h>
 
 #include <algorithm>
@@ -52,9 +55,10 @@ namespace gscr {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr double kScreenErr = 0x1.2p-17;   // relative error of the screened centred dot product
+constexpr double kScreenErr = 0x1.3p-17;   // relative error of the screened centred dot product
 constexpr float kTrust = 4e-5f;            // largest offset error (logit units) a screened row may carry
 constexpr int kNT = 1024;                  // select: threads per row
 constexpr int kNW = kNT / 64;
@@ -64,86 +68,98 @@ constexpr int kRowsWG = 128;               // map: query blocks per workgroup (3
 constexpr int kStep = 64;                  // map: key groups per LDS stage (4 tiles of 16)
 
 // ---------------------------------------------------------------------------
-// Group means and screen operands.  grid = (ceil(L/4 / (4 GPW)), B * heads),
-// 256 threads; LPG lanes per group (a 16-byte chunk of each of its 4 token rows
-// per lane), GPW groups per wave.
+// Screen operands of the key groups.  grid = (ceil(L/4 / 64), B * heads), 256
+// threads: wave w takes the 16 groups of tile 4 x + w, lane l the group l % 16 and
+// its 8-channel chunks l / 16 + 4 u (u < D / 32), so that each fp16 store of a
+// wave fills 1 KB of the tile layout (16-group tiles, per 32-channel step u and
+// half (hi, lo) 1 KB holding, at lane slot 16 (chunk % 4) + group % 16, the 8
+// channels that lane of v_mfma_f32_16x16x32_f16 takes).  The group means are not
+// stored: the exact recomputations form them again from the 4 keys.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(256) pool_groups_screen_kernel(const T* __restrict__ k, double* __restrict__ kg,
-                                                                 ScreenOps ops, Geom g) {
-  constexpr int EPC = 16 / sizeof(T);        // elements per 16-byte chunk
-  constexpr int LPG = D / EPC;               // lanes per group
-  constexpr int GPW = 64 / LPG;              // groups per wave
+__global__ void __launch_bounds__(256) pool_groups_screen_kernel(const T* __restrict__ k, ScreenOps ops, Geom g) {
+  constexpr int KS = D / 32;
+  constexpr int EPC = 16 / sizeof(T);        // elements per 16-byte load
+  constexpr int NLD = 8 / EPC;               // loads per 8-channel chunk
   __shared__ uint64_t red[3][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t bh = blockIdx.y;
   const int SG = g.L / 4, ntg = (SG + 15) / 16, gpb = g.N / 4;
-  const int gid = (blockIdx.x * 4 + wave) * GPW + lane / LPG;
-  const int c = lane % LPG;
+  const int tile = blockIdx.x * 4 + wave;
+  const int g16 = lane & 15, cq = lane >> 4;
+  const int gid = tile * 16 + g16;
   const bool ok = gid < SG;
   const int gq = min(gid, SG - 1);
   const int blk = gq / gpb, m0 = (gq % gpb) * 4;
-  uint4 raw[4];
+  uint4 raw[4][KS][NLD];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const T* src = k + ((size_t)bh * g.L + block_token_row(g, blk, m0 + t)) * D;
+#pragma unroll
+    for (int u = 0; u < KS; ++u)
+#pragma unroll
+      for (int x = 0; x < NLD; ++x) raw[t][u][x] = *(const uint4*)(src + 8 * (cq + 4 * u) + x * EPC);
+  }
+  double acc[KS][8];
+#pragma unroll
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    raw[t] = *(const uint4*)(k + ((size_t)bh * g.L + block_token_row(g, blk, m0 + t)) * D + c * EPC);
-  double acc[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+    for (int u = 0; u < KS; ++u)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) add_chunk<T>(acc, raw[t]);
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] *= 0.25;          // sums of 4 inputs are exact in float64
-  if (ok) {
-    double2* dst = (double2*)(kg + ((size_t)bh * SG + gid) * D + c * EPC);
-#pragma unroll
-    for (int x = 0; x < EPC / 2; ++x) dst[x] = make_double2(acc[2 * x], acc[2 * x + 1]);
-  }
+      for (int x = 0; x < NLD; ++x) add_chunk<T>(&acc[u][x * EPC], raw[t][u][x]);
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) s += acc[e];
-  const double mu = group_reduce<LPG>(s, lane, [](double a, double b) { return a + b; }) * (1.0 / D);
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[u][e] *= 0.25;                                   // sums of 4 inputs are exact in float64
+      s += acc[u][e];
+    }
+  s += xor16(s, lane);                                     // the group's 4 lanes: l, l ^ 16, l ^ 32, l ^ 48
+  s += xor32(s, lane);
+  const double mu = s * (1.0 / D);
   double amax = 0.0, n2 = 0.0;
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) {
-    acc[e] -= mu;
-    amax = fmax(amax, fabs(acc[e]));
-    n2 = fma(acc[e], acc[e], n2);
-  }
-  amax = group_reduce<LPG>(amax, lane, [](double a, double b) { return fmax(a, b); });
-  n2 = group_reduce<LPG>(n2, lane, [](double a, double b) { return a + b; });
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[u][e] -= mu;
+      amax = fmax(amax, fabs(acc[u][e]));
+      n2 = fma(acc[u][e], acc[u][e], n2);
+    }
+  amax = fmax(amax, xor16(amax, lane));
+  amax = fmax(amax, xor32(amax, lane));
+  n2 += xor16(n2, lane);
+  n2 += xor32(n2, lane);
   const int ex = amax > 0.0 ? 13 - ilogb(amax) : 0;     // scaled magnitudes in [2^13, 2^14)
   if (ok) {
-    _Float16 hv[EPC], lv[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      // double -> float -> fp16 on the hardware converts (the opaque copies keep the
-      // compiler from fusing them into a software double -> fp16 rounding)
-      const double x = ldexp(acc[e], ex);
-      float xf = (float)x;
-      asm volatile("" : "+v"(xf));
-      const _Float16 hi = (_Float16)xf;
-      float rf = (float)(x - (double)hi);
-      asm volatile("" : "+v"(rf));
-      hv[e] = hi;
-      lv[e] = (_Float16)rf;
-    }
-    // 16-group tiles, per 32-channel step s and half (hi, lo) 1 KB holding, at lane
-    // slot 16 (channel / 8 % 4) + group % 16, the 8 channels that lane of
-    // v_mfma_f32_16x16x32_f16 takes
-    const int ch0 = c * EPC, cc = ch0 >> 3, st = cc >> 2, kq = cc & 3;
-    _Float16* dst = ops.ks + (((size_t)(bh * ntg + gid / 16) * (D / 32) + st) * 2) * 512 +
-                    (16 * kq + (gid & 15)) * 8 + (ch0 & 7);
-    if constexpr (EPC == 8) {
+    for (int u = 0; u < KS; ++u) {
+      _Float16 hv[8], lv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // double -> float -> fp16 on the hardware converts (the opaque copies keep the
+        // compiler from fusing them into a software double -> fp16 rounding)
+        const double x = ldexp(acc[u][e], ex);
+        float xf = (float)x;
+        asm volatile("" : "+v"(xf));
+        const _Float16 hi = (_Float16)xf;
+        float rf = (float)(x - (double)hi);
+        asm volatile("" : "+v"(rf));
+        hv[e] = hi;
+        lv[e] = (_Float16)rf;
+      }
+      _Float16* dst = ops.ks + (((size_t)(bh * ntg + tile) * KS + u) * 2) * 512 + (16 * cq + g16) * 8;
       *(uint4*)dst = *(const uint4*)hv;
       *(uint4*)(dst + 512) = *(const uint4*)lv;
-    } else {
-      *(uint2*)dst = *(const uint2*)hv;
-      *(uint2*)(dst + 512) = *(const uint2*)lv;
     }
   }
   const double nrm = sqrt(n2) * (1.0 + 0x1p-50);          // rounded up: an upper bound of |e|
-  if (ok && c == 0) ops.krec[(size_t)bh * SG + gid] = make_double2(mu, (double)ex);
+  if (ok && cq == 0) ops.krec[(size_t)bh * SG + gid] = make_double2(mu, (double)ex);
   uint64_t st_max = ok ? order_key(mu) : 0ull, st_min = ok ? order_key(mu) : ~0ull, st_n = ok ? order_key(nrm) : 0ull;
   st_max = wave_reduce(st_max, lane, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
   st_min = wave_reduce(st_min, lane, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
@@ -169,9 +185,10 @@ __global__ void __launch_bounds__(256) pool_groups_screen_kernel(const T* __rest
 }
 
 // the row constants of the screen: a = D mu_i, the upper bound ub_i of the row's
-// logits and the error bound eps_i (identical expressions in both kernels)
+// logits times sqrt(D) and the error bound eps_i (identical expressions in both
+// kernels)
 struct RowScreen {
-  double a, ub, eps;
+  double a, u, eps;
 };
 __device__ __forceinline__ RowScreen row_screen(const ScreenOps& ops, int64_t r, int64_t bh, int D, double inv_sqrt_d) {
   const double a = (double)D * ops.qmu[r];
@@ -180,18 +197,18 @@ __device__ __forceinline__ RowScreen row_screen(const ScreenOps& ops, int64_t r,
   const double nq = ops.qn[r];
   RowScreen rs;
   rs.a = a;
-  rs.ub = (a * (a >= 0.0 ? bmax : bmin) + nq * cmax) * inv_sqrt_d;
+  rs.u = a * (a >= 0.0 ? bmax : bmin) + nq * cmax;
   rs.eps = kScreenErr * nq * cmax * inv_sqrt_d;
   return rs;
 }
 
 // ---------------------------------------------------------------------------
 // Screened map of heads h0 .. h0 + gridDim.z - 1: zt[(h - h0) S + i][j] =
-// float(z~_ij - ub_i), row pitch `pitch` floats.  grid = (column slices,
+// (z~_ij - ub_i) log2(e) in float32 (log2 units), row pitch `pitch` floats.  grid = (column slices,
 // ceil(S / 128), heads), 256 threads.  Wave w holds the A operands (hi, lo) of
 // query blocks i0 + 32 w .. + 31 in registers; the workgroup streams its slice
-// of key groups through LDS 64 at a time (the next stage's 16-byte chunks in
-// registers while the current one is multiplied).  MFMA layouts as in
+// of key groups through LDS 64 at a time, by direct-to-LDS buffer loads into two
+// stage buffers (the next stage in flight while the current one is multiplied).  MFMA layouts as in
 // mask_screen.hip: A[i][k] in lane 16 (k / 8) + i, B[k][j] in lane 16 (k / 8) + j,
 // C[i][j] in lane 16 (i / 4) + j, register i % 4.
 // ---------------------------------------------------------------------------
@@ -200,29 +217,31 @@ __global__ void __launch_bounds__(256, 2) group_logits_screen_kernel(ScreenOps o
                                                                      int64_t h0, int steps_per_slice, int pitch,
                                                                      double inv_sqrt_d) {
   constexpr int KS = D / 32;                 // k-steps of 32 channels
-  constexpr int kTileH = KS * 1024;          // halfs per 16-group tile (hi and lo)
-  constexpr int kChunks = 4 * kTileH * 2 / (256 * 16);   // 16-byte chunks per thread per stage
-  static_assert(kChunks * 256 * 16 == 4 * kTileH * 2, "stage shape");
-  __shared__ __attribute__((aligned(16))) _Float16 bs[4 * kTileH];
-  __shared__ double2 recs[kStep];            // (nu_j, exponent) of the stage's groups
-  __shared__ double rc_a[kRowsWG], rc_ub[kRowsWG];
-  __shared__ int rc_e[kRowsWG];
+  constexpr int kTileB = KS * 2048;          // bytes per 16-group tile (hi and lo)
+  constexpr int kStageB = 4 * kTileB;        // bytes per stage (4 tiles)
+  constexpr int kLoads = kStageB / (4 * 1024);   // 1 KB direct-to-LDS loads per wave per stage
+  static_assert(kLoads * 4 * 1024 == kStageB, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint8_t bs[2][kStageB];   // two stages: the one in use, the next
+  __shared__ __attribute__((aligned(16))) double2 recs[2][kStep];  // (nu_j, exponent) of the stage's groups
+  __shared__ double rc_a[kRowsWG], rc_u[kRowsWG];
+  __shared__ float rc_s[kRowsWG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.S, SG = g.L / 4, ntg = (SG + 15) / 16;
   const int64_t bh = h0 + blockIdx.z;
   const int i0 = blockIdx.y * kRowsWG;
   const int64_t rbase = bh * S;
+  const float sc = (float)(inv_sqrt_d * 1.4426950408889634);   // offsets in log2 units
   if (tid < kRowsWG) {
     const int i = i0 + tid;
     if (i < S) {
       const RowScreen rs = row_screen(ops, rbase + i, bh, D, inv_sqrt_d);
       rc_a[tid] = rs.a;
-      rc_ub[tid] = rs.ub;
-      rc_e[tid] = ops.qe[rbase + i];
+      rc_u[tid] = rs.u;
+      rc_s[tid] = ldexpf(sc, -ops.qe[rbase + i]);          // undoes the row's scaling, then log2(e)/sqrt(D)
     } else {
       rc_a[tid] = 0.0;
-      rc_ub[tid] = 0.0;
-      rc_e[tid] = 0;
+      rc_u[tid] = 0.0;
+      rc_s[tid] = 0.f;
     }
   }
   f16x8 ah[2][KS], al[2][KS];
@@ -238,92 +257,118 @@ __global__ void __launch_bounds__(256, 2) group_logits_screen_kernel(ScreenOps o
   }
   const int nsteps = (SG + kStep - 1) / kStep;
   const int st0 = blockIdx.x * steps_per_slice, st1 = min(st0 + steps_per_slice, nsteps);
-  const _Float16* kh = ops.ks + (size_t)bh * ntg * kTileH;
-  u32x4 stg[kChunks];
-  double2 srec;
-  auto fetch = [&](int st) __attribute__((always_inline)) {
+  // the head's group operands and (mean, exponent) pairs behind buffer resources:
+  // reads past the end (the last stage's missing tiles) return zeros
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(ops.ks + (size_t)bh * ntg * (kTileB / 2)), (short)0, ntg * kTileB,
+                                        0x00020000);
+  const __amdgpu_buffer_rsrc_t rrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(ops.krec + (size_t)bh * SG), (short)0, SG * 16, 0x00020000);
+  // this head's rows of the map: a store whose offset is past the end (rows >= S,
+  // groups >= L/4) is dropped by the hardware, so every lane stores on every tile and
+  // each stage issues the same number of stores
+  const int zbytes = S * pitch * 4;                        // < 2^31 (S <= 4096, pitch <= 32768)
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zt + (size_t)blockIdx.z * S * (size_t)pitch), (short)0, zbytes, 0x00020000);
+  // stage st into LDS buffer st & 1: kLoads 1 KB loads per wave (wave 0 also the
+  // stage's 64 (mean, exponent) pairs)
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const int buf = st & 1;
 #pragma unroll
-    for (int x = 0; x < kChunks; ++x) {
-      const int idx = x * 256 + tid;                       // 16-byte chunk of the stage
-      const int tin = idx / (kTileH / 8), off = idx % (kTileH / 8);
-      const int t = min(4 * st + tin, ntg - 1);            // past the end: the last tile (unused)
-      stg[x] = *(const u32x4*)(kh + (size_t)t * kTileH + off * 8);
-    }
-    if (tid < kStep) srec = ops.krec[(size_t)bh * SG + min(st * kStep + tid, SG - 1)];
+    for (int u = 0; u < kLoads; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&bs[buf][(wave * kLoads + u) * 1024]), 16,
+                                               lane * 16 + (wave * kLoads + u) * 1024, st * kStageB, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void*)(&recs[buf][0]), 16, lane * 16, st * kStep * 16, 0, 0);
   };
-  if (st0 < st1) fetch(st0);
-  __syncthreads();                                         // the row constants
-  double ra[2][4], rub[2][4];
-  int re[2][4];
+  if (st0 < st1) issue(st0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): the A operands and the first stage
+  __syncthreads();                                         // ... in every wave, and the row constants
+  // the transposed product C^T[g][q] = sum_k E[g][k] Q[q][k] (group operands in the A
+  // position): lane l holds query row l % 16 of a row tile and the 4 consecutive
+  // groups 4 (l / 16) .. + 3 of a tile, i.e. 16 contiguous bytes of a map row
+  double ra[2], ru[2];
+  float rsc[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int rho = 32 * wave + 16 * rt + 4 * (lane >> 4) + x;
-      ra[rt][x] = rc_a[rho];
-      rub[rt][x] = rc_ub[rho];
-      re[rt][x] = rc_e[rho];
-    }
-  float* zh = zt + (size_t)blockIdx.z * S * (size_t)pitch;
-  const int jl = lane & 15;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int rho = 32 * wave + 16 * rt + (lane & 15);
+    ra[rt] = rc_a[rho];
+    ru[rt] = rc_u[rho];
+    rsc[rt] = rc_s[rho];
+  }
+  const int gq = 4 * (lane >> 4);                          // this lane's first group of a tile
   for (int st = st0; st < st1; ++st) {
-#pragma unroll
-    for (int x = 0; x < kChunks; ++x) *(u32x4*)(bs + (x * 256 + tid) * 8) = stg[x];
-    if (tid < kStep) recs[tid] = srec;
-    __syncthreads();
-    if (st + 1 < st1) fetch(st + 1);
+    const int buf = st & 1;
+    if (st + 1 < st1) issue(st + 1);                       // into the buffer read two stages ago
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j0 = (4 * st + u) * 16;
-      if (j0 >= SG) break;
-      const int j = j0 + jl;
-      const double2 rec = recs[16 * u + jl];
+      const int j = (4 * st + u) * 16 + gq;
+      const _Float16* tb = (const _Float16*)&bs[buf][u * kTileB];
       f16x8 bhi[KS], blo[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        bhi[s] = *(const f16x8*)(bs + u * kTileH + s * 1024 + 8 * lane);
-        blo[s] = *(const f16x8*)(bs + u * kTileH + s * 1024 + 512 + 8 * lane);
+        bhi[s] = *(const f16x8*)(tb + s * 1024 + 8 * lane);
+        blo[s] = *(const f16x8*)(tb + s * 1024 + 512 + 8 * lane);
+      }
+      double2 rec[4];
+      float csc[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        rec[x] = recs[buf][16 * u + gq + x];
+        csc[x] = ldexpf(1.f, -(int)rec[x].y);             // undoes the group's scaling
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, px = p0;
+        // hi*hi of the two channel halves, and the two cross products, each its own
+        // accumulator (short dependency chains)
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, pa = p0, pb = p0;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           if (s < KS / 2)
-            p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][s], bhi[s], p0, 0, 0, 0);
+            p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bhi[s], ah[rt][s], p0, 0, 0, 0);
           else
-            p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][s], bhi[s], p1, 0, 0, 0);
-          px = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][s], blo[s], px, 0, 0, 0);
-          px = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt][s], bhi[s], px, 0, 0, 0);
+            p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bhi[s], ah[rt][s], p1, 0, 0, 0);
+          pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(blo[s], ah[rt][s], pa, 0, 0, 0);
+          pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(bhi[s], al[rt][s], pb, 0, 0, 0);
         }
-        if (j < SG) {
-          const int ek = (int)rec.y;
+        const int i = i0 + 32 * wave + 16 * rt + (lane & 15);
+        f32x4 v;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int i = i0 + 32 * wave + 16 * rt + 4 * (lane >> 4) + x;
-            if (i < S) {
-              const double dot = ((double)p0[x] + (double)p1[x]) + (double)px[x];
-              const double z = fma(ra[rt][x], rec.x, ldexp(dot, -(re[rt][x] + ek)));
-              zh[(size_t)i * pitch + j] = (float)fma(z, inv_sqrt_d, -rub[rt][x]);
-            }
-          }
+        for (int x = 0; x < 4; ++x) {
+          // (a nu_j - sqrt(D) ub_i) in float64, then everything in float32
+          const float dot = (p0[x] + p1[x]) + (pa[x] + pb[x]);
+          const float rk = (float)fma(ra[rt], rec[x].x, -ru[rt]);
+          v[x] = fmaf(dot, rsc[rt] * csc[x], rk * sc);
         }
+        // groups j .. j + 3 of row i (past L/4 they land in the row's padding, which the
+        // pitch leaves up to a multiple of 32); rows >= S and groups >= L/4: dropped
+        const int off = (i < S && j < SG) ? (i * pitch + j) * 4 : zbytes;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), zrs, off, 0, 0);
       }
     }
-    __syncthreads();                                       // the stage is consumed
+    // this wave's loads of the next stage have landed once at most the 8 stores issued
+    // after them (4 tiles x 2 row tiles) are outstanding; the barrier then publishes
+    // every wave's loads and frees this stage's buffer (the compiler's own barrier
+    // would wait for the stores as well)
+    static_assert(4 * 2 == 8, "stores per stage counted by the wait");
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
 // ---------------------------------------------------------------------------
-// The cut of rows row0 .. row0 + gridDim.x - 1 (zt: those rows, pitch floats
-// apart).  Thread t holds entries 32 t .. 32 t + 31 of the row.
+// The cut of rows row0 .. row0 + gridDim.x - 1 (zt: those rows, pitch floats apart,
+// offsets in log2 units), one 1024-thread workgroup per row.  Thread t holds
+// entries 32 t .. 32 t + 31 of the row in registers, so its bits are one bitmap
+// word; the row's count is taken from the bitmap afterwards.
 // ---------------------------------------------------------------------------
+constexpr int kHist = kNW / 2;             // radix histograms: one per pair of waves
+
 struct SelSmem {
-  uint64_t hist[kNW][256];            // per wave: (count << 44) | mass, top bin first
+  uint64_t hist[kHist][256];          // per wave pair: (count << 44) | mass, top bin first
   uint32_t bm[kNT];                   // the row's bitmap words
   uint32_t cj[kMaxCand], cw[kMaxCand];   // entries inside the margin: index, mass
   uint64_t red_u[kNW];
-  float red_f[kNW];
+  float red_f[kNW], red_g[kNW];
   uint64_t scan[4];
   uint64_t found_above;
   int found_bin;
@@ -331,9 +376,8 @@ struct SelSmem {
 };
 
 __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
-    const float* __restrict__ zt, int pitch, ScreenOps ops, const double* __restrict__ qp,
-    const double* __restrict__ kg, int64_t row0, Geom g, double thr, double lambda, int win_t, int win_h, int win_w,
-    uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts, int words, int32_t* __restrict__ flag_list,
+    const float* __restrict__ zt, int pitch, ScreenOps ops, int64_t row0, Geom g, double thr, int win_t, int win_h,
+    int win_w, uint32_t* __restrict__ bitmap, int words, int32_t* __restrict__ flag_list,
     int32_t* __restrict__ nflag, int32_t* __restrict__ cn, double2* __restrict__ cab, uint2* __restrict__ cjw,
     double inv_sqrt_d) {
   __shared__ SelSmem sm;
@@ -346,6 +390,7 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
   int nv = SG - jb;
   asm volatile("" : "+v"(nv));   // opaque: no per-entry lane masks hoisted and kept live
   constexpr uint64_t kMassMask = (1ull << 44) - 1;
+  constexpr float kLog2e = 1.44269504088896341f;
   auto u64add = [](uint64_t a, uint64_t b) { return a + b; };
   auto bsum = [&](uint64_t v) {
     v = wave_reduce(v, lane, u64add);
@@ -356,92 +401,84 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
     __syncthreads();
     return t;
   };
-  auto bmin_f = [&](float v) {
-    v = wave_reduce(v, lane, [](float a, float b) { return fminf(a, b); });
-    if (lane == 0) sm.red_f[wv] = v;
-    __syncthreads();
-    float t = sm.red_f[0];
-    for (int x = 1; x < kNW; ++x) t = fminf(t, sm.red_f[x]);
-    __syncthreads();
-    return t;
-  };
-  auto bmax_f = [&](float v) {
-    v = wave_reduce(v, lane, [](float a, float b) { return fmaxf(a, b); });
-    if (lane == 0) sm.red_f[wv] = v;
-    __syncthreads();
-    float t = sm.red_f[0];
-    for (int x = 1; x < kNW; ++x) t = fmaxf(t, sm.red_f[x]);
-    __syncthreads();
-    return t;
-  };
 
   uint32_t bits = 0;                                       // bit k: entry jb + k is kept
   uint32_t nrank = 0;                                      // entries left to group_rank_kernel
   if (thr == 0.0) {
     bits = nv >= 32 ? 0xffffffffu : (nv > 0 ? (1u << nv) - 1u : 0u);
   } else {
+    const double nq = ops.qn[r];                           // the screen bound's inputs, early
+    const uint64_t cm = ops.hstat[3 * bh + 2];
     float v[kPer];
     if (nv > 0) {
       const float4* src = (const float4*)(zt + (size_t)blockIdx.x * pitch + jb);   // pitch: a multiple of 32
 #pragma unroll
       for (int m = 0; m < kPer / 4; ++m) {
-        const float4 x = src[m];
-        v[4 * m] = x.x;
-        v[4 * m + 1] = x.y;
-        v[4 * m + 2] = x.z;
-        v[4 * m + 3] = x.w;
+        const float4 q = src[m];
+        v[4 * m] = q.x;
+        v[4 * m + 1] = q.y;
+        v[4 * m + 2] = q.z;
+        v[4 * m + 3] = q.w;
       }
     }
-    float mt = -FLT_MAX;
+    float mt = -FLT_MAX, mn = FLT_MAX;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      v[k] = k < nv ? v[k] : -FLT_MAX;
+      const bool ok = k < nv;
+      v[k] = ok ? v[k] : -FLT_MAX;
       mt = fmaxf(mt, v[k]);
+      mn = fminf(mn, ok ? v[k] : FLT_MAX);
     }
     if (tid == 0) sm.ncand = 0u;
-    mt = bmax_f(mt);
-    // error of the offsets d = v - mt against the exact z - max: the screen (twice)
-    // plus the float32 roundings of v and of d (|d| <= 30 ln 2 for an entry with mass)
-    const double eps_i = row_screen(ops, r, bh, g.D, inv_sqrt_d).eps;
-    const float eps_d = (float)(2.0 * eps_i) + 0x1p-23f * (fabsf(mt) + 22.f);
-    if (!(eps_d <= kTrust)) {                              // uniform: the float64 path owns this row
+    ((uint4*)&sm.hist[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);   // kHist * 256 words of 8 bytes
+    static_assert(kHist * 256 * 8 == kNT * 16, "one 16-byte clear per thread");
+    mt = wave_reduce(mt, lane, [](float a, float b) { return fmaxf(a, b); });
+    mn = wave_reduce(mn, lane, [](float a, float b) { return fminf(a, b); });
+    if (lane == 0) {
+      sm.red_f[wv] = mt;
+      sm.red_g[wv] = mn;
+    }
+    __syncthreads();
+    for (int y = 0; y < kNW; ++y) {
+      mt = fmaxf(mt, sm.red_f[y]);
+      mn = fminf(mn, sm.red_g[y]);
+    }
+    // error of the offsets d = v - mt (log2 units) against the exact ones: the screen
+    // (twice), 2^-22 |v| from the map's float32 epilogue for v and for mt, and the
+    // rounding of d (|d| <= 30 for an entry with mass, |v| <= |mt| + |d|)
+    const double eps_i = kScreenErr * nq * key_to_double(cm) * inv_sqrt_d;   // as in row_screen
+    const float eps_d = (float)(2.0 * (double)kLog2e * eps_i) + 0x1p-21f * (fabsf(mt) + 19.f);
+    if (!(eps_d <= kTrust * kLog2e)) {                     // uniform: the float64 path owns this row
       if (tid == 0) {
         flag_list[atomicAdd(nflag, 1)] = (int32_t)r;
         cn[r] = 0;
       }
       return;
     }
+    // masses in fixed point, 2^30 at the row max: exp2(d + 30), 0 below d = -30
+    const float mref = mt - 30.f;
+    const float vlo = fmaxf(mn, mref);                     // at or below every entry with mass
+    const float tscale = mt > vlo ? 16777215.0f / (mt - vlo) : 0.f;
     uint32_t w[kPer], t[kPer];
     uint64_t wsum = 0;
-    float dmin = 0.f;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const float d = v[k] - mt;
-      const float e = d >= (float)-lambda ? __builtin_amdgcn_exp2f(d * 1.44269504088896341f) : 0.f;
-      w[k] = (uint32_t)(e * 1073741824.0f);                // e <= 1: at most 2^30, exact
+      w[k] = (uint32_t)__builtin_amdgcn_exp2f(v[k] - mref);
       wsum += w[k];
-      dmin = fminf(dmin, w[k] != 0u ? d : 0.f);
-      v[k] = d;
+      // entries without mass get key 2^31: no radix prefix matches it, it is negative
+      // as an int and above every margin unsigned
+      t[k] = w[k] != 0u ? (uint32_t)fminf((v[k] - vlo) * tscale, 16777215.0f) : 0x80000000u;
     }
     const uint64_t total = bsum(wsum);
-    dmin = bmin_f(dmin);
-    const float tscale = dmin < 0.f ? 16777215.0f / (-dmin) : 0.f;
-    // entries without mass get key 2^31: no radix prefix matches it, it is negative
-    // as an int and above every margin unsigned
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      t[k] = w[k] != 0u ? (uint32_t)fminf((v[k] - dmin) * tscale, 16777215.0f) : 0x80000000u;
     const double target = (1.0 - thr) * (double)total;     // keep while the mass before < target
 
-    // one radix pass: (count, mass) histogram of bin(k) >= 0 per wave, summed over
-    // the waves by threads 0..255 (thread x: bin 255 - x), a prefix over the bins
-    // from the top, and the bin in which the mass reaches the target
+    // one radix pass: (count, mass) histogram of bin(k) >= 0 per wave pair, summed over
+    // the pairs by threads 0..255 (thread y: bin 255 - y), a prefix over the bins from
+    // the top, and the bin in which the mass reaches the target; the histograms are
+    // cleared for the next pass once they have been read
     auto crossing = [&](auto bin, uint64_t above_in, int& b_out, uint64_t& above_out, uint32_t& cnt_out)
                         __attribute__((always_inline)) {
-      uint64_t* hw = sm.hist[wv];
-      *(uint4*)(hw + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-      *(uint4*)(hw + 4 * lane + 2) = make_uint4(0u, 0u, 0u, 0u);
-      __builtin_amdgcn_wave_barrier();
+      uint64_t* hw = sm.hist[wv >> 1];
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const int b = bin(k);
@@ -454,8 +491,8 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
       uint32_t cb = 0;
       if (tid < 256) {
 #pragma unroll
-        for (int x = 0; x < kNW; ++x) {
-          const uint64_t h = sm.hist[x][tid];
+        for (int y = 0; y < kHist; ++y) {
+          const uint64_t h = sm.hist[y][tid];
           mb += h & kMassMask;
           cb += (uint32_t)(h >> 44);
         }
@@ -465,7 +502,7 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
       if (wv < 4 && lane == 63) sm.scan[wv] = incl;
       __syncthreads();
       if (tid < 256) {
-        for (int x = 0; x < wv; ++x) incl += sm.scan[x];
+        for (int y = 0; y < wv; ++y) incl += sm.scan[y];
         const uint64_t excl = incl - mb;
         if (cb != 0u && (double)(above_in + excl) < target && target <= (double)(above_in + incl)) {
           sm.found_bin = 255 - tid;
@@ -473,6 +510,7 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
           sm.found_cnt = cb;
         }
       }
+      ((uint4*)&sm.hist[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);   // for the next pass
       __syncthreads();
       b_out = sm.found_bin;
       above_out = sm.found_above;
@@ -504,30 +542,38 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
     }
     if (!reach) {
 #pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        if ((int)t[k] >= 0) bits |= 1u << k;
+      for (int k = 0; k < kPer; ++k) bits |= ((int)t[k] >= 0 ? 1u : 0u) << k;
     } else {
       // the crossing bin widened by the error margin in key units; entries above it
-      // are kept, those inside it ranked exactly, those below dropped
+      // are kept, those inside it handed to group_rank_kernel, those below dropped
       const uint32_t mt_keys = (uint32_t)fminf(ceilf(2.f * eps_d * tscale), 16777215.0f) + 1u;
       const uint32_t lo_t = tpre << tsh, hi_t = lo_t + ((1u << tsh) - 1u);
       const uint32_t lo_m = lo_t > mt_keys ? lo_t - mt_keys : 0u;
       const uint32_t hi_m = hi_t + mt_keys;                // < 2^25: no wrap
       uint64_t sure = 0;
+      uint32_t inm = 0;                                    // bit k: register k inside the margin
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        if ((int)t[k] > (int)hi_m) {
-          bits |= 1u << k;
-          sure += w[k];
-        } else if (t[k] >= lo_m && t[k] <= hi_m) {
-          const uint32_t slot = atomicAdd(&sm.ncand, 1u);
-          if (slot < (uint32_t)kMaxCand) {
-            sm.cj[slot] = (uint32_t)(jb + k);
-            sm.cw[slot] = w[k];
+        const bool up = (int)t[k] > (int)hi_m;
+        bits |= (up ? 1u : 0u) << k;
+        sure += up ? w[k] : 0u;
+        inm |= (t[k] >= lo_m && t[k] <= hi_m ? 1u : 0u) << k;
+      }
+      // the few entries inside the margin (a handful per row): only the waves holding
+      // one take the per-register path
+      if (__builtin_amdgcn_ballot_w64(inm != 0u) != 0ull) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          if ((inm >> k) & 1u) {
+            const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+            if (slot < (uint32_t)kMaxCand) {
+              sm.cj[slot] = (uint32_t)(jb + k);
+              sm.cw[slot] = w[k];
+            }
           }
         }
       }
-      above = bsum(sure);                                  // (its barriers also publish the candidates)
+      above = bsum(sure);                                  // (its barriers also publish the entries)
       const uint32_t ncand = sm.ncand;
       if (ncand > (uint32_t)kMaxCand) {                    // uniform: the float64 path owns this row
         if (tid == 0) {
@@ -543,8 +589,8 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
       nrank = ncand;
     }
   }
-  // the bitmap row: this thread's word, then the window on top (every group of
-  // every window block)
+  // the bitmap row: this thread's word, then the window on top (every group of every
+  // window block)
   if (tid == 0) cn[r] = (int32_t)nrank;
   sm.bm[tid] = bits;
   __syncthreads();
@@ -560,47 +606,57 @@ __global__ void __launch_bounds__(kNT) group_screen_select_kernel(
     });
   }
   __syncthreads();
-  uint64_t pc = 0;
-  if (tid < words) {
-    const uint32_t x = sm.bm[tid];
-    bitmap[r * words + tid] = x;
-    pc = (uint64_t)__popc(x);
-  }
-  pc = bsum(pc);
-  if (tid == 0) counts[r] = (int32_t)pc;
+  if (tid < words) bitmap[r * words + tid] = sm.bm[tid];
+}
+
+// Kept counts of rows from their bitmap rows (after the screened cut, the exact
+// ranking and the float64 path): one wavefront per row.
+__global__ void __launch_bounds__(256) bitmap_count_kernel(const uint32_t* __restrict__ bitmap, int words,
+                                                           int64_t rows, int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;                                   // whole wavefronts
+  uint32_t c = 0;
+  for (int x = lane; x < words; x += 64) c += __popc(bitmap[r * words + x]);
+  c = wave_reduce(c, lane, [](uint32_t a, uint32_t b) { return a + b; });
+  if (lane == 0) counts[r] = (int32_t)c;
 }
 
 // The entries a screened cut left inside its margin, ranked on their exact float64
 // logits (logit descending, index ascending): one wavefront per row, eight lanes per
 // entry (each D / 8 channels), eight entries per pass; the kept ones are added to
-// the row's bits and count.
+// the row's bits.
+template <typename T, int D>
 __global__ void __launch_bounds__(256) group_rank_kernel(const int32_t* __restrict__ cn, const double2* __restrict__ cab,
                                                          const uint2* __restrict__ cjw, const double* __restrict__ qp,
-                                                         const double* __restrict__ kg, Geom g, int64_t rows,
-                                                         uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts,
-                                                         int words, double inv_sqrt_d) {
+                                                         const T* __restrict__ k, Geom g, int64_t rows,
+                                                         uint32_t* __restrict__ bitmap, int words, double inv_sqrt_d) {
+  constexpr int per = D / 8;                 // channels per lane
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;                                   // whole wavefronts
   const uint32_t ncand = (uint32_t)cn[r];
   if (ncand == 0u) return;
-  const int SG = g.L / 4, D = g.D, per = D / 8;
   const int64_t bh = r / g.S;
   const int sub = lane & 7, slot = lane >> 3;
   const bool have = (uint32_t)lane < ncand;
   const uint2 mine_jw = cjw[r * kMaxCand + min((uint32_t)lane, ncand - 1u)];
-  const double* qrow = qp + (size_t)r * D + sub * per;
+  double qv[per];
+#pragma unroll
+  for (int e = 0; e < per; e += 2) {
+    const double2 x = *(const double2*)(qp + (size_t)r * D + sub * per + e);
+    qv[e] = x.x;
+    qv[e + 1] = x.y;
+  }
   double z = 0.0;
   for (int p = 0; p < (int)((ncand + 7u) / 8u); ++p) {
     const uint32_t cidx = min(8u * (uint32_t)p + (uint32_t)slot, ncand - 1u);
-    const uint32_t cj = (uint32_t)__shfl((int)mine_jw.x, (int)cidx, 64);
-    const double* krow = kg + ((size_t)bh * SG + cj) * D + sub * per;
+    const int cj = __shfl((int)mine_jw.x, (int)cidx, 64);
+    double mk[per];
+    group_mean<T, per>(k, g, bh, cj, sub * per, mk);
     double part = 0.0;
-    for (int e = 0; e < per; e += 2) {
-      const double2 qv = *(const double2*)(qrow + e), kv = *(const double2*)(krow + e);
-      part = fma(qv.x, kv.x, part);
-      part = fma(qv.y, kv.y, part);
-    }
+#pragma unroll
+    for (int e = 0; e < per; ++e) part = fma(qv[e], mk[e], part);
     part = sum8(part);
     const double got = __shfl(part, 8 * (lane & 7), 64);   // entry 8 p + lane % 8 -> lane
     if ((lane >> 3) == p) z = got;
@@ -615,29 +671,22 @@ __global__ void __launch_bounds__(256) group_rank_kernel(const int32_t* __restri
     if (ky > my_key || (ky == my_key && jy < my_j)) before += wy;
   }
   const double2 at = cab[r];                               // (mass above the margin, target)
-  if (have && at.x + (double)before < at.y) {
-    const uint32_t bit = 1u << (my_j & 31);
-    const uint32_t old = atomicOr(&bitmap[r * words + (my_j >> 5)], bit);
-    if (!(old & bit)) atomicAdd(&counts[r], 1);            // not already kept by the window
-  }
+  if (have && at.x + (double)before < at.y) atomicOr(&bitmap[r * words + (my_j >> 5)], 1u << (my_j & 31));
 }
 
 }  // namespace gscr
 
-hipError_t launch_pool_groups_screen(const Geom& g, const void* k, double* kg, const ScreenOps& ops, hipStream_t s) {
-  const int SG = g.L / 4;
-  const unsigned heads = (unsigned)((int64_t)g.B * g.nh);
-#define BSA_PGS(T_, D_)                                                                                   \
-  do {                                                                                                    \
-    constexpr int gpw = 64 / (D_ / (16 / (int)sizeof(T_)));                                               \
-    gscr::pool_groups_screen_kernel<T_, D_><<<dim3((unsigned)((SG + 4 * gpw - 1) / (4 * gpw)), heads), 256, 0, \
-                                              s>>>((const T_*)k, kg, ops, g);                              \
-  } while (0)
-  if (g.dtype == 1 && g.D == 64) BSA_PGS(uint16_t, 64);
-  else if (g.dtype == 1) BSA_PGS(uint16_t, 128);
-  else if (g.D == 64) BSA_PGS(float, 64);
-  else BSA_PGS(float, 128);
-#undef BSA_PGS
+hipError_t launch_pool_groups_screen(const Geom& g, const void* k, const ScreenOps& ops, hipStream_t s) {
+  const int ntg = (g.L / 4 + 15) / 16;
+  const dim3 grid((unsigned)((ntg + 3) / 4), (unsigned)((int64_t)g.B * g.nh));
+  if (g.dtype == 1 && g.D == 64)
+    gscr::pool_groups_screen_kernel<uint16_t, 64><<<grid, 256, 0, s>>>((const uint16_t*)k, ops, g);
+  else if (g.dtype == 1)
+    gscr::pool_groups_screen_kernel<uint16_t, 128><<<grid, 256, 0, s>>>((const uint16_t*)k, ops, g);
+  else if (g.D == 64)
+    gscr::pool_groups_screen_kernel<float, 64><<<grid, 256, 0, s>>>((const float*)k, ops, g);
+  else
+    gscr::pool_groups_screen_kernel<float, 128><<<grid, 256, 0, s>>>((const float*)k, ops, g);
   return hipGetLastError();
 }
 
@@ -659,23 +708,34 @@ hipError_t launch_group_logits_screen(const Geom& g, const ScreenOps& ops, float
   return hipGetLastError();
 }
 
-hipError_t launch_group_screen_select(const Geom& g, const float* zt, int pitch, const ScreenOps& ops,
-                                      const double* qp, const double* kg, int64_t row0, int64_t nrows, double thr,
-                                      double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap,
-                                      int32_t* counts, int words, int32_t* flag_list, int32_t* nflag,
-                                      const GroupRankBufs& rb, hipStream_t s) {
+hipError_t launch_group_screen_select(const Geom& g, const float* zt, int pitch, const ScreenOps& ops, int64_t row0,
+                                      int64_t nrows, double thr, int win_t, int win_h, int win_w, uint32_t* bitmap,
+                                      int words, int32_t* flag_list, int32_t* nflag, const GroupRankBufs& rb,
+                                      hipStream_t s) {
   const double inv = 1.0 / sqrt((double)g.D);
-  gscr::group_screen_select_kernel<<<(unsigned)nrows, gscr::kNT, 0, s>>>(zt, pitch, ops, qp, kg, row0, g, thr, lambda,
-                                                                         win_t, win_h, win_w, bitmap, counts, words,
-                                                                         flag_list, nflag, rb.cn, rb.cab, rb.cjw, inv);
+  gscr::group_screen_select_kernel<<<(unsigned)nrows, gscr::kNT, 0, s>>>(zt, pitch, ops, row0, g, thr, win_t, win_h,
+                                                                         win_w, bitmap, words, flag_list, nflag, rb.cn,
+                                                                         rb.cab, rb.cjw, inv);
   return hipGetLastError();
 }
 
-hipError_t launch_group_rank(const Geom& g, const GroupRankBufs& rb, const double* qp, const double* kg,
-                             uint32_t* bitmap, int32_t* counts, int words, hipStream_t s) {
+hipError_t launch_group_rank(const Geom& g, const GroupRankBufs& rb, const double* qp, const void* k,
+                             uint32_t* bitmap, int words, hipStream_t s) {
   const double inv = 1.0 / sqrt((double)g.D);
-  gscr::group_rank_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, s>>>(rb.cn, rb.cab, rb.cjw, qp, kg, g, g.rows, bitmap,
-                                                                       counts, words, inv);
+  const unsigned grid = (unsigned)((g.rows + 3) / 4);
+#define BSA_RANK(T_, D_)                                                                                        \
+  gscr::group_rank_kernel<T_, D_><<<grid, 256, 0, s>>>(rb.cn, rb.cab, rb.cjw, qp, (const T_*)k, g, g.rows, bitmap, \
+                                                       words, inv)
+  if (g.dtype == 1 && g.D == 64) BSA_RANK(uint16_t, 64);
+  else if (g.dtype == 1) BSA_RANK(uint16_t, 128);
+  else if (g.D == 64) BSA_RANK(float, 64);
+  else BSA_RANK(float, 128);
+#undef BSA_RANK
+  return hipGetLastError();
+}
+
+hipError_t launch_bitmap_counts(const uint32_t* bitmap, int words, int64_t rows, int32_t* counts, hipStream_t s) {
+  gscr::bitmap_count_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, words, rows, counts);
   return hipGetLastError();
 }
 

@@ -101,17 +101,18 @@ hipError_t launch_backward(const Geom& g, const void* q, const void* k, const vo
                            void* dv, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* tcolptr,
                            const int32_t* trowidx, int32_t* counters, int32_t* cost, int32_t* order_q,
                            int32_t* order_k, int32_t* bounds, int num_cu, bool delta_walk, hipStream_t s);
-// 4-token key groups (group_screen.hip): float64 group means kg [B*nh, L/4, D] and
-// their screen operands (ops.ks in 16-group MFMA tiles, ops.krec (mean, exponent)
-// per group, ops.hstat per head; after launch_screen_init).
-hipError_t launch_pool_groups_screen(const Geom& g, const void* k, double* kg, const ScreenOps& ops, hipStream_t s);
+// 4-token key groups (group_screen.hip): the screen operands of the group means
+// (ops.ks in 16-group MFMA tiles, ops.krec (mean, exponent) per group, ops.hstat per
+// head; after launch_screen_init).
+hipError_t launch_pool_groups_screen(const Geom& g, const void* k, const ScreenOps& ops, hipStream_t s);
 // Screened group map of heads h0 .. h0+nheads-1 as float32 offsets from each row's
-// upper bound: zt [nheads*S, pitch] (pitch: L/4 rounded up to a multiple of 32).
+// upper bound in log2 units: zt [nheads*S, pitch] (pitch: L/4 rounded up to a
+// multiple of 32).
 hipError_t launch_group_logits_screen(const Geom& g, const ScreenOps& ops, float* zt, int64_t h0, int64_t nheads,
                                       int pitch, hipStream_t s);
 // CDF cut + window union of rows row0 .. row0+nrows-1 from their screened offsets
-// (zt: those rows) -> bitmap rows and counts; rows it cannot decide are appended to
-// flag_list (count in nflag) for launch_group_fallback.
+// (zt: those rows) -> bitmap rows; rows it cannot decide are appended to flag_list
+// (count in nflag) for launch_group_fallback.
 // Per row: the number of entries the screened cut left inside its error margin
 // (cn), the mass above them and the target (cab), and the entries (cjw: up to 64
 // (group id, mass) pairs per row).
@@ -120,17 +121,18 @@ struct GroupRankBufs {
   double2* cab;
   uint2* cjw;
 };
-hipError_t launch_group_screen_select(const Geom& g, const float* zt, int pitch, const ScreenOps& ops,
-                                      const double* qp, const double* kg, int64_t row0, int64_t nrows, double thr,
-                                      double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap,
-                                      int32_t* counts, int words, int32_t* flag_list, int32_t* nflag,
-                                      const GroupRankBufs& rb, hipStream_t s);
-// Exact ranking of the entries the screened cut handed over (every row).
-hipError_t launch_group_rank(const Geom& g, const GroupRankBufs& rb, const double* qp, const double* kg,
-                             uint32_t* bitmap, int32_t* counts, int words, hipStream_t s);
+hipError_t launch_group_screen_select(const Geom& g, const float* zt, int pitch, const ScreenOps& ops, int64_t row0,
+                                      int64_t nrows, double thr, int win_t, int win_h, int win_w, uint32_t* bitmap,
+                                      int words, int32_t* flag_list, int32_t* nflag, const GroupRankBufs& rb,
+                                      hipStream_t s);
+// Exact ranking of the entries the screened cut handed over (every row; k: the keys).
+hipError_t launch_group_rank(const Geom& g, const GroupRankBufs& rb, const double* qp, const void* k,
+                             uint32_t* bitmap, int words, hipStream_t s);
+// Kept counts of rows from their bitmap rows (one wavefront per row).
+hipError_t launch_bitmap_counts(const uint32_t* bitmap, int words, int64_t rows, int32_t* counts, hipStream_t s);
 // The float64 cut of the listed rows (group_mask.hip); zscr: kGroupFallbackRows
 // rows of L/4 doubles.
-hipError_t launch_group_fallback(const Geom& g, const double* qp, const double* kg, double* zscr, double thr,
+hipError_t launch_group_fallback(const Geom& g, const double* qp, const void* k, double* zscr, double thr,
                                  double lambda, int win_t, int win_h, int win_w, uint32_t* bitmap, int32_t* counts,
                                  int words, const int32_t* flag_list, const int32_t* nflag, hipStream_t s);
 int group_select_max_groups();

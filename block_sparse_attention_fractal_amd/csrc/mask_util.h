@@ -133,6 +133,26 @@ __device__ __forceinline__ double group_reduce(double v, int lane, Op op) {
   return v;
 }
 
+// float64 means of channels c0 .. c0 + NC - 1 of the 4 keys of group gid (4
+// consecutive tokens of the fractal order) of head bh: sums of 4 bf16 or float32
+// values in float64, then a quarter (NC a multiple of 8; c0 a multiple of NC)
+template <typename T, int NC>
+__device__ __forceinline__ void group_mean(const T* __restrict__ k, const Geom& g, int64_t bh, int gid, int c0,
+                                           double (&m)[NC]) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int gpb = g.N / 4, blk = gid / gpb, m0 = (gid % gpb) * 4;
+#pragma unroll
+  for (int e = 0; e < NC; ++e) m[e] = 0.0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint4* src = (const uint4*)(k + ((size_t)bh * g.L + block_token_row(g, blk, m0 + t)) * g.D + c0);
+#pragma unroll
+    for (int x = 0; x < NC / EPC; ++x) add_chunk<T>(m + x * EPC, src[x]);
+  }
+#pragma unroll
+  for (int e = 0; e < NC; ++e) m[e] *= 0.25;
+}
+
 // ---- prefix sums and row sums over lanes ----------------------------------
 // value of lane - N inside each row of 16 lanes (0 where that is outside the row)
 template <int N>

@@ -153,7 +153,6 @@ GrpMaskWs grp_mask_ws_layout(const Geom& g) {
   w.words = (int32_t)((SG + 31) / 32);
   int64_t off = 0;
   w.qp = off; off = align256(off + g.rows * g.D * 8);
-  w.kg = off; off = align256(off + bh * SG * g.D * 8);
   w.zt = off; off = align256(off + w.chunk_heads * per_head);
   w.qs = off; off = align256(off + g.rows * 2 * g.D * 2);
   w.ks = off; off = align256(off + bh * ((SG + 15) / 16) * 16 * 2 * g.D * 2);   // whole 16-group tiles

@@ -28,9 +28,9 @@ struct BwdWs {        // transposed mask, per-token (lse*log2e, Delta), work cou
 };
 // Workgroups of the key-group mask's float64 path, each with one float64 scratch row.
 constexpr int kGroupFallbackRows = 256;
-struct GrpMaskWs {     // key-group mask: query-block and group means, the screen operands, a head chunk of
+struct GrpMaskWs {     // key-group mask: query-block means, the screen operands, a head chunk of
                        // screened logits, the rows left to the float64 path and its scratch rows, bits
-  int64_t qp, kg, zt, qs, ks, qmu, krec, qn, qe, hstat, flags, nflag, zfb, cn, cab, cjw, counts, bitmap,
+  int64_t qp, zt, qs, ks, qmu, krec, qn, qe, hstat, flags, nflag, zfb, cn, cab, cjw, counts, bitmap,
       chunk_sums, total;
   int64_t chunk_heads;  // heads whose group logits are computed together
   int32_t pitch;        // floats per screened row (L/4 rounded up to 32)

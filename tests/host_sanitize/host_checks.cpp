@@ -75,7 +75,7 @@ static void valid_problems() {
       std::string msg;
       if (check_group(g, BSA_KEY_GROUP, &msg) == BSA_OK) {
         const GrpMaskWs gm = grp_mask_ws_layout(g);
-        check_offsets({gm.qp, gm.kg, gm.zt, gm.qs, gm.ks, gm.qmu, gm.krec, gm.qn, gm.qe, gm.hstat, gm.flags, gm.nflag,
+        check_offsets({gm.qp, gm.zt, gm.qs, gm.ks, gm.qmu, gm.krec, gm.qn, gm.qe, gm.hstat, gm.flags, gm.nflag,
                        gm.zfb, gm.cn, gm.cab, gm.cjw, gm.counts, gm.bitmap, gm.chunk_sums}, gm.total);
         CHECK(gm.pitch % 32 == 0 && gm.pitch >= g.L / BSA_KEY_GROUP);
         CHECK(gm.chunk_heads >= 1);

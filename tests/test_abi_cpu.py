@@ -258,7 +258,7 @@ def test_query_group_sizes(lib, B, nh, T, H, W):
     S, SG = L // 64, L // 4
     rows = B * nh * S
     assert max_nnz == rows * SG
-    # workspace: query-block and group means, a chunk of heads of screened group
+    # workspace: query-block means, a chunk of heads of screened group
     # logits (float32 rows of L/4 rounded up to 32 entries, as many heads as fit
     # 2 GiB, at least one), the screen operands (query fp16 hi/lo, whole 16-group
     # tiles of group fp16 hi/lo, query means, group (mean, exponent), query norms
@@ -270,7 +270,7 @@ def test_query_group_sizes(lib, B, nh, T, H, W):
     pitch = (SG + 31) // 32 * 32
     per_head = S * pitch * 4
     chunk = max(1, min(B * nh, (1 << 31) // per_head))
-    assert mws == (a(rows * D * 8) + a(B * nh * SG * D * 8) + a(chunk * per_head) + a(rows * 2 * D * 2)
+    assert mws == (a(rows * D * 8) + a(chunk * per_head) + a(rows * 2 * D * 2)
                    + a(B * nh * ((SG + 15) // 16) * 16 * 2 * D * 2) + a(rows * 8) + a(B * nh * SG * 16)
                    + a(rows * 8) + a(rows * 4) + a(B * nh * 3 * 8) + a(rows * 4) + a(4) + a(256 * SG * 8)
                    + a(rows * 4) + a(rows * 16) + a(rows * 64 * 8) + a(rows * 4) + a(rows * ((SG + 31) // 32) * 4) + a((rows + 1023) // 1024 * 4))
