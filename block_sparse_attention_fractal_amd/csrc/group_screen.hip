@@ -64,7 +64,8 @@ constexpr int kNT = 1024;                  // select: threads per row
 constexpr int kNW = kNT / 64;
 constexpr int kPer = 32;                   // entries per thread: 32768 groups per head at most
 constexpr int kMaxCand = 64;               // exactly ranked entries per row
-constexpr int kRowsWG = 128;               // map: query blocks per workgroup (32 per wave)
+constexpr int kRowsWG = 256;               // map: query blocks per workgroup (32 per wave)
+constexpr int kMapWaves = kRowsWG / 32;     // map: waves per workgroup
 constexpr int kStep = 64;                  // map: key groups per LDS stage (4 tiles of 16)
 
 // ---------------------------------------------------------------------------
@@ -204,23 +205,24 @@ __device__ __forceinline__ RowScreen row_screen(const ScreenOps& ops, int64_t r,
 
 // ---------------------------------------------------------------------------
 // Screened map of heads h0 .. h0 + gridDim.z - 1: zt[(h - h0) S + i][j] =
-// (z~_ij - ub_i) log2(e) in float32 (log2 units), row pitch `pitch` floats.  grid = (column slices,
-// ceil(S / 128), heads), 256 threads.  Wave w holds the A operands (hi, lo) of
-// query blocks i0 + 32 w .. + 31 in registers; the workgroup streams its slice
-// of key groups through LDS 64 at a time, by direct-to-LDS buffer loads into two
-// stage buffers (the next stage in flight while the current one is multiplied).  MFMA layouts as in
+// (z~_ij - ub_i) log2(e) in float32 (log2 units), row pitch `pitch` floats.  grid =
+// (column slices, ceil(S / 256), heads), 512 threads.  Wave w holds the operands
+// (hi, lo) of query blocks i0 + 32 w .. + 31 in registers; the workgroup streams
+// its slice of key groups through LDS 64 at a time, by direct-to-LDS buffer loads
+// into two stage buffers (the next stage in flight while the current one is
+// multiplied; 256 query blocks share every group operand read).  MFMA layouts as in
 // mask_screen.hip: A[i][k] in lane 16 (k / 8) + i, B[k][j] in lane 16 (k / 8) + j,
 // C[i][j] in lane 16 (i / 4) + j, register i % 4.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256, 2) group_logits_screen_kernel(ScreenOps ops, float* __restrict__ zt, Geom g,
+__global__ void __launch_bounds__(kMapWaves * 64, 1) group_logits_screen_kernel(ScreenOps ops, float* __restrict__ zt, Geom g,
                                                                      int64_t h0, int steps_per_slice, int pitch,
                                                                      double inv_sqrt_d) {
   constexpr int KS = D / 32;                 // k-steps of 32 channels
   constexpr int kTileB = KS * 2048;          // bytes per 16-group tile (hi and lo)
   constexpr int kStageB = 4 * kTileB;        // bytes per stage (4 tiles)
-  constexpr int kLoads = kStageB / (4 * 1024);   // 1 KB direct-to-LDS loads per wave per stage
-  static_assert(kLoads * 4 * 1024 == kStageB, "stage shape");
+  constexpr int kLoads = kStageB / (kMapWaves * 1024);   // 1 KB direct-to-LDS loads per wave per stage
+  static_assert(kLoads * kMapWaves * 1024 == kStageB, "stage shape");
   __shared__ __attribute__((aligned(16))) uint8_t bs[2][kStageB];   // two stages: the one in use, the next
   __shared__ __attribute__((aligned(16))) double2 recs[2][kStep];  // (nu_j, exponent) of the stage's groups
   __shared__ double rc_a[kRowsWG], rc_u[kRowsWG];
@@ -702,9 +704,9 @@ hipError_t launch_group_logits_screen(const Geom& g, const ScreenOps& ops, float
   dim3 grid((unsigned)((nsteps + per - 1) / per), (unsigned)rowblocks, (unsigned)nheads);
   const double inv = 1.0 / sqrt((double)g.D);
   if (g.D == 64)
-    gscr::group_logits_screen_kernel<64><<<grid, 256, 0, s>>>(ops, zt, g, h0, per, pitch, inv);
+    gscr::group_logits_screen_kernel<64><<<grid, gscr::kMapWaves * 64, 0, s>>>(ops, zt, g, h0, per, pitch, inv);
   else
-    gscr::group_logits_screen_kernel<128><<<grid, 256, 0, s>>>(ops, zt, g, h0, per, pitch, inv);
+    gscr::group_logits_screen_kernel<128><<<grid, gscr::kMapWaves * 64, 0, s>>>(ops, zt, g, h0, per, pitch, inv);
   return hipGetLastError();
 }
 
