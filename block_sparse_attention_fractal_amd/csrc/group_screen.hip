@@ -14,9 +14,10 @@
 // the rank-one part in float64, the centred part on the fp16 matrix cores with both
 // operands split into hi + lo (each vector scaled by a power of two into
 // [2^13, 2^14)).  The products hi*hi of the first and of the second half of the
-// channels and the cross products hi*lo + lo*hi go to three float32 accumulators:
-// with at most 64 additions per accumulator (D = 128) the float32 sums are within
-// 2^-17 of the sum of |products|, the split and the dropped lo*lo term add
+// channels and the two cross products hi*lo, lo*hi go to four float32
+// accumulators: with at most 64 additions per hi*hi accumulator (D = 128) the
+// float32 sums are within 2^-17 of the sum of |products| (the cross products are
+// 2^-10 smaller), the split and the dropped lo*lo term add
 // 3 * 2^-22 and the float32 epilogue (the accumulators summed, scaled and added to
 // the rank-one part minus the row's bound) 2^-22, so every screened logit of row i
 // is within
@@ -28,15 +29,17 @@
 //   * pool_groups_screen_kernel: the screen operands of every group (from the
 //     float64 means of its 4 keys), in MFMA tile order;
 //   * group_logits_screen_kernel: the screened map of a chunk of heads as float32
-//     offsets z - ub_i (ub_i an upper bound of the row's largest logit), written
-//     to HBM (4 bytes per entry instead of 8);
+//     offsets (z - ub_i) log2(e) (ub_i an upper bound of the row's largest logit;
+//     log2 units, so a mass is one exp2), written to HBM (4 bytes per entry
+//     instead of 8);
 //   * group_screen_select_kernel: one 1024-thread workgroup per row, each thread
 //     holding 32 consecutive entries in registers (so its bits are one bitmap
 //     word).  The cut is the block screen's: masses in fixed point from the
 //     screened offsets, a 24-bit key radix-selected 8 bits per pass with one
-//     histogram per wavefront, the crossing bin widened by the error margin; the
-//     entries above it are kept, those inside it (at most 64) are handed with the
-//     mass above them to group_rank_kernel.  Rows whose margin the screen cannot
+//     histogram per pair of wavefronts, the crossing bin widened by the error
+//     margin; the entries above it are kept, those inside it (at most 64) are
+//     handed with the mass above them to group_rank_kernel; the rows' counts are
+//     taken from the bitmap afterwards (bitmap_count_kernel).  Rows whose margin the screen cannot
 //     guarantee, or with more than 64 entries inside it, are listed for the exact
 //     float64 path (group_mask.hip);
 //   * group_rank_kernel: the handed-over entries get their exact float64 logits

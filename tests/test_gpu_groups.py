@@ -102,16 +102,21 @@ def _with_bf16(inputs, name, x):
     inputs[name + "_bits"], inputs[name] = bits, bf16_bits_to_f32(bits)
 
 
-@pytest.mark.parametrize("frames", [4, 2], ids=["every-row-float64", "half-the-rows-float64"])
-def test_group_mask_rows_beyond_the_screen(frames):
+@pytest.mark.parametrize("frames,dtype,D", [(4, "bf16", 128), (2, "bf16", 128), (2, "f32", 64)],
+                         ids=["every-row-float64", "half-the-rows-float64", "f32-d64-half-the-rows-float64"])
+def test_group_mask_rows_beyond_the_screen(frames, dtype, D):
     """Queries of the first `frames` frames scaled by 96: the screened group logits of
     their rows cannot be trusted to the band, so those rows are cut from float64
-    logits; the CSR must match the oracle's, alone and mixed with screened rows."""
-    cfg = small(T=4, H=24, W=40, thr=0.1, window=(1, 1, 1), amp=0.0, seed=52)
+    logits (the group means formed from the keys in the input's own type); the CSR
+    must match the oracle's, alone and mixed with screened rows."""
+    cfg = small(dtype=dtype, D=D, T=4, H=24, W=40, thr=0.1, window=(1, 1, 1), amp=0.0, seed=52)
     inputs = make_inputs(cfg)
     x = inputs["q"].copy()
     x[:, :, : frames * cfg.H * cfg.W] *= 96.0
-    _with_bf16(inputs, "q", x)
+    if dtype == "bf16":
+        _with_bf16(inputs, "q", x)
+    else:
+        inputs["q"] = x
     rp, (n_mis, n_band) = _group_mask_vs_oracle(cfg, inputs)
     print(f"groups, frames scaled {frames}: nnz={rp[-1]} mismatches={n_mis} band={n_band}")
 
