@@ -29,10 +29,12 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
 //     columns from registers): each lane's accumulator holds 32 keys of ONE
 //     query, so the online-softmax state is per lane;
-//   * the running max is refreshed lazily: exponentials use a reference max
-//     that is only raised (and O rescaled) when some lane's true max exceeds it
-//     by more than 2^8, which keeps every p <= 256 and skips the rescale of the
-//     64 output accumulators on almost every tile;
+//   * the running max is refreshed lazily and found only when needed:
+//     exponentials use a reference max, P of a tile is formed under it first,
+//     and the reference is raised (the tile's row max taken, O rescaled, P formed
+//     again) only when some lane's sum of its 32 values exceeds 2^13, so every p
+//     stays <= 2^13, the common tile spends no instructions on its max, and the
+//     64 output accumulators are rarely rescaled;
 //   * O^T += V^T P^T with the same MFMA: A = V^T rows from LDS (pre-transposed
 //     in HBM, keys stored in the accumulator's order), B = P^T straight from the
 //     S^T accumulator registers after rounding to bf16.
@@ -90,7 +92,7 @@ struct Shape {
   static constexpr int kLds = 5 * kTile;              // 80 KB at D = 128: two workgroups fill a CU's 160 KB
   static constexpr int kItemSlot = kLds - 4;          // the item index, only live between items
 };
-constexpr float kLazy = 8.0f;          // log2 slack before the reference max is raised
+constexpr float kSumCap = 8192.0f;     // a lane's P sum over a tile above which the reference max is raised
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -290,7 +292,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     };
     auto issue_v = [&](int j, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
-      const int jc = min(max(j, 0), g.S - 1);
+      // readfirstlane: the tile id is wave-uniform, and saying so keeps the load's
+      // offset in an SGPR (else each load becomes a one-trip waterfall loop)
+      const int jc = __builtin_amdgcn_readfirstlane(min(max(j, 0), g.S - 1));
       const int vs = jc * D * 64 * 2;
 #pragma unroll
       for (int u = 0; u < kLoads; ++u)
@@ -352,29 +356,55 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       bf16x8 pbv[4], pbl[4];
       if (m0) {
         f32x16 sacc[2];
+        auto qk = [&]() {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < 2; ++t) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
+            for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
-          for (int s = 0; s < kQS; ++s) {
-            const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * (kTile / 2));
-            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+            for (int s = 0; s < kQS; ++s) {
+              const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * (kTile / 2));
+              sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
+            }
           }
-        }
-        // tile max as a tree of three-input maxima (16 instructions for 32 values)
-        float m10[11];
+        };
+        // P of the tile under the current reference (bf16 operands for PV), and this
+        // lane's float32 sum of its 32 values
+        float lt;
+        auto softmax = [&]() {
+          lt = 0.f;
 #pragma unroll
-        for (int x = 0; x < 10; ++x) {
-          const int a0 = 3 * x, a1 = 3 * x + 1, a2 = 3 * x + 2;
-          m10[x] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
-        }
-        m10[10] = fmaxf(sacc[1][14], sacc[1][15]);
-        const float mA = fmaxf(fmaxf(m10[0], m10[1]), m10[2]), mB = fmaxf(fmaxf(m10[3], m10[4]), m10[5]);
-        const float mC = fmaxf(fmaxf(m10[6], m10[7]), m10[8]);
-        float mx = fmaxf(fmaxf(mA, mB), fmaxf(fmaxf(mC, m10[9]), m10[10]));
-        mx = pair_max(mx) * c_log2 + shl;
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0) {
+          for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
+              lt += p;
+              const __bf16 ph = (__bf16)p;
+              pbv[2 * t + (e >> 3)][e & 7] = ph;
+              if constexpr (kTrain) pbl[2 * t + (e >> 3)][e & 7] = (__bf16)(p - (float)ph);
+            }
+          }
+        };
+        qk();
+        // The reference max is raised only when it must be: the tile's P is formed
+        // under the current reference first, and kept unless some lane's sum of its
+        // 32 values passes 2^13 (p >= 0, so every kept p is <= 2^13; an overflow
+        // shows as an infinite sum).  Then, and on the first tile of the item (no
+        // reference yet), the products are formed again from the K tile (still in
+        // its slot), the row max found, O rescaled, and P formed afresh.
+        auto raise_ref = [&]() {   // the tile's row max, O rescaled, P formed afresh
+          // tile max as a tree of three-input maxima (16 instructions for 32 values)
+          float m10[11];
+#pragma unroll
+          for (int x = 0; x < 10; ++x) {
+            const int a0 = 3 * x, a1 = 3 * x + 1, a2 = 3 * x + 2;
+            m10[x] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
+          }
+          m10[10] = fmaxf(sacc[1][14], sacc[1][15]);
+          const float mA = fmaxf(fmaxf(m10[0], m10[1]), m10[2]), mB = fmaxf(fmaxf(m10[3], m10[4]), m10[5]);
+          const float mC = fmaxf(fmaxf(m10[6], m10[7]), m10[8]);
+          float mx = fmaxf(fmaxf(mA, mB), fmaxf(fmaxf(mC, m10[9]), m10[10]));
+          mx = pair_max(mx) * c_log2 + shl;
           const float m_new = fmaxf(m_ref, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
           m_ref = m_new;
@@ -384,18 +414,21 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int u = 0; u < kOU; ++u)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
-            l_run += p;
-            const __bf16 ph = (__bf16)p;
-            pbv[2 * t + (e >> 3)][e & 7] = ph;
-            if constexpr (kTrain) pbl[2 * t + (e >> 3)][e & 7] = (__bf16)(p - (float)ph);
+          softmax();
+        };
+        if (__builtin_amdgcn_readfirstlane(__float_as_int(m_ref)) == __float_as_int(-INFINITY)) {
+          raise_ref();
+        } else {
+          softmax();
+          if (__builtin_amdgcn_ballot_w64(lt > kSumCap) != 0) {
+            // a compiler-level memory clobber: the products are formed again from LDS
+            // rather than kept alive through the fast path (which would cost 32 VGPRs)
+            asm volatile("" ::: "memory");
+            qk();
+            raise_ref();
           }
         }
+        l_run += lt;
         if constexpr (!kTrain) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
