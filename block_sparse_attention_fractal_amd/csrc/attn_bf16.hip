@@ -44,6 +44,7 @@
 // of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).  Both contractions
 // pair "element e of half h" of A and B, so the physical k order inside the
 // instruction does not matter.
+#include <float.h>
 #include <math.h>
 
 #include <algorithm>
@@ -92,7 +93,7 @@ struct Shape {
   static constexpr int kLds = 5 * kTile;              // 80 KB at D = 128: two workgroups fill a CU's 160 KB
   static constexpr int kItemSlot = kLds - 4;          // the item index, only live between items
 };
-constexpr float kSumCap = 8192.0f;     // a lane's P sum over a tile above which the reference max is raised
+constexpr float kSumCap = 4096.0f;     // a lane's P sum over a key half above which the reference max is raised
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -328,7 +329,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
     // combination of the kept V rows with exactly the weights the MFMA applied (P of
     // the dominant key is not exactly 1 under the lazy reference, and its 2^-9
     // rounding would otherwise show at full size in O)
-    float m_ref = -INFINITY, l_run = 0.f, l_pv = 0.f;
+    float m_ref = -FLT_MAX, l_run = 0.f, l_pv = 0.f;
 
     // tiles j (current), j1, j2: K of a tile is loaded two steps ahead of its QK
     // products, V^T one step ahead (issued first, so a step's wait can leave the
@@ -356,54 +357,41 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
       bf16x8 pbv[4], pbl[4];
       if (m0) {
         f32x16 sacc[2];
-        auto qk = [&]() {
+        // the products of key half t (keys 32t .. 32t+31 of the tile)
+        auto qk = [&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+          bf16x8 ak[kQS];   // every operand read issued ahead of the products
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int s = 0; s < kQS; ++s) ak[s] = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * (kTile / 2));
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
+          for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
-            for (int s = 0; s < kQS; ++s) {
-              const bf16x8 ak = *(lds_bf16x8*)(uintptr_t)(kaddr[s] + KS * kTile + t * (kTile / 2));
-              sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[t], 0, 0, 0);
-            }
-          }
+          for (int s = 0; s < kQS; ++s) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[s], qreg[s], sacc[t], 0, 0, 0);
         };
-        // P of the tile under the current reference (bf16 operands for PV), and this
-        // lane's float32 sum of its 32 values
-        float lt;
-        auto softmax = [&]() {
-          lt = 0.f;
+        // P of key half t under the current reference (bf16 operands of its two PV
+        // k-steps); returns this lane's float32 sum of its 16 values
+        auto softmax = [&](auto t_c) -> float {
+          constexpr int t = decltype(t_c)::value;
+          float lt = 0.f;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
-              lt += p;
-              const __bf16 ph = (__bf16)p;
-              pbv[2 * t + (e >> 3)][e & 7] = ph;
-              if constexpr (kTrain) pbl[2 * t + (e >> 3)][e & 7] = (__bf16)(p - (float)ph);
-            }
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], c_log2, shl - m_ref));
+            lt += p;
+            const __bf16 ph = (__bf16)p;
+            pbv[2 * t + (e >> 3)][e & 7] = ph;
+            if constexpr (kTrain) pbl[2 * t + (e >> 3)][e & 7] = (__bf16)(p - (float)ph);
           }
+          return lt;
         };
-        qk();
-        // The reference max is raised only when it must be: the tile's P is formed
-        // under the current reference first, and kept unless some lane's sum of its
-        // 32 values passes 2^13 (p >= 0, so every kept p is <= 2^13; an overflow
-        // shows as an infinite sum).  Then, and on the first tile of the item (no
-        // reference yet), the products are formed again from the K tile (still in
-        // its slot), the row max found, O rescaled, and P formed afresh.
-        auto raise_ref = [&]() {   // the tile's row max, O rescaled, P formed afresh
-          // tile max as a tree of three-input maxima (16 instructions for 32 values)
-          float m10[11];
+        // raise the reference to cover the row max of key half t (a tree of
+        // three-input maxima over its 16 values): O and the sums rescaled
+        auto raise_ref = [&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+          float m5[6];
 #pragma unroll
-          for (int x = 0; x < 10; ++x) {
-            const int a0 = 3 * x, a1 = 3 * x + 1, a2 = 3 * x + 2;
-            m10[x] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
-          }
-          m10[10] = fmaxf(sacc[1][14], sacc[1][15]);
-          const float mA = fmaxf(fmaxf(m10[0], m10[1]), m10[2]), mB = fmaxf(fmaxf(m10[3], m10[4]), m10[5]);
-          const float mC = fmaxf(fmaxf(m10[6], m10[7]), m10[8]);
-          float mx = fmaxf(fmaxf(mA, mB), fmaxf(fmaxf(mC, m10[9]), m10[10]));
+          for (int x = 0; x < 5; ++x) m5[x] = fmaxf(fmaxf(sacc[t][3 * x], sacc[t][3 * x + 1]), sacc[t][3 * x + 2]);
+          m5[5] = sacc[t][15];
+          float mx = fmaxf(fmaxf(fmaxf(m5[0], m5[1]), m5[2]), fmaxf(fmaxf(m5[3], m5[4]), m5[5]));
           mx = pair_max(mx) * c_log2 + shl;
           const float m_new = fmaxf(m_ref, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -414,43 +402,84 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
           for (int u = 0; u < kOU; ++u)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[u][e] *= alpha;
-          softmax();
         };
-        if (__builtin_amdgcn_readfirstlane(__float_as_int(m_ref)) == __float_as_int(-INFINITY)) {
-          raise_ref();
-        } else {
-          softmax();
+        // l_pv: the float32 sum of the bf16 P of key half t, as the PV product uses it
+        auto sum_pv = [&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+          if constexpr (!kTrain) {
+#pragma unroll
+            for (int s = 2 * t; s < 2 * t + 2; ++s) {
+              l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
+              l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
+              l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
+              l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
+            }
+          }
+        };
+        // O^T += V^T P^T over the 32 keys of half t (two 16-key k-steps)
+        auto pv = [&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+#pragma unroll
+          for (int s = 2 * t; s < 2 * t + 2; ++s) {
+#pragma unroll
+            for (int u = 0; u < kOU; ++u) {
+              const bf16x8 av = *(lds_bf16x8*)(uintptr_t)(vaddr[s] + VS * kTile + u * 4096);
+              oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
+              if constexpr (kTrain) oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbl[s], oacc[u], 0, 0, 0);
+            }
+          }
+        };
+        using T0 = std::integral_constant<int, 0>;
+        using T1 = std::integral_constant<int, 1>;
+        {
+          // The reference max is raised only when it must be: P of a key half is
+          // formed under the current reference and kept unless some lane's sum of
+          // its 16 values passes 2^12 (p >= 0, so every kept p is <= 2^12; an
+          // overflow shows as an infinite sum, and so does every sum of the item's
+          // first tile, whose reference starts at -FLT_MAX); then that half's
+          // products are formed again from the K tile (still in its slot), O
+          // rescaled and its P formed afresh.  The halves are staggered so that
+          // each one's exponentials run beside the other half's matrix products:
+          // QK of half 1 with the softmax of half 0, PV of half 0 with the softmax
+          // of half 1.
+          __builtin_amdgcn_s_setprio(1);
+          qk(T0{});
+          // half 0's products first (the scheduler would otherwise interleave the two
+          // accumulation chains and leave half 0 unfinished until the end), with its
+          // operand reads kept four ahead of the products
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+#pragma unroll
+          for (int x = 0; x < kQS - 4; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 MFMA
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(0);
+          qk(T1{});
+          float lt = softmax(T0{});
           if (__builtin_amdgcn_ballot_w64(lt > kSumCap) != 0) {
-            // a compiler-level memory clobber: the products are formed again from LDS
-            // rather than kept alive through the fast path (which would cost 32 VGPRs)
+            // a compiler-level memory clobber: the products are formed again from
+            // LDS rather than kept alive through the fast path
             asm volatile("" ::: "memory");
-            qk();
-            raise_ref();
+            qk(T0{});
+            raise_ref(T0{});
+            lt = softmax(T0{});
           }
-        }
-        l_run += lt;
-        if constexpr (!kTrain) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 0, 1), kOnes2, l_pv, false);
-            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 2, 3), kOnes2, l_pv, false);
-            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 4, 5), kOnes2, l_pv, false);
-            l_pv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pbv[s], pbv[s], 6, 7), kOnes2, l_pv, false);
+          l_run += lt;
+          sum_pv(T0{});
+          pv(T0{});
+          lt = softmax(T1{});
+          if (__builtin_amdgcn_ballot_w64(lt > kSumCap) != 0) {
+            asm volatile("" ::: "memory");
+            qk(T1{});
+            raise_ref(T1{});
+            lt = softmax(T1{});
           }
+          l_run += lt;
+          sum_pv(T1{});
+          pv(T1{});
         }
-        // raised wave priority for the PV products: when the other wave of the SIMD is
-        // in its softmax, this wave's MFMAs go first and the VALU work fills in
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-          for (int u = 0; u < kOU; ++u) {
-            const bf16x8 av = *(lds_bf16x8*)(uintptr_t)(vaddr[s] + VS * kTile + u * 4096);
-            oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbv[s], oacc[u], 0, 0, 0);
-            if constexpr (kTrain) oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbl[s], oacc[u], 0, 0, 0);
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
       }
       j = j1; m0 = m1; shl = shl1;
       j1 = j2; m1 = m2; shl1 = shl2;
