@@ -477,8 +477,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnBf16Args a) {
             lt = softmax(T1{});
           }
           l_run += lt;
+          // raised priority again for the step's MFMA-only tail (PV of half 1)
+          __builtin_amdgcn_s_setprio(1);
           sum_pv(T1{});
           pv(T1{});
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       j = j1; m0 = m1; shl = shl1;
