@@ -366,3 +366,44 @@ def test_bf16_head_dim_64_matches_oracle(name):
     compare_outputs(to_host_f64(o2), O2, "bf16")
     print(f"bf16 D=64 {name}: nnz={res['row_ptr'][-1]} mismatches={n_mis} band={n_band} max_abs={ma:.3e} "
           f"mean_rel={mr:.3e}")
+
+
+def _rising_inputs(D, sign, seed=3, T=2, H=16, W=24, nh=2):
+    """bf16 inputs whose logits move by ~16 (log2 units) from one 32-key half of a key
+    block to the next, in block order: with sign +1 every half carries a new row max
+    (the attention kernel must raise its reference on each of them, including key half
+    1 after half 0 of the same tile was already added), with sign -1 the first tile
+    holds the max.  Keys are a_f * (1, ..., 1) + noise with a_f = 2 j + h for fractal
+    key f in half h of block j; queries are (1, ..., 1) + noise."""
+    from workloads.generate import bf16_round
+    rng = np.random.default_rng(seed)
+    L = T * H * W
+    src = oracle.fractal_positions(T, H, W, 8)          # fractal index -> original token
+    f = np.arange(L)
+    a = np.empty(L)
+    a[src] = 2 * (f // 64) + (f % 64) // 32
+    amp = 128.0 / D * np.sqrt(D / 128.0)                # logit step per half ~ 16 (log2 units) at any D
+    q = 1.0 + 0.1 * rng.standard_normal((1, nh, L, D))
+    k = sign * amp * a[None, None, :, None] + 0.1 * rng.standard_normal((1, nh, L, D))
+    v = rng.standard_normal((1, nh, L, D))
+    out = {}
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        bits = bf16_round(x.astype(np.float32))
+        out[n + "_bits"] = bits
+        out[n] = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("D", [128, 64])
+def test_rising_logits_raise_the_reference(D, sign):
+    """Dense attention (thr = 0) on logits that rise (or fall) by ~16 log2 units per
+    32-key half: the bf16 kernel's lazy reference is raised on every half (or only on
+    the first tile), and O and the LSE still match the float64 oracle."""
+    cfg = small_cfg(dtype="bf16", nh=2, T=2, H=16, W=24, D=D, thr=0.0)
+    inputs = _rising_inputs(D, sign)
+    res = run_all(cfg, inputs, thr=0.0)
+    assert res["row_ptr"][-1] == (len(res["row_ptr"]) - 1) * cfg.S
+    O, LSE = oracle.dense_attention(inputs["q"], inputs["k"], inputs["v"])
+    compare_outputs(res["o"], O, "bf16")
+    assert np.abs(res["lse"] - LSE).max() < 2e-3
